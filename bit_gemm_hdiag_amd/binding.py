@@ -1,0 +1,269 @@
+"""ctypes binding of libmxsens (include/mxsens.h), same names as the C ABI.
+
+Argument marshalling only: tensors must already live in GPU memory; the
+binding checks dtypes and layouts, allocates outputs and workspaces with
+torch when the caller passes none, and enqueues the C call on the current
+HIP stream. Every step of the method runs in the library's kernels. There
+is no CPU fallback: a missing library raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int32, c_int64, c_size_t, c_void_p
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libmxsens.so")
+
+MXS_F32, MXS_BF16 = 0, 1
+STATUS = {0: "MXS_OK", -1: "MXS_ERR_ARG", -2: "MXS_ERR_SHAPE", -3: "MXS_ERR_BUDGET",
+          -4: "MXS_ERR_WORKSPACE", -5: "MXS_ERR_DEVICE", -6: "MXS_ERR_UNSUPPORTED"}
+
+
+class MxsError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _QMat(Structure):
+    _fields_ = [("rows", c_int64), ("K", c_int64), ("n8", c_int32), ("n6", c_int32),
+                ("n4", c_int32), ("reserved", c_int32),
+                ("q8", c_void_p), ("ld8", c_int64), ("q6", c_void_p), ("ld6", c_int64),
+                ("q4", c_void_p), ("ld4", c_int64), ("sc", c_void_p), ("lds", c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libmxsens.so is not built ({_LIB_PATH}); run __graft_entry__.build() "
+                          "or python -m bit_gemm_hdiag_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, S = c_void_p, c_int32
+    sig = {
+        "mxs_status_string": (c_char_p, [S]),
+        "mxs_last_error": (c_char_p, []),
+        "mxs_version": (c_int32, []),
+        "mxs_budget_blocks": (S, [c_int64, c_int32, c_int32, P]),
+        "mxs_calibrate_workspace": (c_size_t, [c_int64, c_int64]),
+        "mxs_score_workspace": (c_size_t, [c_int64, c_int64]),
+        "mxs_calibrate": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, c_size_t, P]),
+        "mxs_score": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, P, c_size_t, P]),
+        "mxs_allocate": (S, [P, c_int64, c_int32, c_int32, P, P, P]),
+        "mxs_quantize": (S, [P, c_int32, c_int64, P, POINTER(_QMat), P]),
+        "mxs_mixed_gemm_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
+        "mxs_mixed_gemm": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
+        "mxs_quantize_kv": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_blocks",
+            "mxs_calibrate_workspace", "mxs_score_workspace", "mxs_calibrate", "mxs_score",
+            "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
+            "mxs_quantize_kv")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MxsError(status, where, _lib.mxs_last_error().decode())
+
+
+def _stream(dev) -> c_void_p:
+    return c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MXS_BF16
+    if t.dtype == torch.float32:
+        return MXS_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bf16 or fp32)")
+
+
+def _dev2d(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.data_ptr(), t.stride(0)
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _workspace(nbytes: int, dev, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+# --------------------------------------------------------------------- plain calls
+def mxs_version() -> int:
+    return _lib.mxs_version()
+
+
+def mxs_status_string(status: int) -> str:
+    return _lib.mxs_status_string(status).decode()
+
+
+def mxs_last_error() -> str:
+    return _lib.mxs_last_error().decode()
+
+
+def mxs_budget_blocks(K: int, bp8: int, bp6: int):
+    out = (c_int32 * 3)()
+    _check(_lib.mxs_budget_blocks(K, bp8, bp6, ctypes.cast(out, c_void_p)), "mxs_budget_blocks")
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def mxs_calibrate_workspace(M: int, K: int) -> int:
+    return int(_lib.mxs_calibrate_workspace(M, K))
+
+
+def mxs_score_workspace(N: int, K: int) -> int:
+    return int(_lib.mxs_score_workspace(N, K))
+
+
+def mxs_calibrate(X: torch.Tensor, hdiag: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """hdiag[k] += sum_t X[t, k]^2 (fp64, fixed order). X [M, K] bf16/fp32 on the GPU."""
+    px, ldx = _dev2d(X, "X")
+    M, K = X.shape
+    if hdiag is None:
+        hdiag = torch.zeros(K, dtype=torch.float64, device=X.device)
+    if hdiag.dtype != torch.float64 or not hdiag.is_contiguous() or hdiag.numel() != K:
+        raise ValueError("hdiag must be a contiguous fp64 [K] tensor")
+    pw, nw = _workspace(mxs_calibrate_workspace(M, K), X.device, ws)
+    _check(_lib.mxs_calibrate(px, _dtype(X), M, K, ldx, hdiag.data_ptr(), pw, nw, _stream(X.device)),
+           "mxs_calibrate")
+    return hdiag
+
+
+def mxs_score(W: torch.Tensor, hdiag: torch.Tensor, score: torch.Tensor | None = None, ws=None):
+    """score[k] = hdiag[k] * sum_n (W - Q4(W))[n, k]^2, fp64 [K]."""
+    pw_, ldw = _dev2d(W, "W")
+    N, K = W.shape
+    if score is None:
+        score = torch.empty(K, dtype=torch.float64, device=W.device)
+    if hdiag.dtype != torch.float64 or not hdiag.is_contiguous() or hdiag.numel() != K:
+        raise ValueError("hdiag must be a contiguous fp64 [K] tensor")
+    p, n = _workspace(mxs_score_workspace(N, K), W.device, ws)
+    _check(_lib.mxs_score(pw_, _dtype(W), N, K, ldw, hdiag.data_ptr(), score.data_ptr(), p, n,
+                          _stream(W.device)), "mxs_score")
+    return score
+
+
+def mxs_allocate(score: torch.Tensor, bp8: int, bp6: int, bits=None, perm=None):
+    """(bits uint8 [K] in {8, 6, 4}, perm int32 [K] gather form)."""
+    if not score.is_cuda or score.dtype != torch.float64 or not score.is_contiguous():
+        raise ValueError("score must be a contiguous fp64 GPU tensor")
+    K = score.numel()
+    if bits is None:
+        bits = torch.empty(K, dtype=torch.uint8, device=score.device)
+    if perm is None:
+        perm = torch.empty(K, dtype=torch.int32, device=score.device)
+    _check(_lib.mxs_allocate(score.data_ptr(), K, bp8, bp6, bits.data_ptr(), perm.data_ptr(),
+                             _stream(score.device)), "mxs_allocate")
+    return bits, perm
+
+
+@dataclass
+class QMat:
+    """Planes of a matrix quantised with one bit map (see mxs_qmat)."""
+    rows: int
+    K: int
+    n8: int
+    n6: int
+    n4: int
+    q8: torch.Tensor
+    q6: torch.Tensor
+    q4: torch.Tensor
+    sc: torch.Tensor
+
+    def c_struct(self) -> _QMat:
+        def ld(t, width):
+            return t.stride(0) if t.numel() else max(width, 1)
+        for t in (self.q8, self.q6, self.q4, self.sc):
+            if t.numel() and t.stride(1) != 1:
+                raise ValueError("planes need unit column stride")
+        return _QMat(self.rows, self.K, self.n8, self.n6, self.n4, 0,
+                     _ptr(self.q8), ld(self.q8, 32 * self.n8), _ptr(self.q6), ld(self.q6, 24 * self.n6),
+                     _ptr(self.q4), ld(self.q4, 16 * self.n4), _ptr(self.sc), ld(self.sc, self.K // 32))
+
+    def rows_slice(self, r0: int, r1: int) -> "QMat":
+        return QMat(r1 - r0, self.K, self.n8, self.n6, self.n4, self.q8[r0:r1], self.q6[r0:r1],
+                    self.q4[r0:r1], self.sc[r0:r1])
+
+
+def qmat_alloc(rows: int, K: int, n8: int, n6: int, n4: int, device) -> QMat:
+    kw = dict(device=device)
+    return QMat(rows, K, n8, n6, n4,
+                torch.empty((rows, 32 * n8), dtype=torch.int8, **kw),
+                torch.empty((rows, 24 * n6), dtype=torch.uint8, **kw),
+                torch.empty((rows, 16 * n4), dtype=torch.uint8, **kw),
+                torch.empty((rows, K // 32), dtype=torch.uint8, **kw))
+
+
+def mxs_quantize(X: torch.Tensor, perm: torch.Tensor | None, n8: int, n6: int, n4: int,
+                 out: QMat | None = None) -> QMat:
+    """MXINT 8/6/4 planes of X[:, perm] (perm None = identity)."""
+    px, ldx = _dev2d(X, "X")
+    R, K = X.shape
+    if perm is not None and (perm.dtype != torch.int32 or not perm.is_contiguous() or perm.numel() != K
+                             or not perm.is_cuda):
+        raise ValueError("perm must be a contiguous int32 [K] GPU tensor")
+    if out is None:
+        out = qmat_alloc(R, K, n8, n6, n4, X.device)
+    if out.rows != R or out.K != K:
+        raise ValueError("output planes do not match X")
+    q = out.c_struct()
+    _check(_lib.mxs_quantize(px, _dtype(X), ldx, _ptr(perm), ctypes.byref(q), _stream(X.device)),
+           "mxs_quantize")
+    return out
+
+
+def mxs_mixed_gemm_workspace(A: QMat, W: QMat) -> int:
+    a, w = A.c_struct(), W.c_struct()
+    return int(_lib.mxs_mixed_gemm_workspace(ctypes.byref(a), ctypes.byref(w)))
+
+
+def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """Y [M, N] fp32 = Qa(X) Qw(W)^T with per-block MX scales."""
+    dev = A.sc.device
+    if Y is None:
+        Y = torch.empty((A.rows, W.rows), dtype=torch.float32, device=dev)
+    if Y.dtype != torch.float32:
+        raise TypeError("Y must be fp32")
+    py, ldy = _dev2d(Y, "Y")
+    a, w = A.c_struct(), W.c_struct()
+    p, n = _workspace(int(_lib.mxs_mixed_gemm_workspace(ctypes.byref(a), ctypes.byref(w))), dev, ws)
+    _check(_lib.mxs_mixed_gemm(ctypes.byref(a), ctypes.byref(w), py, ldy, p, n, _stream(dev)),
+           "mxs_mixed_gemm")
+    return Y
+
+
+def mxs_quantize_kv(kv: torch.Tensor, codes=None, scales=None):
+    """codes uint8 [T, H, D/2], scales uint8 [T, H, D/32] for kv [T, H, D]."""
+    if not kv.is_cuda or kv.dim() != 3 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [T, H, D] GPU tensor")
+    T, H, D = kv.shape
+    if codes is None:
+        codes = torch.empty((T, H, D // 2), dtype=torch.uint8, device=kv.device)
+    if scales is None:
+        scales = torch.empty((T, H, D // 32), dtype=torch.uint8, device=kv.device)
+    _check(_lib.mxs_quantize_kv(kv.data_ptr(), _dtype(kv), T, H, D, _ptr(codes), _ptr(scales),
+                                _stream(kv.device)), "mxs_quantize_kv")
+    return codes, scales

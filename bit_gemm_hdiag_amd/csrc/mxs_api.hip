@@ -1,0 +1,194 @@
+// mxs_api.hip -- extern "C" entry points of libmxsens: argument checks,
+// workspace sizing and kernel launches on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mxs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mxs_status fail(mxs_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mxs_status ok() {
+    g_err[0] = '\0';
+    return MXS_OK;
+}
+
+mxs_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MXS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(mxs_dtype d) { return d == MXS_F32 || d == MXS_BF16; }
+
+int64_t nchunks(int64_t rows) { return mxs::ceil_div(rows, mxs::kChunkRows); }
+
+size_t colsum_ws(int64_t rows, int64_t K, bool score) {
+    if (rows <= 0 || K <= 0) return 0;
+    const int64_t n = nchunks(rows);
+    if (n <= 1) return 0;
+    const int64_t per = n < mxs::kMaxChunksPerLaunch ? n : mxs::kMaxChunksPerLaunch;
+    return (size_t)(per + (score ? 1 : 0)) * (size_t)K * sizeof(double);
+}
+
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+mxs_status check_qmat(const mxs_qmat *q, const char *name) {
+    if (!q) return fail(MXS_ERR_ARG, "%s is NULL", name);
+    if (q->rows < 0 || q->K <= 0 || q->K % 32) return fail(MXS_ERR_SHAPE, "%s: rows=%lld K=%lld (K must be a positive multiple of 32)", name, (long long)q->rows, (long long)q->K);
+    if (q->n8 < 0 || q->n6 < 0 || q->n4 < 0 || (int64_t)q->n8 + q->n6 + q->n4 != q->K / 32)
+        return fail(MXS_ERR_SHAPE, "%s: block counts %d/%d/%d do not sum to K/32=%lld", name, q->n8, q->n6, q->n4, (long long)(q->K / 32));
+    if (q->reserved != 0) return fail(MXS_ERR_ARG, "%s: reserved field must be 0", name);
+    if (q->rows == 0) return MXS_OK;   // nothing is read or written
+    if (!q->sc) return fail(MXS_ERR_ARG, "%s: scale plane is NULL", name);
+    if (q->lds < q->K / 32) return fail(MXS_ERR_SHAPE, "%s: lds < K/32", name);
+    if (q->n8 && (!q->q8 || q->ld8 < 32LL * q->n8)) return fail(q->q8 ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: 8-bit plane missing or ld8 < 32*n8", name);
+    if (q->n6 && (!q->q6 || q->ld6 < 24LL * q->n6)) return fail(q->q6 ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: 6-bit plane missing or ld6 < 24*n6", name);
+    if (q->n4 && (!q->q4 || q->ld4 < 16LL * q->n4)) return fail(q->q4 ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: 4-bit plane missing or ld4 < 16*n4", name);
+    return MXS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mxs_status_string(mxs_status s) {
+    switch (s) {
+        case MXS_OK: return "MXS_OK";
+        case MXS_ERR_ARG: return "MXS_ERR_ARG";
+        case MXS_ERR_SHAPE: return "MXS_ERR_SHAPE";
+        case MXS_ERR_BUDGET: return "MXS_ERR_BUDGET";
+        case MXS_ERR_WORKSPACE: return "MXS_ERR_WORKSPACE";
+        case MXS_ERR_DEVICE: return "MXS_ERR_DEVICE";
+        case MXS_ERR_UNSUPPORTED: return "MXS_ERR_UNSUPPORTED";
+        default: return "MXS_UNKNOWN_STATUS";
+    }
+}
+
+const char *mxs_last_error(void) { return g_err; }
+
+int32_t mxs_version(void) { return 1; }
+
+mxs_status mxs_budget_blocks(int64_t K, int32_t bp8, int32_t bp6, int32_t nblk[3]) {
+    if (!nblk) return fail(MXS_ERR_ARG, "nblk is NULL");
+    if (K <= 0 || K % 32) return fail(MXS_ERR_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+    if (bp8 < 0 || bp6 < 0 || (int64_t)bp8 + bp6 > 10000)
+        return fail(MXS_ERR_BUDGET, "budget bp8=%d bp6=%d outside [0, 10000]", bp8, bp6);
+    const int64_t nb = K / 32;
+    const int64_t U = nb * (2 * (int64_t)bp8 + bp6) / 10000;
+    int64_t n8 = 0;
+    if (bp8 > 0) {
+        n8 = nb * bp8 / 10000;
+        if (n8 < 1) n8 = 1;
+    }
+    if (n8 > U / 2) n8 = U / 2;
+    int64_t n6 = U - 2 * n8;
+    if (n6 > nb - n8) n6 = nb - n8;
+    nblk[0] = (int32_t)n8;
+    nblk[1] = (int32_t)n6;
+    nblk[2] = (int32_t)(nb - n8 - n6);
+    return ok();
+}
+
+size_t mxs_calibrate_workspace(int64_t M, int64_t K) { return colsum_ws(M, K, false); }
+size_t mxs_score_workspace(int64_t N, int64_t K) { return colsum_ws(N, K, true); }
+
+mxs_status mxs_calibrate(const void *X, mxs_dtype dtype, int64_t M, int64_t K, int64_t ldx,
+                         double *hdiag, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || K <= 0 || K % 32 || ldx < K)
+        return fail(MXS_ERR_SHAPE, "calibrate: M=%lld K=%lld ldx=%lld", (long long)M, (long long)K, (long long)ldx);
+    if (!hdiag || (M > 0 && !X)) return fail(MXS_ERR_ARG, "calibrate: NULL pointer");
+    const size_t need = colsum_ws(M, K, false);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
+        return fail(MXS_ERR_WORKSPACE, "calibrate: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+    if (M == 0) return ok();
+    return device_status(mxs::launch_calibrate(X, dtype, M, K, ldx, hdiag, static_cast<double *>(ws), stream), "calibrate");
+}
+
+mxs_status mxs_score(const void *W, mxs_dtype dtype, int64_t N, int64_t K, int64_t ldw,
+                     const double *hdiag, double *score, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (N <= 0 || K <= 0 || K % 32 || ldw < K)
+        return fail(MXS_ERR_SHAPE, "score: N=%lld K=%lld ldw=%lld", (long long)N, (long long)K, (long long)ldw);
+    if (!W || !hdiag || !score) return fail(MXS_ERR_ARG, "score: NULL pointer");
+    const size_t need = colsum_ws(N, K, true);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 16)))
+        return fail(MXS_ERR_WORKSPACE, "score: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+    return device_status(mxs::launch_score(W, dtype, N, K, ldw, hdiag, score, static_cast<double *>(ws), stream), "score");
+}
+
+mxs_status mxs_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6, uint8_t *bits,
+                        int32_t *perm, hipStream_t stream) {
+    int32_t nb3[3];
+    mxs_status s = mxs_budget_blocks(K, bp8, bp6, nb3);
+    if (s != MXS_OK) return s;
+    if (!score || !bits || !perm) return fail(MXS_ERR_ARG, "allocate: NULL pointer");
+    if (K > 131072) return fail(MXS_ERR_UNSUPPORTED, "allocate: K=%lld above 131072", (long long)K);
+    return device_status(mxs::launch_allocate(score, K, 32 * nb3[0], 32 * nb3[1], bits, perm, stream), "allocate");
+}
+
+mxs_status mxs_quantize(const void *X, mxs_dtype dtype, int64_t ldx, const int32_t *perm,
+                        const mxs_qmat *out, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "unknown dtype %d", (int)dtype);
+    mxs_status s = check_qmat(out, "quantize out");
+    if (s != MXS_OK) return s;
+    if (ldx < out->K) return fail(MXS_ERR_SHAPE, "quantize: ldx=%lld < K=%lld", (long long)ldx, (long long)out->K);
+    if (out->rows > 0 && !X) return fail(MXS_ERR_ARG, "quantize: X is NULL");
+    return device_status(mxs::launch_quantize(X, dtype, ldx, perm, *out, stream), "quantize");
+}
+
+size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W) {
+    if (!A || !W) return 0;
+    return mxs::gemm_workspace(*A, *W);
+}
+
+mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    mxs_status s = check_qmat(A, "A");
+    if (s != MXS_OK) return s;
+    if ((s = check_qmat(W, "W")) != MXS_OK) return s;
+    if (A->K != W->K || A->n8 != W->n8 || A->n6 != W->n6 || A->n4 != W->n4)
+        return fail(MXS_ERR_SHAPE, "mixed_gemm: A and W differ in K or block counts");
+    if (ldy < W->rows || (!Y && A->rows > 0 && W->rows > 0)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "mixed_gemm: Y NULL or ldy < N");
+    // operand loads are 16/4/8-byte vector loads per row
+    const mxs_qmat *q[2] = {A, W};
+    for (const mxs_qmat *m : q) {
+        if ((m->n8 && (!aligned(m->q8, 16) || m->ld8 % 16)) || (m->n6 && (!aligned(m->q6, 4) || m->ld6 % 4)) ||
+            (m->n4 && (!aligned(m->q4, 8) || m->ld4 % 8)))
+            return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm: planes need q8/ld8 16-byte, q6/ld6 4-byte and q4/ld4 8-byte alignment");
+    }
+    if (A->rows > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm: more than 4194304 rows in A");
+    const size_t need = mxs::gemm_workspace(*A, *W);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return fail(MXS_ERR_WORKSPACE, "mixed_gemm: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+    return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm");
+}
+
+mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H, int64_t D,
+                           uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (T < 0 || H <= 0 || D <= 0 || D % 32) return fail(MXS_ERR_SHAPE, "quantize_kv: T=%lld H=%lld D=%lld", (long long)T, (long long)H, (long long)D);
+    if (T > 0 && (!kv || !codes || !scales)) return fail(MXS_ERR_ARG, "quantize_kv: NULL pointer");
+    mxs_qmat o;
+    memset(&o, 0, sizeof o);
+    o.rows = T * H;
+    o.K = D;
+    o.n4 = (int32_t)(D / 32);
+    o.q4 = codes;
+    o.ld4 = D / 2;
+    o.sc = scales;
+    o.lds = D / 32;
+    return device_status(mxs::launch_quantize(kv, dtype, D, nullptr, o, stream), "quantize_kv");
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// mxs_internal.h -- host-side launchers shared between the kernel files and
+// the C-ABI entry points. Every launcher validates nothing (the entry points
+// do) and returns the HIP status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mxsens.h"
+
+namespace mxs {
+
+constexpr int64_t kChunkRows = 256;        // rows per ordered partial sum
+constexpr int64_t kMaxChunksPerLaunch = 65535;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// calibrate / score (mxs_colsum.hip)
+hipError_t launch_calibrate(const void *X, mxs_dtype dt, int64_t M, int64_t K, int64_t ldx,
+                            double *hdiag, double *ws, hipStream_t st);
+hipError_t launch_score(const void *W, mxs_dtype dt, int64_t N, int64_t K, int64_t ldw,
+                        const double *hdiag, double *score, double *ws, hipStream_t st);
+
+// allocate (mxs_allocate.hip)
+hipError_t launch_allocate(const double *score, int64_t K, int32_t c8, int32_t c6,
+                           uint8_t *bits, int32_t *perm, hipStream_t st);
+
+// quantize (mxs_quantize.hip)
+hipError_t launch_quantize(const void *X, mxs_dtype dt, int64_t ldx, const int32_t *perm,
+                           const mxs_qmat &out, hipStream_t st);
+
+// mixed GEMM (mxs_gemm.hip)
+size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W);
+hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
+                             void *ws, size_t ws_bytes, hipStream_t st);
+
+}  // namespace mxs

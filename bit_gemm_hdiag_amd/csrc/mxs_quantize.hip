@@ -1,0 +1,120 @@
+// mxs_quantize.hip -- MXINT 4/6/8-bit block quantisation with the
+// block-uniform channel permutation, packed into per-width planes.
+//
+// gist.science/nl "Technische Samenvatting" §1 (one shared power-of-two
+// scale per 32 values), §2.2 (4/6/8-bit mantissas), §2.3 (blocks of one
+// width after regrouping the channels); researchpod.app bullet "Triplet
+// Quantization" (weights and activations). Per permuted block b with width
+// m: s = max(floor(log2 amax) - (m-2), -127), c = clamp(rne(v / 2^s),
+// +-(2^(m-1)-1)); E8M0 byte s + 127 (0 for an all-zero block, 0xFF for a block
+// with NaN/Inf, whose codes are 0).
+//
+// Each lane quantises 8 consecutive positions (a quarter block); the block
+// maximum is a DPP reduction over the aligned quad. Two kernels:
+//  - direct (no permutation): flat grid over (row, 8-column group), 16-byte
+//    coalesced loads; also serves KV quantisation (rows = tokens x heads).
+//  - gather (with permutation): each lane keeps its 8 source indices in
+//    registers and walks a slice of rows, so the permutation is read once
+//    per workgroup; the source reads hit L1/L2 lines of the row being read.
+#include "mxs_device.h"
+#include "mxs_internal.h"
+
+namespace mxs {
+
+namespace {
+
+struct Planes {
+    int64_t K;
+    int32_t n8, n6, n4;
+    int8_t *q8; int64_t ld8;
+    uint8_t *q6; int64_t ld6;
+    uint8_t *q4; int64_t ld4;
+    uint8_t *sc; int64_t lds;
+};
+
+__device__ __forceinline__ void emit(const Planes &P, int64_t row, int64_t blk, int q, const float v[8]) {
+    const int m = blk < P.n8 ? 8 : (blk < (int64_t)P.n8 + P.n6 ? 6 : 4);
+    int c[8];
+    BlockScale bs = quantize8(v, m, c);
+    if (m == 8) {
+        store_bytes(reinterpret_cast<uint8_t *>(P.q8) + row * P.ld8 + 32 * blk + 8 * q, pack8(c), 8);
+    } else if (m == 6) {
+        store_bytes(P.q6 + row * P.ld6 + 24 * (blk - P.n8) + 6 * q, pack6(c), 6);
+    } else {
+        store_bytes(P.q4 + row * P.ld4 + 16 * (blk - P.n8 - P.n6) + 4 * q, pack4(c), 4);
+    }
+    if (q == 0) P.sc[row * P.lds + blk] = (uint8_t)bs.byte;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void k_quant_direct(const T *__restrict__ X, int64_t R, int64_t ldx,
+                                                      Planes P) {
+    const int64_t G = P.K / 8;                     // 8-column groups per row
+    const int64_t total = R * G;
+    for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total;
+         gid += (int64_t)gridDim.x * 256) {
+        const int64_t row = gid / G;
+        const int64_t cg = gid - row * G;
+        float v[8];
+        load8<T, VEC>(X + row * ldx + cg * 8, v);
+        emit(P, row, cg >> 2, (int)(cg & 3), v);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_gather(const T *__restrict__ X, int64_t R, int64_t ldx,
+                                                      const int32_t *__restrict__ perm,
+                                                      int64_t rows_per_block, Planes P) {
+    const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8-position group
+    if (cg * 8 >= P.K) return;                                       // whole quads leave together
+    int32_t src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // an index outside [0, K) is clamped, never dereferenced
+        const uint32_t j = (uint32_t)perm[cg * 8 + i];
+        src[i] = (int32_t)(j < (uint32_t)P.K ? j : (uint32_t)P.K - 1u);
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < R ? r0 + rows_per_block : R;
+    for (int64_t row = r0; row < r1; ++row) {
+        const T *x = X + row * ldx;
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = load1<T>(x + src[i]);
+        emit(P, row, cg >> 2, (int)(cg & 3), v);
+    }
+}
+
+template <typename T>
+hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
+                        hipStream_t st) {
+    if (R == 0) return hipSuccess;
+    if (!perm) {
+        const int64_t total = R * (P.K / 8);
+        int64_t blocks = ceil_div(total, 256);
+        if (blocks > 65536) blocks = 65536;
+        const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
+        if (vec) hipLaunchKernelGGL((k_quant_direct<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, X, R, ldx, P);
+        else hipLaunchKernelGGL((k_quant_direct<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, X, R, ldx, P);
+        return hipGetLastError();
+    }
+    const int64_t gx = ceil_div(P.K / 8, 256);
+    int64_t gy = ceil_div(4096, gx);
+    if (gy > R) gy = R;
+    if (gy > 65535) gy = 65535;
+    const int64_t rpb = ceil_div(R, gy);
+    gy = ceil_div(R, rpb);
+    hipLaunchKernelGGL((k_quant_gather<T>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, X, R, ldx,
+                       perm, rpb, P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *X, mxs_dtype dt, int64_t ldx, const int32_t *perm,
+                           const mxs_qmat &o, hipStream_t st) {
+    Planes P{o.K, o.n8, o.n6, o.n4, o.q8, o.ld8, o.q6, o.ld6, o.q4, o.ld4, o.sc, o.lds};
+    if (dt == MXS_BF16) return run_quantize<uint16_t>(static_cast<const uint16_t *>(X), ldx, perm, P, o.rows, st);
+    return run_quantize<float>(static_cast<const float *>(X), ldx, perm, P, o.rows, st);
+}
+
+}  // namespace mxs

@@ -1,0 +1,219 @@
+/*
+ * mxsens.h -- C ABI of libmxsens, the MI355X (gfx950) hot path of MXSens.
+ *
+ * MXSens ("MXSens: Sensitivity-Aware Mixed-Precision Quantization for
+ * Efficient LLM Inference") gives every input channel of a linear layer a
+ * 4-, 6- or 8-bit MXINT mantissa, chosen from a Hessian-diagonal
+ * sensitivity score, and keeps every 32-value MXINT block at one width.
+ * Page citations below:
+ *   [NL]  gist.science/nl/paper/2607.17733, "Technische Samenvatting", §n
+ *   [REV] romaanj.github.io/reviews/mxsens, named paragraph
+ *   [RP]  researchpod.app summary, named bullet
+ *
+ * Common rules
+ *   - Device pointers: every array argument is device memory, except the
+ *     host-side `nblk` of mxs_budget_blocks and the mxs_qmat structs, which
+ *     are read on the host during the call.
+ *   - Ownership: the caller owns every buffer. The library allocates no
+ *     memory; workspaces are passed in after a size query.
+ *   - Streams: every call enqueues its kernels on `stream` (0 = the null
+ *     stream) and returns without synchronising. Outputs are ready when the
+ *     stream reaches that point.
+ *   - Errors: argument errors are detected before anything is enqueued; a
+ *     failed launch returns MXS_ERR_DEVICE. On error, outputs are undefined
+ *     and mxs_last_error() (thread-local) describes the cause. No C++
+ *     exception crosses this boundary.
+ *   - Layout: matrices are row-major with a leading dimension (elements per
+ *     row, >= the row width). X is [tokens, K] (activations), W is [N, K]
+ *     (out x in), column k is input channel k. K is a multiple of 32.
+ *   - Element types: MXS_F32 (fp32) or MXS_BF16 (bfloat16) inputs; bf16
+ *     values are widened to fp32 exactly. Sums are fp64 where stated.
+ *   - Thread safety: reentrant; the library holds no mutable global state
+ *     other than the thread-local error string.
+ */
+#ifndef MXSENS_H
+#define MXSENS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mxs_status;
+#define MXS_OK               0
+#define MXS_ERR_ARG         -1  /* null pointer, unknown enum value            */
+#define MXS_ERR_SHAPE       -2  /* K % 32 != 0, negative size, ld < width, ... */
+#define MXS_ERR_BUDGET      -3  /* bp8 < 0, bp6 < 0 or bp8 + bp6 > 10000       */
+#define MXS_ERR_WORKSPACE   -4  /* workspace missing or smaller than required  */
+#define MXS_ERR_DEVICE      -5  /* HIP launch or runtime error                 */
+#define MXS_ERR_UNSUPPORTED -6  /* valid but unsupported (alignment, size cap) */
+
+typedef enum { MXS_F32 = 0, MXS_BF16 = 1 } mxs_dtype;
+
+/*
+ * A matrix quantised with one bit map: `rows` rows of K permuted channels,
+ * made of n8 8-bit blocks, then n6 6-bit blocks, then n4 4-bit blocks
+ * (n8 + n6 + n4 = K/32). Storage (all device memory, row-major):
+ *   q8 [rows, ld8 >= 32 n8]  int8 codes, byte j of 8-bit block i at 32 i + j
+ *   q6 [rows, ld6 >= 24 n6]  6-bit codes: block i at 24 i; codes 4g..4g+3
+ *                            form the little-endian 24-bit word
+ *                            c0 | c1<<6 | c2<<12 | c3<<18 at byte 24 i + 3 g
+ *   q4 [rows, ld4 >= 16 n4]  4-bit codes: block i at 16 i; byte h holds
+ *                            c_2h in bits 0-3 and c_2h+1 in bits 4-7
+ *   sc [rows, lds >= K/32]   E8M0 scale byte s + 127 of permuted block b
+ * Codes are two's complement in [-(2^(m-1)-1), 2^(m-1)-1]; the value of a
+ * code c in a block with scale byte e is c * 2^(e-127); e = 0xFF marks a
+ * block that held NaN or Inf (its value is NaN).
+ * Pointers of empty planes (count 0) may be NULL.
+ */
+typedef struct mxs_qmat {
+    int64_t rows;
+    int64_t K;
+    int32_t n8, n6, n4;
+    int32_t reserved;   /* must be 0 */
+    int8_t  *q8; int64_t ld8;
+    uint8_t *q6; int64_t ld6;
+    uint8_t *q4; int64_t ld4;
+    uint8_t *sc; int64_t lds;
+} mxs_qmat;
+
+/* Text for a status code (static storage). */
+const char *mxs_status_string(mxs_status status);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char *mxs_last_error(void);
+
+/* Library ABI version: 1. */
+int32_t mxs_version(void);
+
+/*
+ * Budget -> whole-block counts for one layer of K channels ([NL] §2.2-§2.3:
+ * the 32 most sensitive columns of each layer take 8 bits, a budgeted number
+ * of columns take 6 bits, the rest 4 bits, under a target average width B).
+ * bp8 and bp6 are the 8- and 6-bit column shares in basis points. Reading:
+ *   nb = K/32; U = floor(nb (2 bp8 + bp6) / 10000);
+ *   n8 = bp8 > 0 ? max(1, floor(nb bp8 / 10000)) : 0, capped at floor(U/2);
+ *   n6 = min(U - 2 n8, nb - n8); n4 = nb - n8 - n6,
+ * so the layer average never exceeds B = 8 f8 + 6 f6 + 4 f4.
+ * Host-only and pure: nblk is host memory {n8, n6, n4}.
+ * Errors: MXS_ERR_ARG (nblk NULL), MXS_ERR_SHAPE (K <= 0 or K % 32),
+ * MXS_ERR_BUDGET.
+ */
+mxs_status mxs_budget_blocks(int64_t K, int32_t bp8, int32_t bp6, int32_t nblk[3]);
+
+/* Workspace bytes needed by mxs_calibrate / mxs_score for these sizes. */
+size_t mxs_calibrate_workspace(int64_t M, int64_t K);
+size_t mxs_score_workspace(int64_t N, int64_t K);
+
+/*
+ * Calibration ([NL] §2.1, column-wise sensitivity): accumulate the diagonal
+ * of the empirical Hessian H = X^T X,
+ *     hdiag[k] += sum_t X[t, k]^2,   t < M,
+ * with no normalisation or damping. X: [M, ldx] device array of `dtype`;
+ * hdiag: [K] fp64 device array, read and written (zero it before the first
+ * call; later calls add more calibration tokens). Summation order (so that
+ * rankings built on it are reproducible bit for bit): rows in chunks of 256;
+ * inside a chunk eight partial sums over rows congruent mod 8, combined as
+ * ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); chunk totals added in chunk order.
+ * Squares are exact in fp64. ws: >= mxs_calibrate_workspace(M, K) bytes of
+ * device memory, 256-byte aligned, contents scratch. M = 0 is a no-op.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K <= 0, K % 32, ldx < K, M < 0),
+ * MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+mxs_status mxs_calibrate(const void *X, mxs_dtype dtype, int64_t M, int64_t K, int64_t ldx,
+                         double *hdiag, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Column sensitivity ([NL] §2.1: columns with large Hessian-diagonal entries
+ * turn quantisation noise into the largest output error). Reading for the
+ * score, which the pages leave open:
+ *     score[k] = hdiag[k] * sum_n (W[n, k] - Q4(W)[n, k])^2
+ * where Q4 is uniform 4-bit MXINT in 32-blocks along K in the original
+ * channel order. The residual is exact in fp32, its square exact in fp64,
+ * the sum over n follows the order of mxs_calibrate, the product is rounded
+ * once. W: [N, ldw] of `dtype`; hdiag, score: [K] fp64 device arrays.
+ * ws: >= mxs_score_workspace(N, K) bytes. A block holding NaN/Inf yields NaN
+ * for its 32 columns.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (N <= 0, K % 32, ldw < K),
+ * MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+mxs_status mxs_score(const void *W, mxs_dtype dtype, int64_t N, int64_t K, int64_t ldw,
+                     const double *hdiag, double *score, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Allocation ([NL] §2.3): rank the K columns by score (descending; ties by
+ * ascending index; scores compared as a total order on the fp64 bit pattern,
+ * NaN above +Inf above all finite values), give the first 32 n8 columns 8
+ * bits, the next 32 n6 6 bits and the rest 4 bits, with (n8, n6, n4) from
+ * mxs_budget_blocks. Block-uniform permutation ([NL] §2.3 last paragraph,
+ * [REV] "Key idea": the allocation rides on MXINT's block structure): perm
+ * lists the 8-bit columns in ascending index, then the 6-bit, then the
+ * 4-bit ones, so every 32-block of the permuted order has one width and an
+ * all-4 map gives the identity.
+ * score: [K] fp64 device; bits: [K] uint8 device out (values 8, 6, 4);
+ * perm: [K] int32 device out, gather form (perm[j] = source column of
+ * position j). K <= 131072.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_BUDGET, MXS_ERR_UNSUPPORTED
+ * (K too large), MXS_ERR_DEVICE.
+ */
+mxs_status mxs_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6,
+                        uint8_t *bits, int32_t *perm, hipStream_t stream);
+
+/*
+ * MXINT quantisation of weights or activations ([NL] §1: one shared
+ * power-of-two scale per block of 32; §2.2: 4/6/8-bit mantissas; [RP]
+ * "Triplet Quantization": weights and activations). Row r, permuted block b
+ * with width m takes v = X[r, perm[32 b .. 32 b + 31]] and stores
+ *     s = clamp(floor(log2 max|v|) - (m - 2), -127, 127)   (E8M0 byte s+127)
+ *     c_i = clamp(round_half_even(v_i / 2^s), -(2^(m-1)-1), 2^(m-1)-1)
+ * (reading of the MX rule; all-zero block -> byte 0, NaN/Inf -> byte 0xFF,
+ * codes 0), packed as described at mxs_qmat. Activation scales are computed
+ * per token and block from the values at hand.
+ * X: [out->rows, ldx] of `dtype`; perm: [K] int32 device array or NULL for
+ * the identity; out: host struct describing the caller's output planes
+ * (rows, K, n8, n6, n4, pointers, strides), all written by the call.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_DEVICE.
+ */
+mxs_status mxs_quantize(const void *X, mxs_dtype dtype, int64_t ldx, const int32_t *perm,
+                        const mxs_qmat *out, hipStream_t stream);
+
+/* Workspace bytes needed by mxs_mixed_gemm for these shapes (may be 0). */
+size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W);
+
+/*
+ * Block-scaled mixed-precision GEMM ([NL] §1 and §5, [REV] "Comparison":
+ * the block scales are applied inside the product, with no separate
+ * dequantisation pass):
+ *     Y[t, n] = sum_b 2^(sa[t,b] + sw[n,b]) * sum_{j in b} ca[t, j] cw[n, j]
+ * where A (activations, A->rows = M tokens) and W (weights, W->rows = N) are
+ * quantised with the same K, the same (n8, n6, n4) and the same permutation.
+ * Each block's integer dot product is exact (int8 MFMA, int32 sums); block
+ * terms are combined in fp32 (error ~ sqrt(K/32) ulp relative to
+ * sum |A||W|). Y: [M, ldy] fp32 device output, ldy >= N.
+ * ws: >= mxs_mixed_gemm_workspace(A, W) bytes (NULL if that is 0).
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K or block counts differ, ldy < N),
+ * MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * KV-cache quantisation (W4A4KV4, [NL] §4 and [REV] "Validation": keys and
+ * values stored as 4-bit MXINT). Reading: uniform 4-bit, blocks of 32
+ * consecutive elements along the head dimension, no permutation.
+ * kv: [T, H, D] contiguous of `dtype`; codes: [T, H, D/2] uint8 (4-bit
+ * packing of mxs_qmat); scales: [T, H, D/32] uint8 E8M0. D % 32 == 0.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_DEVICE.
+ */
+mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H, int64_t D,
+                           uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXSENS_H */

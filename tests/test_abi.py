@@ -1,0 +1,147 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/mxsens.h declares, and rejects bad arguments before any
+device work (every call below fails validation, so nothing is enqueued).
+The budget helper is host code and is compared with the oracle here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxsens.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_gemm_hdiag_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    return ctypes.CDLL(build.LIB)
+
+
+@pytest.fixture(scope="module")
+def mx(lib):
+    import bit_gemm_hdiag_amd as mx
+    return mx
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for n in ("mxs_calibrate", "mxs_score", "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm",
+              "mxs_quantize_kv"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from bit_gemm_hdiag_amd import build
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mxs_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_binding_exposes_same_names(mx):
+    from bit_gemm_hdiag_amd import binding
+    for n in declared_functions():
+        assert n in binding.EXPORTED and callable(getattr(mx, n))
+
+
+def test_budget_matches_oracle(mx, orc):
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        K = 32 * int(rng.integers(1, 2000))
+        bp8 = int(rng.integers(0, 4000))
+        bp6 = int(rng.integers(0, 10001 - bp8))
+        assert mx.mxs_budget_blocks(K, bp8, bp6) == orc.budget_blocks(K, bp8, bp6)
+
+
+def test_status_strings(mx):
+    assert mx.mxs_status_string(0) == "MXS_OK"
+    assert mx.mxs_status_string(-4) == "MXS_ERR_WORKSPACE"
+    assert mx.mxs_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+
+
+def test_budget_errors(lib):
+    out = (ctypes.c_int32 * 3)()
+    f = lib.mxs_budget_blocks
+    f.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert f(100, 0, 0, ctypes.cast(out, ctypes.c_void_p)) == -2
+    assert f(256, -5, 0, ctypes.cast(out, ctypes.c_void_p)) == -3
+    assert f(256, 6000, 4001, ctypes.cast(out, ctypes.c_void_p)) == -3
+    assert f(256, 0, 0, None) == -1
+
+
+def test_calibrate_score_errors(lib):
+    P, I64, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    cal = lib.mxs_calibrate
+    cal.argtypes = [P, ctypes.c_int32, I64, I64, I64, P, P, S, P]
+    assert cal(FAKE, 1, 10, 33, 33, FAKE, None, 0, None) == -2        # K % 32
+    assert cal(FAKE, 1, 10, 64, 32, FAKE, None, 0, None) == -2        # ldx < K
+    assert cal(FAKE, 7, 10, 64, 64, FAKE, None, 0, None) == -1        # dtype
+    assert cal(FAKE, 1, 10, 64, 64, None, None, 0, None) == -1        # hdiag NULL
+    assert cal(FAKE, 1, 1000, 64, 64, FAKE, None, 0, None) == -4      # needs workspace
+    need = lib.mxs_calibrate_workspace
+    need.restype, need.argtypes = S, [I64, I64]
+    assert need(256, 64) == 0 and need(257, 64) == 2 * 64 * 8
+    assert cal(FAKE, 1, 1000, 64, 64, FAKE, FAKE, need(1000, 64) - 8, None) == -4
+    sc = lib.mxs_score
+    sc.argtypes = [P, ctypes.c_int32, I64, I64, I64, P, P, P, S, P]
+    assert sc(FAKE, 0, 0, 64, 64, FAKE, FAKE, None, 0, None) == -2      # N = 0
+    assert sc(FAKE, 0, 10, 64, 64, None, FAKE, None, 0, None) == -1
+    assert sc(FAKE, 0, 600, 64, 64, FAKE, FAKE, None, 0, None) == -4
+    lib.mxs_last_error.restype = ctypes.c_char_p
+    assert b"workspace" in lib.mxs_last_error()
+
+
+def test_allocate_errors(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.mxs_allocate
+    f.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    assert f(FAKE, 100, 0, 0, FAKE, FAKE, None) == -2
+    assert f(FAKE, 256, 9000, 2000, FAKE, FAKE, None) == -3
+    assert f(None, 256, 0, 0, FAKE, FAKE, None) == -1
+    assert f(FAKE, 32 * 8192, 0, 0, FAKE, FAKE, None) == -6
+
+
+def qm(rows=4, K=64, n8=0, n6=1, n4=1, **kw):
+    from bit_gemm_hdiag_amd.binding import _QMat
+    d = dict(q8=None, ld8=0, q6=0x10000, ld6=24 * n6, q4=0x20000, ld4=16 * n4, sc=0x30000, lds=K // 32)
+    d.update(kw)
+    return _QMat(rows, K, n8, n6, n4, 0, d["q8"], d["ld8"], d["q6"], d["ld6"], d["q4"], d["ld4"],
+                 d["sc"], d["lds"])
+
+
+def test_quantize_and_gemm_errors(lib):
+    P = ctypes.c_void_p
+    q = lib.mxs_quantize
+    q.argtypes = [P, ctypes.c_int32, ctypes.c_int64, P, P, P]
+    assert q(FAKE, 0, 64, None, ctypes.byref(qm(n4=2)), None) == -2          # counts != K/32
+    assert q(FAKE, 0, 32, None, ctypes.byref(qm()), None) == -2               # ldx < K
+    assert q(FAKE, 0, 64, None, ctypes.byref(qm(ld6=10)), None) == -2         # ld6 < 24 n6
+    assert q(FAKE, 0, 64, None, ctypes.byref(qm(q4=None)), None) == -1        # missing plane
+    assert q(FAKE, 0, 64, None, None, None) == -1
+    g = lib.mxs_mixed_gemm
+    g.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_size_t, P]
+    A, W = qm(rows=8), qm(rows=16, n6=0, n4=2)
+    assert g(ctypes.byref(A), ctypes.byref(W), FAKE, 16, None, 0, None) == -2  # block counts differ
+    W2 = qm(rows=16)
+    assert g(ctypes.byref(A), ctypes.byref(W2), FAKE, 8, None, 0, None) == -2  # ldy < N
+    A3 = qm(rows=8, q4=0x20004)                                                 # misaligned 4-bit plane
+    assert g(ctypes.byref(A3), ctypes.byref(W2), FAKE, 16, None, 0, None) == -6
+    kv = lib.mxs_quantize_kv
+    kv.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    assert kv(FAKE, 1, 4, 8, 100, FAKE, FAKE, None) == -2
+    assert kv(None, 1, 4, 8, 128, FAKE, FAKE, None) == -1

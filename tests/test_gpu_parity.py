@@ -1,0 +1,276 @@
+"""GPU parity: every entry point of libmxsens against the CPU oracle on the
+same seeded inputs (the oracle receives host copies of the device tensors).
+
+Bar: bit-exact Hdiag, scores, bit map, permutation, codes and scales (both
+sides follow one fp64 summation order and exact quantiser arithmetic);
+GEMM componentwise |Y - Y_ref| <= 1e-5 * (|Qa| |Qw|^T)[t, n] against the
+fp64 definition. Sizes span several tiles with ragged tails; the
+full-size workloads check sampled GEMM rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_gemm_hdiag_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GEMM_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def mx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bit_gemm_hdiag_amd as mx
+    return mx
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
+
+
+def assert_planes(Q, R, what=""):
+    for key in ("q8", "q6", "q4", "sc"):
+        g = getattr(Q, key).cpu().numpy().view(np.uint8)
+        r = R[key].view(np.uint8)
+        assert g.shape == r.shape, (what, key)
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, f"{what} {key}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def assert_gemm(Y, Yref, Yabs, what=""):
+    y = Y.cpu().numpy().astype(np.float64) if isinstance(Y, torch.Tensor) else Y
+    err = np.abs(y - Yref)
+    ok = err <= GEMM_RTOL * Yabs
+    assert ok.all(), f"{what}: {int((~ok).sum())} outputs off, worst rel {float((err / np.maximum(Yabs, 1e-300)).max()):.3e}"
+    nrm = np.linalg.norm(y - Yref) / max(np.linalg.norm(Yref), 1e-300)
+    assert nrm < 1e-6, f"{what}: normwise {nrm:.3e}"
+
+
+def layer(K, N, M, calib_rows, seed, dtype=torch.bfloat16, n_ext=None, n_mild=None):
+    gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS, n_ext, n_mild)
+    Xc = synth.activations(calib_rows, K, seed + synth.ROLE_CALIB, gains, dtype=dtype, device=DEV)
+    X = synth.activations(M, K, seed + synth.ROLE_X, gains, dtype=dtype, device=DEV)
+    W = synth.weights(N, K, seed + synth.ROLE_W, dtype=dtype, device=DEV)
+    return Xc, X, W
+
+
+# ------------------------------------------------------------------ quantize
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("R,K,budget", [(64, 256, (500, 1500)), (7, 1024, (500, 1500)),
+                                        (300, 4096, (300, 1000)), (33, 96, (0, 0))])
+def test_quantize_identity_and_perm(mx, orc, dtype, R, K, budget):
+    torch.manual_seed(R + K)
+    gains = synth.outlier_gains(K, 11, max(1, K // 1000), max(2, K // 100))
+    X = synth.activations(R, K, 12, gains, dtype=dtype, device=DEV)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
+    perm = torch.randperm(K, device=DEV).to(torch.int32)
+    Xh = host(X)
+    for p in (None, perm):
+        Q = mx.mxs_quantize(X, p, n8, n6, n4)
+        R_ = orc.quantize(Xh, None if p is None else p.cpu().numpy(), n8, n6, n4)
+        assert_planes(Q, R_, f"R={R} K={K} perm={p is not None}")
+
+
+def test_quantize_edge_values(mx, orc):
+    # zeros, subnormals, exponent clamp, huge values, NaN/Inf blocks, ties
+    K = 256
+    X = np.zeros((6, K), np.float32)
+    X[1, :32] = 2.0 ** -140
+    X[1, 32:64] = np.array([2.0 ** -122, 2.0 ** -127, 2.0 ** -149] * 10 + [0, 0], np.float32)
+    X[2, :] = np.float32(3.4e38) * np.sign(np.sin(np.arange(K)))
+    X[3, 5] = np.nan
+    X[3, 100] = np.inf
+    X[3, 200] = -np.inf
+    X[4, :] = (np.arange(K) % 16 - 8) * 0.5          # exact ties at every width
+    X[5, :] = np.random.default_rng(0).standard_normal(K) * 2.0 ** 100
+    for n8, n6, n4 in ((1, 0, 7), (2, 3, 3), (0, 0, 8), (8, 0, 0), (0, 8, 0)):
+        for dt in (torch.float32, torch.bfloat16):
+            Xd = torch.from_numpy(X).to(DEV).to(dt)
+            Q = mx.mxs_quantize(Xd, None, n8, n6, n4)
+            assert_planes(Q, orc.quantize(host(Xd), None, n8, n6, n4), f"edge {n8}/{n6}/{n4} {dt}")
+
+
+def test_quantize_strided_and_unaligned(mx, orc):
+    # ld > K and an fp32 leading dimension that is not a multiple of 4 (scalar loads)
+    base = torch.randn(50, 1031, device=DEV)
+    X = base[:, 3:3 + 1024]
+    n8, n6, n4 = 1, 6, 25
+    perm = torch.randperm(1024, device=DEV).to(torch.int32)
+    for p in (None, perm):
+        Q = mx.mxs_quantize(X, p, n8, n6, n4)
+        ref = orc.quantize(np.ascontiguousarray(host(X)), None if p is None else p.cpu().numpy(), n8, n6, n4)
+        assert_planes(Q, ref, "strided")
+    # odd output strides: planes as slices of wider buffers
+    q8 = torch.empty(50, 40, dtype=torch.int8, device=DEV)[:, 1:33]
+    q6 = torch.empty(50, 151, dtype=torch.uint8, device=DEV)[:, 1:145]
+    q4 = torch.empty(50, 403, dtype=torch.uint8, device=DEV)[:, 3:403]
+    sc = torch.empty(50, 33, dtype=torch.uint8, device=DEV)[:, 1:33]
+    out = mx.QMat(50, 1024, n8, n6, n4, q8, q6, q4, sc)
+    mx.mxs_quantize(X, perm, n8, n6, n4, out=out)
+    assert_planes(out, orc.quantize(np.ascontiguousarray(host(X)), perm.cpu().numpy(), n8, n6, n4), "odd ld")
+
+
+def test_quantize_empty(mx):
+    X = torch.empty(0, 256, device=DEV)
+    Q = mx.mxs_quantize(X, None, 1, 0, 7)
+    assert Q.rows == 0
+
+
+@pytest.mark.parametrize("T,H,D", [(2048, 8, 128), (5, 3, 64), (1, 1, 32)])
+def test_quantize_kv(mx, orc, T, H, D):
+    kv = synth.kv(T, H, D, 2004, device=DEV)
+    codes, scales = mx.mxs_quantize_kv(kv)
+    c_ref, s_ref = orc.quantize_kv(host(kv))
+    assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
+
+
+# ------------------------------------------------------------ calibrate/score
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M,K", [(64, 256), (1000, 96), (257, 4096), (8 * 2048, 4096)])
+def test_calibrate(mx, orc, dtype, M, K):
+    gains = synth.outlier_gains(K, 3, max(1, K // 1000), max(2, K // 100))
+    X = synth.activations(M, K, 1, gains, dtype=dtype, device=DEV)
+    h = mx.mxs_calibrate(X)
+    ref = orc.calibrate(host(X))
+    assert np.array_equal(h.cpu().numpy(), ref)
+
+
+def test_calibrate_in_calls_and_strided(mx, orc):
+    gains = synth.outlier_gains(4096, 2003)
+    X = synth.activations(8 * 2048, 4096, 2001, gains, device=DEV)
+    h = torch.zeros(4096, dtype=torch.float64, device=DEV)
+    ref = np.zeros(4096)
+    for i in range(8):
+        mx.mxs_calibrate(X[2048 * i:2048 * (i + 1)], h)
+        orc.calibrate(host(X[2048 * i:2048 * (i + 1)]), ref)
+    assert np.array_equal(h.cpu().numpy(), ref)
+    base = torch.randn(700, 200, device=DEV)
+    Xs = base[:, 5:197]                                  # ldx = 200, unaligned start
+    assert np.array_equal(mx.mxs_calibrate(Xs).cpu().numpy(), orc.calibrate(np.ascontiguousarray(host(Xs))))
+    assert not mx.mxs_calibrate(torch.empty(0, 64, device=DEV)).any()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N,K", [(256, 256), (1000, 96), (4096, 4096), (300, 14336)])
+def test_score(mx, orc, dtype, N, K):
+    W = synth.weights(N, K, 5, dtype=dtype, device=DEV)
+    hd = torch.rand(K, dtype=torch.float64, device=DEV) * 100
+    s = mx.mxs_score(W, hd)
+    ref = orc.score(host(W), hd.cpu().numpy())
+    assert np.array_equal(s.cpu().numpy(), ref)
+
+
+def test_score_nonfinite_block(mx, orc):
+    W = torch.randn(300, 128, device=DEV)
+    W[17, 40] = float("nan")
+    W[290, 100] = float("inf")
+    hd = torch.ones(128, dtype=torch.float64, device=DEV)
+    s = mx.mxs_score(W, hd).cpu().numpy()
+    ref = orc.score(host(W), hd.cpu().numpy())
+    assert np.array_equal(s, ref, equal_nan=True)
+    assert np.isnan(s[32:64]).all() and np.isnan(s[96:128]).all() and np.isfinite(s[:32]).all()
+
+
+# ------------------------------------------------------------------ allocate
+@pytest.mark.parametrize("K,budget", [(256, (500, 1500)), (1024, (500, 1500)), (4096, (300, 1000)),
+                                      (14336, (800, 2000)), (28672, (500, 1500)), (96, (0, 0))])
+def test_allocate(mx, orc, K, budget):
+    g = torch.Generator(device="cpu").manual_seed(K)
+    s = torch.rand(K, generator=g, dtype=torch.float64) ** 4
+    s[torch.randint(0, K, (K // 10,), generator=g)] = float(s[0])     # ties
+    s[3] = float("inf")
+    sd = s.to(DEV)
+    bits, perm = mx.mxs_allocate(sd, *budget)
+    rb, rp = orc.allocate(s.numpy(), *budget)
+    assert np.array_equal(bits.cpu().numpy(), rb) and np.array_equal(perm.cpu().numpy(), rp)
+
+
+# ----------------------------------------------------------------------- GEMM
+def gemm_case(mx, orc, M, N, K, budget, seed, dtype=torch.bfloat16, sample_rows=None):
+    Xc, X, W = layer(K, N, M, 512, seed, dtype)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(DEV)
+    A = mx.mxs_quantize(X, perm, n8, n6, n4)
+    B = mx.mxs_quantize(W, perm, n8, n6, n4)
+    Y = mx.mxs_mixed_gemm(A, B)
+    rows = np.arange(M) if sample_rows is None else sample_rows
+    A_ref = orc.quantize(host(X[torch.as_tensor(rows, device=DEV)]), perm.cpu().numpy(), n8, n6, n4)
+    B_ref = orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4)
+    Yref, Yabs = orc.mixed_gemm(A_ref, B_ref)
+    assert_gemm(Y.cpu().numpy()[rows].astype(np.float64), Yref, Yabs, f"M={M} N={N} K={K}")
+    return Y
+
+
+@pytest.mark.parametrize("M,N,K,budget", [(64, 256, 256, (500, 1500)), (77, 200, 1024, (500, 1500)),
+                                          (1, 300, 8192, (500, 1500)), (8, 130, 8192, (500, 1500)),
+                                          (32, 96, 8192, (500, 1500)), (130, 64, 4096, (300, 1000)),
+                                          (129, 257, 14336, (800, 2000)), (40, 50, 96, (0, 0)),
+                                          (33, 65, 512, (10000, 0)), (33, 65, 512, (0, 10000))])
+def test_mixed_gemm(mx, orc, M, N, K, budget):
+    gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N)
+
+
+def test_mixed_gemm_fp32_tiny_layer(mx, orc):
+    cfg = synth.CONFIGS[1]
+    gemm_case(mx, orc, cfg["M"], cfg["N"], cfg["K"], cfg["budget"], seed=1000, dtype=torch.float32)
+
+
+def test_mixed_gemm_q_proj_full_size_sampled(mx, orc):
+    rows = np.array([0, 1, 2, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
+    gemm_case(mx, orc, 2048, 4096, 4096, (500, 1500), seed=2000, sample_rows=rows)
+
+
+def test_mixed_gemm_strided_output_and_determinism(mx, orc):
+    Xc, X, W = layer(1024, 160, 70, 256, 77)
+    perm = torch.arange(1024, dtype=torch.int32, device=DEV)
+    A = mx.mxs_quantize(X, perm, 1, 6, 25)
+    B = mx.mxs_quantize(W, perm, 1, 6, 25)
+    Ybig = torch.full((70, 200), 7.0, device=DEV)
+    mx.mxs_mixed_gemm(A, B, Y=Ybig[:, 10:170])
+    Y2 = mx.mxs_mixed_gemm(A, B)
+    assert torch.equal(Ybig[:, 10:170], Y2)
+    assert (Ybig[:, :10] == 7).all() and (Ybig[:, 170:] == 7).all()
+    Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), None, 1, 6, 25), orc.quantize(host(W), None, 1, 6, 25))
+    assert_gemm(Y2, Yref, Yabs, "strided")
+
+
+# ------------------------------------------------------------------- pipeline
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_pipeline_matches_oracle(mx, orc, cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    dt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
+    K, N, M = cfg["K"], cfg["N"], cfg["M"]
+    seed = 1000 * cfg_id
+    gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS, cfg.get("n_extreme"), cfg.get("n_mild"))
+    if cfg_id == 1:
+        X = synth.activations(M, K, seed + synth.ROLE_X, gains, dtype=dt, device=DEV)
+        Xc = X
+    else:
+        Xc = synth.activations(cfg["calib_rows"], K, seed + synth.ROLE_CALIB, gains, dtype=dt, device=DEV)
+        X = synth.activations(M, K, seed + synth.ROLE_X, gains, dtype=dt, device=DEV)
+    W = synth.weights(N, K, seed + synth.ROLE_W, dtype=dt, device=DEV)
+    bp8, bp6 = cfg["budget"]
+    h = mx.mxs_calibrate(Xc)
+    s = mx.mxs_score(W, h)
+    bits, perm = mx.mxs_allocate(s, bp8, bp6)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, bp8, bp6)
+    A = mx.mxs_quantize(X, perm, n8, n6, n4)
+    B = mx.mxs_quantize(W, perm, n8, n6, n4)
+    Y = mx.mxs_mixed_gemm(A, B)
+
+    h_ref = orc.calibrate(host(Xc))
+    s_ref = orc.score(host(W), h_ref)
+    b_ref, p_ref = orc.allocate(s_ref, bp8, bp6)
+    assert np.array_equal(h.cpu().numpy(), h_ref)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(bits.cpu().numpy(), b_ref) and np.array_equal(perm.cpu().numpy(), p_ref)
+    rows = np.arange(M) if M <= 64 else np.array([0, 5, 700, M - 1])
+    A_ref = orc.quantize(host(X[torch.as_tensor(rows, device=DEV)]), p_ref, n8, n6, n4)
+    B_ref = orc.quantize(host(W), p_ref, n8, n6, n4)
+    full_A = orc.quantize(host(X), p_ref, n8, n6, n4) if M <= 2048 else None
+    if full_A is not None:
+        assert_planes(A, full_A, "X planes")
+    assert_planes(B, B_ref, "W planes")
+    Yref, Yabs = orc.mixed_gemm(A_ref, B_ref)
+    assert_gemm(Y.cpu().numpy()[rows].astype(np.float64), Yref, Yabs, f"config {cfg_id}")
