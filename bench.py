@@ -1,0 +1,235 @@
+"""Benchmark of the MXSens hot path on one MI355X.
+
+One step = one pass of every stage over the Llama-3-8B q_proj-shaped layer
+(synthetic, seeded): calibrate over 8 x 2048 tokens, score, allocate,
+quantize W, quantize X, the mixed 8/6/4-bit GEMM (2048 x 4096 x 4096) and
+MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128). Inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
+(2 M N K per step over the step time); per-stage times, TOPS and GB/s are
+in `stages`; `roofline` is for the dominant kernel; `cpu_baseline` is the
+CPU oracle timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+INT8_PEAK = 5.0e15         # OP/s, MI355X dense int8 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(mx, synth, torch, dev):
+    cfg = synth.CONFIGS[2]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    bp8, bp6 = cfg["budget"]
+    seed = 2000
+    gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+    w = dict(
+        M=M, N=N, K=K, bp8=bp8, bp6=bp6, calib_rows=cfg["calib_rows"], kv_shape=cfg["kv"],
+        Xc=synth.activations(cfg["calib_rows"], K, seed + synth.ROLE_CALIB, gains, device=dev),
+        X=synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev),
+        W=synth.weights(N, K, seed + synth.ROLE_W, device=dev),
+        Kc=synth.kv(cfg["kv"]["T"], cfg["kv"]["H"], cfg["kv"]["D"], seed + synth.ROLE_KV, device=dev),
+        Vc=synth.kv(cfg["kv"]["T"], cfg["kv"]["H"], cfg["kv"]["D"], seed + synth.ROLE_KV + 8, device=dev),
+    )
+    n8, n6, n4 = mx.mxs_budget_blocks(K, bp8, bp6)
+    w["blocks"] = (n8, n6, n4)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    w["hdiag"] = torch.zeros(K, dtype=torch.float64, device=dev)
+    w["score"] = torch.empty(K, dtype=torch.float64, device=dev)
+    w["bits"] = torch.empty(K, **u8)
+    w["perm"] = torch.empty(K, dtype=torch.int32, device=dev)
+    w["ws_cal"] = torch.empty(max(1, mx.mxs_calibrate_workspace(w["calib_rows"], K)), **u8)
+    w["ws_sc"] = torch.empty(max(1, mx.mxs_score_workspace(N, K)), **u8)
+    w["Aq"] = mx.qmat_alloc(M, K, n8, n6, n4, dev)
+    w["Wq"] = mx.qmat_alloc(N, K, n8, n6, n4, dev)
+    w["Y"] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    w["ws_g"] = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(w["Aq"], w["Wq"])), **u8)
+    T, H, D = cfg["kv"]["T"], cfg["kv"]["H"], cfg["kv"]["D"]
+    w["kc"] = [torch.empty((T, H, D // 2), **u8) for _ in range(2)]
+    w["ks"] = [torch.empty((T, H, D // 32), **u8) for _ in range(2)]
+    return w
+
+
+def stage_fns(mx, w):
+    n8, n6, n4 = w["blocks"]
+    return [
+        ("calibrate", lambda: (w["hdiag"].zero_(), mx.mxs_calibrate(w["Xc"], w["hdiag"], ws=w["ws_cal"]))),
+        ("score", lambda: mx.mxs_score(w["W"], w["hdiag"], w["score"], ws=w["ws_sc"])),
+        ("allocate", lambda: mx.mxs_allocate(w["score"], w["bp8"], w["bp6"], w["bits"], w["perm"])),
+        ("quantize_w", lambda: mx.mxs_quantize(w["W"], w["perm"], n8, n6, n4, out=w["Wq"])),
+        ("quantize_x", lambda: mx.mxs_quantize(w["X"], w["perm"], n8, n6, n4, out=w["Aq"])),
+        ("mixed_gemm", lambda: mx.mxs_mixed_gemm(w["Aq"], w["Wq"], w["Y"], ws=w["ws_g"])),
+        ("quantize_kv", lambda: (mx.mxs_quantize_kv(w["Kc"], w["kc"][0], w["ks"][0]),
+                                 mx.mxs_quantize_kv(w["Vc"], w["kc"][1], w["ks"][1]))),
+    ]
+
+
+def algorithmic_work(w):
+    """Bytes (or ops) each stage must move (or do) by definition."""
+    M, N, K = w["M"], w["N"], w["K"]
+    n8, n6, n4 = w["blocks"]
+    nb = K // 32
+    packed = 32 * n8 + 24 * n6 + 16 * n4 + nb          # bytes per quantised row
+    T, H, D = w["kv_shape"]["T"], w["kv_shape"]["H"], w["kv_shape"]["D"]
+    return {
+        "calibrate": dict(bytes=w["calib_rows"] * K * 2 + 16 * K),
+        "score": dict(bytes=N * K * 2 + 24 * K),
+        "allocate": dict(bytes=K * 8 + K * 5),
+        "quantize_w": dict(bytes=N * K * 2 + N * packed + 4 * K),
+        "quantize_x": dict(bytes=M * K * 2 + M * packed + 4 * K),
+        "mixed_gemm": dict(ops=2 * M * N * K, bytes=(M + N) * packed + 4 * M * N),
+        "quantize_kv": dict(bytes=2 * T * H * D * (2 + 0.5 + 1 / 32)),
+    }
+
+
+def time_stage(torch, fn, reps):
+    for _ in range(3):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps * 1e-3
+
+
+def cpu_baseline(w, torch):
+    """The CPU oracle on a bounded sample of the step, extrapolated to one step."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    K, N, M = w["K"], w["N"], w["M"]
+    n8, n6, n4 = w["blocks"]
+    Xc = w["Xc"].float().cpu().numpy()
+    Wh = w["W"].float().cpu().numpy()
+    X_rows = 1024
+    Xh = w["X"][:X_rows].float().cpu().numpy()
+    kv = w["Kc"].float().cpu().numpy()
+    t = {}
+    t0 = time.perf_counter(); h = oracle.calibrate(Xc); t["calibrate"] = time.perf_counter() - t0
+    t0 = time.perf_counter(); s = oracle.score(Wh, h); t["score"] = time.perf_counter() - t0
+    t0 = time.perf_counter(); bits, perm = oracle.allocate(s, w["bp8"], w["bp6"]); t["allocate"] = time.perf_counter() - t0
+    t0 = time.perf_counter(); Wq = oracle.quantize(Wh, perm, n8, n6, n4); t["quantize_w"] = time.perf_counter() - t0
+    t0 = time.perf_counter(); Aq = oracle.quantize(Xh, perm, n8, n6, n4); t["quantize_x"] = (time.perf_counter() - t0) * (M / X_rows)
+    t0 = time.perf_counter(); oracle.mixed_gemm(Aq, Wq); t["mixed_gemm"] = (time.perf_counter() - t0) * (M / X_rows)
+    t0 = time.perf_counter(); oracle.quantize_kv(kv); t["quantize_kv"] = 2 * (time.perf_counter() - t0)
+    step = sum(t.values())
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=2 * M * N * K / step / 1e12, unit="TOPS", cores=cores, kind="oracle",
+                sample=f"calibrate, score, allocate, quantize W in full and one KV tensor in full (x2 for "
+                       f"K and V); quantize X and the GEMM on "
+                       f"{X_rows} of {M} token rows; per-stage times scaled to the full step",
+                step_s_extrapolated=step, stage_s=t)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(the hot path would shard by rows and columns; no collective is built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_gemm_hdiag_amd as mx
+    from bit_gemm_hdiag_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("building workload")
+    w = build_workload(mx, synth, torch, dev)
+    stages = stage_fns(mx, w)
+
+    def step():
+        for _, fn in stages:
+            fn()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    step_s = s.elapsed_time(e) / args.steps * 1e-3
+    log(f"step {step_s * 1e3:.3f} ms")
+
+    work = algorithmic_work(w)
+    stage_out = {}
+    for name, fn in stages:
+        t = time_stage(torch, fn, args.stage_reps)
+        d = dict(ms=t * 1e3)
+        if "bytes" in work[name]:
+            d["GBps"] = work[name]["bytes"] / t / 1e9
+            d["hbm_frac"] = work[name]["bytes"] / t / HBM_PEAK
+        if "ops" in work[name]:
+            d["TOPS"] = work[name]["ops"] / t / 1e12
+            d["int8_mfma_frac"] = work[name]["ops"] / t / INT8_PEAK
+        stage_out[name] = d
+        log(name, json.dumps(d))
+
+    gemm = stage_out["mixed_gemm"]
+    M, N, K = w["M"], w["N"], w["K"]
+    ops = 2 * M * N * K
+    roofline = dict(bound="mfma", achieved=gemm["TOPS"], peak=INT8_PEAK / 1e12, unit="TOP/s",
+                    frac=gemm["TOPS"] * 1e12 / INT8_PEAK, traffic=None,
+                    kernel="mixed_gemm (k_gemm_blockwise)", algorithmic_ops_per_launch=ops)
+    qx = stage_out["quantize_x"]
+    out = {
+        "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
+        "value": ops / step_s / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 MFMA / fp32 epilogue / fp64 sums",
+        "data": "synthetic (seeded outlier-channel activations, Student-t weights, bf16)",
+        "config": {"workload": "Llama-3-8B q_proj prefill layer: calibrate 8x2048 tokens, score/allocate/"
+                               "quantize W 4096x4096, quantize X 2048x4096, mixed GEMM 2048x4096x4096 "
+                               "(5/15/80% 8/6/4-bit, 6/20/102 blocks), MXINT4 K and V 2048x8x128",
+                   "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)"},
+        "gemm_tops": gemm["TOPS"],
+        "quantize_gbps": {"w": stage_out["quantize_w"]["GBps"], "x": qx["GBps"],
+                          "kv": stage_out["quantize_kv"]["GBps"]},
+        "stages": stage_out,
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -145,17 +145,437 @@ QView view_of(const mxs_qmat &q) {
     return QView{q.q8, q.ld8, q.q6, q.ld6, q.q4, q.ld4, q.sc, q.lds};
 }
 
+// ---------------------------------------------------------------------------
+// Prefill path (M >= kPrefillMinRows): operand preparation + grouped GEMM.
+//
+// The per-block epilogue above costs 3 VALU operations per output and block,
+// six times the MFMA time of the block. The prefill path removes it by exact
+// exponent alignment over groups = aligned windows of kG consecutive blocks.
+// If a window lies inside one width class and a row's nonzero blocks in it
+// have scale exponents within F of each other (F = 4, 2, 0 for 4-, 6-, 8-bit
+// codes: the headroom an int8 byte has over the code), code c of block b is
+// stored as c << (s_b - base) with base = max s_b - F; aligned A and W rows
+// make the int32 MFMA sum over the window exact, times 2^(base_a + base_w):
+// one epilogue per window. Other rows keep c << F with scale 2^(s_b - F) and
+// the wave takes one epilogue per block for that window. Window sums stay
+// below 2^24 (16 * 32 * 127^2), so the int32 -> fp32 conversion is exact and
+// only the fp32 accumulation across windows rounds.
+//
+// Prepared operand (workspace), per matrix with R rows padded to Rp and K
+// padded to Kp = whole windows:
+//   codes int8 [Rp, Kp]   shifted codes, natural k order inside each block
+//   cs    f32  [nbp, Rp]  code scale of (row, block); negative when the
+//                         row's window is not aligned; -Inf for a NaN/Inf block
+// Padding rows and blocks hold zero codes and scale +1.
+constexpr int kG = 16;              // blocks per alignment window
+constexpr int kPrefillMinRows = 64; // smaller M uses the per-block kernel
+
+__device__ __forceinline__ int sext(uint32_t v, int bits) {
+    return (int)(v << (32 - bits)) >> (32 - bits);
+}
+
+// codes c[0..31] of block `b` (global block index) of row r
+__device__ __forceinline__ void unpack_block(const QView &Q, int64_t r, int64_t b, int cls,
+                                             int32_t n8, int32_t n6, int c[32]) {
+    if (cls == 8) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(Q.q8 + r * Q.ld8 + 32 * b);
+        const uint4 x = p[0], y = p[1];
+        const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 2] >> (8 * (i & 3))) & 255u, 8);
+    } else if (cls == 6) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(Q.q6 + r * Q.ld6 + 24 * (b - n8));
+        uint32_t w[7];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) w[i] = p[i];
+        w[6] = 0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            // 24-bit group g starts at bit 24 g of the 192-bit little-endian stream
+            const int bit = 24 * g;
+            const uint32_t grp = __builtin_amdgcn_alignbit(w[(bit >> 5) + 1], w[bit >> 5], bit & 31);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[4 * g + j] = sext((grp >> (6 * j)) & 63u, 6);
+        }
+    } else {
+        const uint2 *p = reinterpret_cast<const uint2 *>(Q.q4 + r * Q.ld4 + 16 * (b - n8 - n6));
+        const uint2 x = p[0], y = p[1];
+        const uint32_t w[4] = {x.x, x.y, y.x, y.y};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 3] >> (4 * (i & 7))) & 15u, 4);
+    }
+}
+
+// One workgroup prepares a 64-row x 16-block window of one matrix: thread t
+// takes block t % 16 of rows t / 16 + 16 i (reads and code writes run along
+// the row), the window reduction is a 16-lane butterfly, and the scales are
+// transposed through LDS so that they are written 64 rows at a time.
+struct PrepJob {
+    QView Q;
+    int64_t R, Rp;
+    int8_t *codes;
+    float *cs;
+    int64_t tiles_r;      // Rp / 64
+};
+
+// Windows start at the first block of each width class: window j of class
+// segment [lo, hi) covers blocks lo + kG j .. min(hi, lo + kG (j + 1)) - 1.
+struct Segs {
+    int32_t lo[3], hi[3], F[3], cls[3];
+    int32_t win_base[4];   // prefix count of windows per segment
+};
+
+__host__ __device__ inline Segs make_segs(int32_t n8, int32_t n6, int32_t n4) {
+    Segs S;
+    const int32_t n[3] = {n8, n6, n4};
+    int32_t lo = 0, wb = 0;
+    for (int i = 0; i < 3; ++i) {
+        S.lo[i] = lo;
+        S.hi[i] = lo + n[i];
+        S.F[i] = i == 0 ? 0 : (i == 1 ? 2 : 4);
+        S.cls[i] = i == 0 ? 8 : (i == 1 ? 6 : 4);
+        S.win_base[i] = wb;
+        wb += (n[i] + kG - 1) / kG;
+        lo += n[i];
+    }
+    S.win_base[3] = wb;
+    return S;
+}
+
+// One workgroup prepares a 64-row x (one window) tile of one matrix: thread t
+// takes block t % 16 of the window for rows t / 16 + 16 i (reads and code
+// writes run along the row), the window reduction is a 16-lane butterfly, and
+// the scales are transposed through LDS to be written 64 rows at a time.
+// Prepared rows are padded to a multiple of 16 blocks with zero codes.
+__global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64_t ntiles_a, int64_t K,
+                                                   int64_t Kp, Segs S) {
+    __shared__ float s_cs[kG][64];
+    const bool is_a = blockIdx.x < ntiles_a;
+    const PrepJob &J = is_a ? ja : jw;
+    const int64_t tile = is_a ? blockIdx.x : blockIdx.x - ntiles_a;
+    const int64_t rt = tile % J.tiles_r, win = tile / J.tiles_r;   // win < windows + pad windows
+    const int tid = threadIdx.x, blk = tid & 15;
+    const int64_t nb = K / 32, nbp = Kp / 32;
+    int sg = 0;
+    int64_t b;
+    bool real_blk;
+    if (win < S.win_base[3]) {
+        sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : 2);
+        b = S.lo[sg] + (win - S.win_base[sg]) * kG + blk;
+        real_blk = b < S.hi[sg];
+    } else {   // padding blocks nb .. nbp - 1, 16 per pad window
+        b = nb + (win - S.win_base[3]) * kG + blk;
+        real_blk = false;
+    }
+    const int cls = S.cls[sg], F = S.F[sg];
+    const bool in_range = b < nbp;
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+        const int lr = (tid >> 4) + 16 * i;
+        const int64_t r = rt * 64 + lr;
+        const bool real = real_blk && r < J.R;
+        int c[32];
+        int s = 0;
+        bool bad = false, nz = false;
+        if (real) {
+            unpack_block(J.Q, r, b, cls, S.hi[0], S.hi[1] - S.hi[0], c);
+            const uint32_t byte = J.Q.sc[r * J.Q.lds + b];
+            bad = byte == 0xFFu;
+            s = (int)byte - 127;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) nz |= c[k] != 0;
+            if (bad) nz = false;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) c[k] = 0;
+        }
+        int smax = nz ? s : -100000, smin = nz ? s : 100000, anybad = bad;
+#pragma unroll
+        for (int off = 1; off < kG; off <<= 1) {
+            smax = max(smax, __shfl_xor(smax, off));
+            smin = min(smin, __shfl_xor(smin, off));
+            anybad |= __shfl_xor(anybad, off);
+        }
+        const bool allzero = smax == -100000;
+        const bool aligned = !anybad && (allzero || smax - smin <= F);
+        const int base = allzero ? 0 : smax - F;
+        const int shift = aligned ? (nz ? s - base : 0) : F;
+        float scale;
+        if (!real) scale = 1.0f;
+        else if (bad) scale = -__builtin_inff();
+        else scale = aligned ? __builtin_ldexpf(1.0f, base) : -__builtin_ldexpf(1.0f, s - F);
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v |= (((uint32_t)c[4 * k + j] << shift) & 255u) << (8 * j);
+            w[k] = v;
+        }
+        if (in_range && (real_blk || b >= nb)) {
+            uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * b);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+        s_cs[blk][lr] = scale;
+    }
+    __syncthreads();
+    {
+        const int bb = tid >> 4, part = tid & 15;
+        const int64_t ob = b - blk + bb;   // block of this transposed slice
+        const bool ok = win < S.win_base[3] ? ob < S.hi[sg] : ob < nbp;
+        if (ok) {
+            const float4 v = *reinterpret_cast<const float4 *>(&s_cs[bb][4 * part]);
+            *reinterpret_cast<float4 *>(J.cs + ob * J.Rp + rt * 64 + 4 * part) = v;
+        }
+    }
+}
+
+// Grouped int8 GEMM over prepared operands.
+//
+// Workgroup: 8 waves (4 x 2), tile 256 (A rows) x 128 (W rows); each wave
+// owns 64 x 64 outputs as 2 x 2 MFMA tiles (64 int32 + 64 fp32 accumulators
+// per lane, two waves per SIMD). K advances 2 blocks (64 bytes of every row)
+// per stage: each thread prefetches its share of the next stage into
+// registers (global_load_dwordx4) while the waves run the MFMAs of the
+// current stage out of LDS, then stores it into the other LDS buffer; one
+// barrier per stage. (Direct global->LDS loads measured ~1.7x slower into LDS
+// on gfx950 than this register path.) Within a stage, row r keeps its four
+// 16-byte chunks c at slot c ^ ((r >> 2) & 3): the 16 lanes of one LDS read
+// pass (16 consecutive rows, same chunk) touch 16 distinct bank groups.
+constexpr int kGBM = 256, kGBN = 128;    // workgroup tile
+constexpr int kSB = 2;                   // blocks per stage
+constexpr int kStA = kGBM * kSB * 32;    // 16 KiB of A codes per stage
+constexpr int kStW = kGBN * kSB * 32;    //  8 KiB of W codes
+constexpr int kStCA = kSB * kGBM * 4;    //  2 KiB of A scales [blk][row]
+constexpr int kStCW = kSB * kGBN * 4;    //  1 KiB of W scales [blk][row]
+constexpr int kStage = kStA + kStW + kStCA + kStCW;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(512, 1) void k_gemm_grouped(
+    const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
+    const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
+    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy) {
+    __shared__ __attribute__((aligned(16))) int8_t smem[2 * kStage];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+
+    // tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
+    // takes a contiguous run of tiles; runs sweep groups of 8 row-tiles
+    const int64_t tilesM = Mp / kGBM, tilesN = Np / kGBN, ntiles = tilesM * tilesN;
+    int64_t t = blockIdx.x;
+    if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+    const int64_t per_group = 8 * tilesN;
+    const int64_t gid = t / per_group, first_m = gid * 8;
+    const int64_t gsz = tilesM - first_m < 8 ? tilesM - first_m : 8;
+    const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
+    const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
+    const int nstage = (nb + kSB - 1) / kSB;
+    const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
+
+    // this thread's share of a stage: A rows rA0, rA1 and W row rW, 16-byte
+    // chunk `ch` of the row's 64 stage bytes, plus one 16-byte piece of the
+    // scales (threads < 192)
+    const int lr = tid >> 2, ch = tid & 3;
+    const int rA0 = lr, rA1 = lr + 128, rW = lr;
+    const int8_t *gA0 = Aq + (m0 + rA0) * Kp + ch * 16;
+    const int8_t *gA1 = Aq + (m0 + rA1) * Kp + ch * 16;
+    const int8_t *gW = Wq + (n0 + rW) * Kp + ch * 16;
+    const int dA0 = rA0 * 64 + ((ch ^ ((rA0 >> 2) & 3)) << 4);
+    const int dA1 = rA1 * 64 + ((ch ^ ((rA1 >> 2) & 3)) << 4);
+    const int dW = kStA + rW * 64 + ((ch ^ ((rW >> 2) & 3)) << 4);
+    // scales: threads 0..127 -> A [blk = tid / 64][rows 4 (tid % 64) ..],
+    // threads 128..191 -> W [blk = (tid - 128) / 32][rows 4 ((tid - 128) % 32) ..]
+    const bool hasC = tid < 192;
+    const float *gC = tid < 128 ? csA + (tid >> 6) * Mp + m0 + 4 * (tid & 63)
+                                : csW + ((tid - 128) >> 5) * Np + n0 + 4 * ((tid - 128) & 31);
+    const int64_t cstride = tid < 128 ? 2 * Mp : 2 * Np;
+    const int dC = tid < 128 ? kStA + kStW + tid * 16 : kStA + kStW + kStCA + (tid - 128) * 16;
+
+    uint4 pa0, pa1, pw;
+    float4 pc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load = [&](int st) {
+        const int64_t kb = (int64_t)st * (kSB * 32);
+        pa0 = *reinterpret_cast<const uint4 *>(gA0 + kb);
+        pa1 = *reinterpret_cast<const uint4 *>(gA1 + kb);
+        pw = *reinterpret_cast<const uint4 *>(gW + kb);
+        if (hasC) pc = *reinterpret_cast<const float4 *>(gC + st * cstride);
+    };
+    auto store = [&](int buf) {
+        int8_t *base = smem + buf * kStage;
+        *reinterpret_cast<uint4 *>(base + dA0) = pa0;
+        *reinterpret_cast<uint4 *>(base + dA1) = pa1;
+        *reinterpret_cast<uint4 *>(base + dW) = pw;
+        if (hasC) *reinterpret_cast<float4 *>(base + dC) = pc;
+    };
+
+    // LDS offsets of this lane's MFMA fragments (stage-relative), per block
+    int offA[kSB][2], offW[kSB][2];
+#pragma unroll
+    for (int blk = 0; blk < kSB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = 2 * blk + h;
+            const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
+            offA[blk][i] = ra * 64 + ((c ^ ((ra >> 2) & 3)) << 4);
+            offW[blk][i] = kStA + rw * 64 + ((c ^ ((rw >> 2) & 3)) << 4);
+        }
+
+    float acc[2][2][16];
+    v16i I[2][2];
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            I[i][j] = zero;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        }
+
+    load(0);
+    store(0);
+    __syncthreads();
+    bool aligned = true;
+    for (int st = 0; st < nstage; ++st) {
+        if (st + 1 < nstage) load(st + 1);
+        const int8_t *sbase = smem + (st & 1) * kStage;
+        const float *sCA = reinterpret_cast<const float *>(sbase + kStA + kStW);
+        const float *sCW = sCA + kSB * kGBM;
+#pragma unroll
+        for (int blk = 0; blk < kSB; ++blk) {
+            const int b = st * kSB + blk;
+            if (b >= nb) break;
+            v4i fa[2], fw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i] = *reinterpret_cast<const v4i *>(sbase + offA[blk][i]);
+                fw[i] = *reinterpret_cast<const v4i *>(sbase + offW[blk][i]);
+            }
+            // window position of block b (scalar selects: no table lookups)
+            const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
+            const int hi = b >= h1 ? nb : (b >= h0 ? h1 : h0);
+            const int off = b - lo;
+            const bool first = (off % kG) == 0;
+            const bool last = (off % kG) == kG - 1 || b == hi - 1;
+            if (first) {
+                const float va = sCA[blk * kGBM + wm * 64 + lane];
+                const float vw = sCW[blk * kGBN + wn * 64 + lane];
+                aligned = __all(va > 0.f && vw > 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fw[j], I[i][j], 0, 0, 0);
+            // an aligned window has one scale per row for all its blocks, so
+            // the scales of its last block serve the whole window
+            if (last || !aligned) {
+                float cw[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) cw[j] = __builtin_fabsf(sCW[blk * kGBN + wn * 64 + j * 32 + l32]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sCA + blk * kGBM + wm * 64 + i * 32 + 8 * q + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float sa = __builtin_fabsf(v[e]);
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                acc[i][j][4 * q + e] = __builtin_fmaf((float)I[i][j][4 * q + e], sa * cw[j], acc[i][j][4 * q + e]);
+                        }
+                    }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) I[i][j] = zero;
+            }
+        }
+        if (st + 1 < nstage) {
+            store((st + 1) & 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 32 + l32;
+            if (col >= N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * q + 4 * h + r;
+                    if (row < M) Y[row * ldy + col] = acc[i][j][4 * q + r];
+                }
+        }
+}
+
+struct PrepLayout {
+    int64_t Mp, Np, Kp;
+    size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
+    PrepLayout L;
+    L.Mp = ceil_div(A.rows, kGBM) * kGBM;
+    L.Np = ceil_div(W.rows, kGBN) * kGBN;
+    L.Kp = ceil_div(A.K, 32 * kSB) * (32 * kSB);   // whole stages
+    const int64_t nbp = L.Kp / 32;
+    size_t off = 0;
+    L.a_codes = off; off = align256(off + (size_t)L.Mp * L.Kp);
+    L.w_codes = off; off = align256(off + (size_t)L.Np * L.Kp);
+    L.a_cs = off;    off = align256(off + (size_t)nbp * L.Mp * 4);
+    L.w_cs = off;    off = align256(off + (size_t)nbp * L.Np * 4);
+    L.total = off;
+    return L;
+}
+
+bool use_prefill(const mxs_qmat &A) { return A.rows >= kPrefillMinRows; }
+
 }  // namespace
 
-size_t gemm_workspace(const mxs_qmat &, const mxs_qmat &) { return 0; }
+size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
+    if (!use_prefill(A) || W.rows == 0) return 0;
+    return prep_layout(A, W).total;
+}
 
 hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
-                             void *, size_t, hipStream_t st) {
+                             void *ws, size_t, hipStream_t st) {
     const int64_t M = A.rows, N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
-    hipLaunchKernelGGL(k_gemm_blockwise, grid, dim3(256), 0, st, view_of(A), view_of(W), M, N,
-                       A.n8, A.n6, A.n4, Y, ldy);
+    if (!use_prefill(A)) {
+        const dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
+        hipLaunchKernelGGL(k_gemm_blockwise, grid, dim3(256), 0, st, view_of(A), view_of(W), M, N,
+                           A.n8, A.n6, A.n4, Y, ldy);
+        return hipGetLastError();
+    }
+    const PrepLayout L = prep_layout(A, W);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int8_t *ac = reinterpret_cast<int8_t *>(base + L.a_codes);
+    int8_t *wc = reinterpret_cast<int8_t *>(base + L.w_codes);
+    float *acs = reinterpret_cast<float *>(base + L.a_cs);
+    float *wcs = reinterpret_cast<float *>(base + L.w_cs);
+    const Segs S = make_segs(A.n8, A.n6, A.n4);
+    const int64_t nb = A.K / 32, nbp = L.Kp / 32;
+    const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
+    PrepJob ja{view_of(A), M, L.Mp, ac, acs, L.Mp / 64};
+    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
+    const int64_t ta = ja.tiles_r * windows, tw = jw.tiles_r * windows;
+    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
+    hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
     return hipGetLastError();
 }
 

@@ -211,6 +211,28 @@ def test_mixed_gemm(mx, orc, M, N, K, budget):
     gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N)
 
 
+@pytest.mark.parametrize("M,N,K,budget", [(200, 300, 1024, (500, 1500)), (64, 128, 8192, (300, 1000))])
+def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
+    # per-block scales spread over +-2^12 so that many (row, group) pairs cannot
+    # share one exponent: exercises the per-block path next to aligned groups
+    g = torch.Generator(device="cpu").manual_seed(M + N)
+    X = torch.randn(M, K, generator=g) * 2.0 ** torch.randint(-12, 13, (M, K // 32), generator=g).repeat_interleave(32, 1)
+    W = torch.randn(N, K, generator=g) * 2.0 ** torch.randint(-12, 13, (N, K // 32), generator=g).repeat_interleave(32, 1)
+    X[:, 40:72] = 0.0                                   # all-zero blocks inside groups
+    W[5, 100] = float("nan") if M == 200 else W[5, 100]  # one non-finite block
+    X, W = X.to(DEV).to(torch.bfloat16), W.to(DEV).to(torch.bfloat16)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
+    perm = torch.randperm(K, generator=g).to(torch.int32).to(DEV)
+    A = mx.mxs_quantize(X, perm, n8, n6, n4)
+    B = mx.mxs_quantize(W, perm, n8, n6, n4)
+    Y = mx.mxs_mixed_gemm(A, B).cpu().numpy().astype(np.float64)
+    Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), perm.cpu().numpy(), n8, n6, n4),
+                                orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4))
+    nan_ref = np.isnan(Yref)
+    assert np.array_equal(np.isnan(Y), nan_ref)
+    assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), "spread")
+
+
 def test_mixed_gemm_fp32_tiny_layer(mx, orc):
     cfg = synth.CONFIGS[1]
     gemm_case(mx, orc, cfg["M"], cfg["N"], cfg["K"], cfg["budget"], seed=1000, dtype=torch.float32)
