@@ -335,20 +335,24 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
 //
 // Workgroup: 8 waves (4 x 2), tile 256 (A rows) x 128 (W rows); each wave
 // owns 64 x 64 outputs as 2 x 2 MFMA tiles (64 int32 + 64 fp32 accumulators
-// per lane, two waves per SIMD). K advances 2 blocks (64 bytes of every row)
-// per stage: each thread prefetches its share of the next stage into
-// registers (global_load_dwordx4) while the waves run the MFMAs of the
-// current stage out of LDS, then stores it into the other LDS buffer; one
-// barrier per stage. (Direct global->LDS loads measured ~1.7x slower into LDS
-// on gfx950 than this register path.) Within a stage, row r keeps its four
-// 16-byte chunks c at slot c ^ ((r >> 2) & 3): the 16 lanes of one LDS read
-// pass (16 consecutive rows, same chunk) touch 16 distinct bank groups.
+// per lane, two waves per SIMD). K advances kSB = 4 blocks (128 bytes of
+// every row) per stage through two LDS buffers. Latency hiding:
+//  - global loads run one stage ahead: each thread loads its share of the
+//    next stage into registers while the current stage is computed and then
+//    stores it into the other buffer; one barrier per stage;
+//  - LDS fragment reads run one block ahead of the MFMAs that use them.
+// (Direct global->LDS loads measured ~1.7x slower into LDS on gfx950 than
+// this register path.) Within a stage, row r keeps its eight 16-byte chunks c
+// at slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS read pass (16
+// consecutive rows, same chunk) then cover all 16 16-byte bank groups of a
+// 256-byte row of banks.
 constexpr int kGBM = 256, kGBN = 128;    // workgroup tile
-constexpr int kSB = 2;                   // blocks per stage
-constexpr int kStA = kGBM * kSB * 32;    // 16 KiB of A codes per stage
-constexpr int kStW = kGBN * kSB * 32;    //  8 KiB of W codes
-constexpr int kStCA = kSB * kGBM * 4;    //  2 KiB of A scales [blk][row]
-constexpr int kStCW = kSB * kGBN * 4;    //  1 KiB of W scales [blk][row]
+constexpr int kSB = 4;                   // blocks per stage
+constexpr int kRowB = kSB * 32;          // stage bytes per row (128)
+constexpr int kStA = kGBM * kRowB;       // 32 KiB of A codes per stage
+constexpr int kStW = kGBN * kRowB;       // 16 KiB of W codes
+constexpr int kStCA = kSB * kGBM * 4;    //  4 KiB of A scales [blk][row]
+constexpr int kStCW = kSB * kGBN * 4;    //  2 KiB of W scales [blk][row]
 constexpr int kStage = kStA + kStW + kStCA + kStCW;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
     const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
     const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
     int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy) {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2 * kStage];
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -376,41 +380,48 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
     const int nstage = (nb + kSB - 1) / kSB;
     const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
 
-    // this thread's share of a stage: A rows rA0, rA1 and W row rW, 16-byte
-    // chunk `ch` of the row's 64 stage bytes, plus one 16-byte piece of the
-    // scales (threads < 192)
-    const int lr = tid >> 2, ch = tid & 3;
-    const int rA0 = lr, rA1 = lr + 128, rW = lr;
-    const int8_t *gA0 = Aq + (m0 + rA0) * Kp + ch * 16;
-    const int8_t *gA1 = Aq + (m0 + rA1) * Kp + ch * 16;
-    const int8_t *gW = Wq + (n0 + rW) * Kp + ch * 16;
-    const int dA0 = rA0 * 64 + ((ch ^ ((rA0 >> 2) & 3)) << 4);
-    const int dA1 = rA1 * 64 + ((ch ^ ((rA1 >> 2) & 3)) << 4);
-    const int dW = kStA + rW * 64 + ((ch ^ ((rW >> 2) & 3)) << 4);
-    // scales: threads 0..127 -> A [blk = tid / 64][rows 4 (tid % 64) ..],
-    // threads 128..191 -> W [blk = (tid - 128) / 32][rows 4 ((tid - 128) % 32) ..]
-    const bool hasC = tid < 192;
-    const float *gC = tid < 128 ? csA + (tid >> 6) * Mp + m0 + 4 * (tid & 63)
-                                : csW + ((tid - 128) >> 5) * Np + n0 + 4 * ((tid - 128) & 31);
-    const int64_t cstride = tid < 128 ? 2 * Mp : 2 * Np;
-    const int dC = tid < 128 ? kStA + kStW + tid * 16 : kStA + kStW + kStCA + (tid - 128) * 16;
+    // this thread's share of a stage: 16-byte chunk `ch` of the 128 stage
+    // bytes of A rows lr + 64 i (i < 4) and W rows lr + 64 i (i < 2), plus
+    // one 16-byte piece of the scales (threads < 384)
+    const int lr = tid >> 3, ch = tid & 7;
+    const int8_t *gA = Aq + (m0 + lr) * Kp + ch * 16;
+    const int8_t *gW = Wq + (n0 + lr) * Kp + ch * 16;
+    const int dA = lr * kRowB + ((ch ^ ((lr >> 1) & 7)) << 4);     // + 64 i rows (same swizzle)
+    const int dW = kStA + lr * kRowB + ((ch ^ ((lr >> 1) & 7)) << 4);
+    // scales: threads 0..255 -> A [blk = tid / 64][rows 4 (tid % 64) ..],
+    // threads 256..383 -> W [blk = (tid - 256) / 32][rows 4 ((tid - 256) % 32) ..]
+    const bool hasC = tid < 384;
+    const float *gC = tid < 256 ? csA + (tid >> 6) * Mp + m0 + 4 * (tid & 63)
+                                : csW + ((tid - 256) >> 5) * Np + n0 + 4 * ((tid - 256) & 31);
+    const int64_t cstride = tid < 256 ? kSB * Mp : kSB * Np;
+    const int dC = tid < 256 ? kStA + kStW + tid * 16 : kStA + kStW + kStCA + (tid - 256) * 16;
 
-    uint4 pa0, pa1, pw;
-    float4 pc = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto load = [&](int st) {
-        const int64_t kb = (int64_t)st * (kSB * 32);
-        pa0 = *reinterpret_cast<const uint4 *>(gA0 + kb);
-        pa1 = *reinterpret_cast<const uint4 *>(gA1 + kb);
-        pw = *reinterpret_cast<const uint4 *>(gW + kb);
-        if (hasC) pc = *reinterpret_cast<const float4 *>(gC + st * cstride);
-    };
-    auto store = [&](int buf) {
-        int8_t *base = smem + buf * kStage;
-        *reinterpret_cast<uint4 *>(base + dA0) = pa0;
-        *reinterpret_cast<uint4 *>(base + dA1) = pa1;
-        *reinterpret_cast<uint4 *>(base + dW) = pw;
-        if (hasC) *reinterpret_cast<float4 *>(base + dC) = pc;
-    };
+    // prefetch registers: this thread's share of one stage
+#define MXS_LOAD(S_, st_)                                                                      \
+    do {                                                                                       \
+        const int st__ = (st_) < nstage ? (st_) : nstage - 1;   /* past the end: reload */    \
+        const int64_t kb__ = (int64_t)st__ * kRowB;                                            \
+        a0##S_ = *reinterpret_cast<const uint4 *>(gA + kb__);                                  \
+        a1##S_ = *reinterpret_cast<const uint4 *>(gA + 64 * Kp + kb__);                        \
+        a2##S_ = *reinterpret_cast<const uint4 *>(gA + 128 * Kp + kb__);                       \
+        a3##S_ = *reinterpret_cast<const uint4 *>(gA + 192 * Kp + kb__);                       \
+        w0##S_ = *reinterpret_cast<const uint4 *>(gW + kb__);                                  \
+        w1##S_ = *reinterpret_cast<const uint4 *>(gW + 64 * Kp + kb__);                        \
+        if (hasC) c##S_ = *reinterpret_cast<const float4 *>(gC + st__ * cstride);              \
+    } while (0)
+#define MXS_STORE(S_, buf_)                                                                    \
+    do {                                                                                       \
+        int8_t *base__ = smem + (buf_) * kStage;                                               \
+        *reinterpret_cast<uint4 *>(base__ + dA) = a0##S_;                                      \
+        *reinterpret_cast<uint4 *>(base__ + dA + 64 * kRowB) = a1##S_;                         \
+        *reinterpret_cast<uint4 *>(base__ + dA + 128 * kRowB) = a2##S_;                        \
+        *reinterpret_cast<uint4 *>(base__ + dA + 192 * kRowB) = a3##S_;                        \
+        *reinterpret_cast<uint4 *>(base__ + dW) = w0##S_;                                      \
+        *reinterpret_cast<uint4 *>(base__ + dW + 64 * kRowB) = w1##S_;                         \
+        if (hasC) *reinterpret_cast<float4 *>(base__ + dC) = c##S_;                            \
+    } while (0)
+    uint4 a00, a10, a20, a30, w00, w10;
+    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f);
 
     // LDS offsets of this lane's MFMA fragments (stage-relative), per block
     int offA[kSB][2], offW[kSB][2];
@@ -420,8 +431,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
         for (int i = 0; i < 2; ++i) {
             const int c = 2 * blk + h;
             const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
-            offA[blk][i] = ra * 64 + ((c ^ ((ra >> 2) & 3)) << 4);
-            offW[blk][i] = kStA + rw * 64 + ((c ^ ((rw >> 2) & 3)) << 4);
+            offA[blk][i] = ra * kRowB + ((c ^ ((ra >> 1) & 7)) << 4);
+            offW[blk][i] = kStA + rw * kRowB + ((c ^ ((rw >> 1) & 7)) << 4);
         }
 
     float acc[2][2][16];
@@ -436,25 +447,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
         }
 
-    load(0);
-    store(0);
-    __syncthreads();
     bool aligned = true;
-    for (int st = 0; st < nstage; ++st) {
-        if (st + 1 < nstage) load(st + 1);
-        const int8_t *sbase = smem + (st & 1) * kStage;
+    // MFMAs and epilogues of one stage out of LDS buffer `buf`
+    auto compute = [&](int st, int buf) {
+        const int8_t *sbase = smem + buf * kStage;
         const float *sCA = reinterpret_cast<const float *>(sbase + kStA + kStW);
         const float *sCW = sCA + kSB * kGBM;
+        v4i fa[2], fw[2], na[2], nw[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            na[i] = *reinterpret_cast<const v4i *>(sbase + offA[0][i]);
+            nw[i] = *reinterpret_cast<const v4i *>(sbase + offW[0][i]);
+        }
 #pragma unroll
         for (int blk = 0; blk < kSB; ++blk) {
             const int b = st * kSB + blk;
-            if (b >= nb) break;
-            v4i fa[2], fw[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                fa[i] = *reinterpret_cast<const v4i *>(sbase + offA[blk][i]);
-                fw[i] = *reinterpret_cast<const v4i *>(sbase + offW[blk][i]);
+            for (int i = 0; i < 2; ++i) { fa[i] = na[i]; fw[i] = nw[i]; }
+            if (blk + 1 < kSB) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    na[i] = *reinterpret_cast<const v4i *>(sbase + offA[blk + 1][i]);
+                    nw[i] = *reinterpret_cast<const v4i *>(sbase + offW[blk + 1][i]);
+                }
             }
+            if (b >= nb) break;
             // window position of block b (scalar selects: no table lookups)
             const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
             const int hi = b >= h1 ? nb : (b >= h0 ? h1 : h0);
@@ -496,11 +513,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
                     for (int j = 0; j < 2; ++j) I[i][j] = zero;
             }
         }
-        if (st + 1 < nstage) {
-            store((st + 1) & 1);
-            __syncthreads();
-        }
+    };
+
+    MXS_LOAD(0, 0);
+    MXS_STORE(0, 0);
+    __syncthreads();
+    // iteration st: prefetch stage st + 1 into registers, compute stage st
+    // from buffer st & 1, then store the prefetched stage into the other buffer
+    for (int st = 0; st < nstage; st += 2) {
+        if (st + 1 < nstage) MXS_LOAD(0, st + 1);
+        compute(st, 0);
+        if (st + 1 >= nstage) break;
+        MXS_STORE(0, 1);
+        __syncthreads();
+        if (st + 2 < nstage) MXS_LOAD(0, st + 2);
+        compute(st + 1, 1);
+        if (st + 2 >= nstage) break;
+        MXS_STORE(0, 0);
+        __syncthreads();
     }
+#undef MXS_LOAD
+#undef MXS_STORE
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -528,7 +561,7 @@ PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
     PrepLayout L;
     L.Mp = ceil_div(A.rows, kGBM) * kGBM;
     L.Np = ceil_div(W.rows, kGBN) * kGBN;
-    L.Kp = ceil_div(A.K, 32 * kSB) * (32 * kSB);   // whole stages
+    L.Kp = ceil_div(A.K, 32 * kSB) * (32 * kSB);   // whole stages (prep pads the tail)
     const int64_t nbp = L.Kp / 32;
     size_t off = 0;
     L.a_codes = off; off = align256(off + (size_t)L.Mp * L.Kp);
@@ -574,7 +607,11 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+    // more than 64 KiB of LDS needs the opt-in (idempotent, per call)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_grouped),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)ntiles), dim3(512), 2 * kStage, st, ac, acs, wc, wcs,
                        M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
     return hipGetLastError();
 }
