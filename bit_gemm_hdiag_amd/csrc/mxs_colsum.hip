@@ -128,14 +128,23 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
 // calibrate: acc[k] += part[0][k]; acc[k] += part[1][k]; ...
 // score: e = (init ? 0 : E[k]) + part[0][k] + ...; fin ? score = hdiag*e : E = e
 template <bool SCORE>
-__global__ __launch_bounds__(256) void k_combine(const double *__restrict__ part, int64_t nch,
-                                                 int64_t K, double *__restrict__ acc,
-                                                 const double *__restrict__ hdiag,
-                                                 double *__restrict__ score, int init, int fin) {
-    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part, int64_t nch,
+                                                int64_t K, double *__restrict__ acc,
+                                                const double *__restrict__ hdiag,
+                                                double *__restrict__ score, int init, int fin) {
+    const int64_t k = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (k >= K) return;
     double e = (SCORE && init) ? 0.0 : acc[k];
-    for (int64_t c = 0; c < nch; ++c) e = e + part[c * K + k];
+    int64_t c = 0;
+    // loads 16 chunks ahead of the (ordered) additions
+    for (; c + 16 <= nch; c += 16) {
+        double v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = part[(c + u) * K + k];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) e = e + v[u];
+    }
+    for (; c < nch; ++c) e = e + part[c * K + k];
     if (SCORE && fin) score[k] = hdiag[k] * e;
     else acc[k] = e;
 }
@@ -160,10 +169,10 @@ hipError_t run_colsum(const T *X, int64_t M, int64_t K, int64_t ldx, bool score_
         else hipLaunchKernelGGL((k_colsum<T, VEC, 0>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const unsigned gk = (unsigned)ceil_div(K, 256);
+        const unsigned gk = (unsigned)ceil_div(K, 64);
         const int init = c0 == 0, fin = c0 + n >= nch;
-        if (score_mode) hipLaunchKernelGGL((k_combine<true>), dim3(gk), block, 0, st, part, n, K, E, hdiag, result, init, fin);
-        else hipLaunchKernelGGL((k_combine<false>), dim3(gk), block, 0, st, part, n, K, result, hdiag, result, init, fin);
+        if (score_mode) hipLaunchKernelGGL((k_combine<true>), dim3(gk), dim3(64), 0, st, part, n, K, E, hdiag, result, init, fin);
+        else hipLaunchKernelGGL((k_combine<false>), dim3(gk), dim3(64), 0, st, part, n, K, result, hdiag, result, init, fin);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -84,6 +84,49 @@ __global__ __launch_bounds__(256) void k_quant_gather(const T *__restrict__ X, i
     }
 }
 
+// LDS-staged gather: the permutation (as 16-bit indices) is staged once per
+// workgroup, then each row is read with coalesced 16-byte loads into LDS and
+// gathered from there. Used when the permutation and one row fit in LDS.
+constexpr int64_t kStageLds = 96 * 1024;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_gather_lds(const T *__restrict__ X, int64_t R, int64_t ldx,
+                                                          const int32_t *__restrict__ perm, Planes P) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int64_t K = P.K;
+    uint16_t *sperm = reinterpret_cast<uint16_t *>(lds);
+    T *srow = reinterpret_cast<T *>(lds + ((2 * K + 15) / 16) * 16);
+    const int tid = threadIdx.x;
+    for (int64_t j = tid; j < K; j += 256) {   // an index outside [0, K) is clamped
+        const uint32_t v = (uint32_t)perm[j];
+        sperm[j] = (uint16_t)(v < (uint32_t)K ? v : (uint32_t)K - 1u);
+    }
+    const int64_t nvec = K * (int64_t)sizeof(T) / 16;          // 16-byte pieces per row
+    const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
+    for (int64_t row = blockIdx.x; row < R; row += gridDim.x) {
+        __syncthreads();                       // previous row's gathers are done
+        const T *x = X + row * ldx;
+        if (vec) {
+            for (int64_t v = tid; v < nvec; v += 256)
+                reinterpret_cast<uint4 *>(srow)[v] = reinterpret_cast<const uint4 *>(x)[v];
+        } else {
+            for (int64_t j = tid; j < K; j += 256) srow[j] = x[j];
+        }
+        __syncthreads();
+        for (int64_t cg = tid; cg * 8 < K; cg += 256) {   // whole quads stay together
+            const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + cg * 8);
+            const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = load1<T>(srow + (w[i] & 0xFFFFu));
+                v[2 * i + 1] = load1<T>(srow + (w[i] >> 16));
+            }
+            emit(P, row, cg >> 2, (int)(cg & 3), v);
+        }
+    }
+}
+
 template <typename T>
 hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
                         hipStream_t st) {
@@ -95,6 +138,16 @@ hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Plan
         const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
         if (vec) hipLaunchKernelGGL((k_quant_direct<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, X, R, ldx, P);
         else hipLaunchKernelGGL((k_quant_direct<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, X, R, ldx, P);
+        return hipGetLastError();
+    }
+    const int64_t lds_bytes = ((2 * P.K + 15) / 16) * 16 + P.K * (int64_t)sizeof(T);
+    if (lds_bytes <= kStageLds && P.K <= 65536) {
+        int64_t blocks = R < 512 ? R : 512;   // each workgroup stages the permutation once
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_lds<T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_quant_gather_lds<T>), dim3((unsigned)blocks), dim3(256), (size_t)lds_bytes, st, X, R,
+                           ldx, perm, P);
         return hipGetLastError();
     }
     const int64_t gx = ceil_div(P.K / 8, 256);
