@@ -11,11 +11,19 @@ Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
 in `stages`; `roofline` is for the dominant kernel; `cpu_baseline` is the
 CPU oracle timed on a bounded sample of the same step.
 
+The dominant kernel's roofline uses the mixed_gemm call's own duration,
+timed with HIP events on its stream inside every timed step; its HBM
+traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored in
+profiles/ and is reported only while the GEMM source is unchanged since.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --copy-probe   (a plain device copy of known size, to
+                                       scale the HBM byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,8 +36,43 @@ HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 INT8_PEAK = 5.0e15         # OP/s, MI355X dense int8 MFMA
 
 
+GEMM_SOURCE = os.path.join(ROOT, "bit_gemm_hdiag_amd", "csrc", "mxs_gemm.hip")
+GEMM_TRAFFIC = os.path.join(ROOT, "profiles", "mixed_gemm_q_proj_2048x4096x4096.traffic.txt")
+COPY_BYTES = 1 << 29
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per mixed_gemm call from the stored counter summary, or None
+    when the summary is missing or the GEMM source changed since it was taken."""
+    try:
+        kv = {}
+        with open(GEMM_TRAFFIC) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return float(kv["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch):
+    """A plain device-to-device copy of COPY_BYTES, for counter scaling."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": COPY_BYTES, "dispatches": 3}), flush=True)
 
 
 def build_workload(mx, synth, torch, dev):
@@ -110,33 +153,39 @@ def time_stage(torch, fn, reps):
     return s.elapsed_time(e) / reps * 1e-3
 
 
-def cpu_baseline(w, torch):
-    """The CPU oracle on a bounded sample of the step, extrapolated to one step."""
-    import numpy as np
+def cpu_baseline(w, torch, min_seconds=10.0, max_reps=20):
+    """The CPU oracle over the whole step (every stage, every row), repeated
+    until about min_seconds of CPU work; the mean step time gives the rate."""
     import oracle
     oracle.build()
     K, N, M = w["K"], w["N"], w["M"]
     n8, n6, n4 = w["blocks"]
     Xc = w["Xc"].float().cpu().numpy()
     Wh = w["W"].float().cpu().numpy()
-    X_rows = 1024
-    Xh = w["X"][:X_rows].float().cpu().numpy()
-    kv = w["Kc"].float().cpu().numpy()
-    t = {}
-    t0 = time.perf_counter(); h = oracle.calibrate(Xc); t["calibrate"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); s = oracle.score(Wh, h); t["score"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); bits, perm = oracle.allocate(s, w["bp8"], w["bp6"]); t["allocate"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); Wq = oracle.quantize(Wh, perm, n8, n6, n4); t["quantize_w"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); Aq = oracle.quantize(Xh, perm, n8, n6, n4); t["quantize_x"] = (time.perf_counter() - t0) * (M / X_rows)
-    t0 = time.perf_counter(); oracle.mixed_gemm(Aq, Wq); t["mixed_gemm"] = (time.perf_counter() - t0) * (M / X_rows)
-    t0 = time.perf_counter(); oracle.quantize_kv(kv); t["quantize_kv"] = 2 * (time.perf_counter() - t0)
-    step = sum(t.values())
+    Xh = w["X"].float().cpu().numpy()
+    kv = [w["Kc"].float().cpu().numpy(), w["Vc"].float().cpu().numpy()]
+    tot = {}
+    reps = 0
+    t_all = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t_all < min_seconds):
+        t = {}
+        t0 = time.perf_counter(); h = oracle.calibrate(Xc); t["calibrate"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); s = oracle.score(Wh, h); t["score"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); bits, perm = oracle.allocate(s, w["bp8"], w["bp6"]); t["allocate"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); Wq = oracle.quantize(Wh, perm, n8, n6, n4); t["quantize_w"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); Aq = oracle.quantize(Xh, perm, n8, n6, n4); t["quantize_x"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); oracle.mixed_gemm(Aq, Wq); t["mixed_gemm"] = time.perf_counter() - t0
+        t0 = time.perf_counter(); [oracle.quantize_kv(x) for x in kv]; t["quantize_kv"] = time.perf_counter() - t0
+        for k, v in t.items():
+            tot[k] = tot.get(k, 0.0) + v
+        reps += 1
+    stage = {k: v / reps for k, v in tot.items()}
+    step = sum(stage.values())
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return dict(value=2 * M * N * K / step / 1e12, unit="TOPS", cores=cores, kind="oracle",
-                sample=f"calibrate, score, allocate, quantize W in full and one KV tensor in full (x2 for "
-                       f"K and V); quantize X and the GEMM on "
-                       f"{X_rows} of {M} token rows; per-stage times scaled to the full step",
-                step_s_extrapolated=step, stage_s=t)
+                sample=f"the whole step (every stage, all {M} token rows) run {reps} times back to back, "
+                       f"{time.perf_counter() - t_all:.1f} s of CPU work in total; value from the mean step",
+                step_s=step, stage_s=stage)
 
 
 def main():
@@ -146,6 +195,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -154,6 +204,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     import bit_gemm_hdiag_amd as mx
     from bit_gemm_hdiag_amd import synth
 
@@ -163,9 +216,18 @@ def main():
     w = build_workload(mx, synth, torch, dev)
     stages = stage_fns(mx, w)
 
-    def step():
-        for _, fn in stages:
-            fn()
+    gemm_ev = []
+
+    def step(timed=False):
+        for name, fn in stages:
+            if timed and name == "mixed_gemm":
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                gemm_ev.append((a, b))
+            else:
+                fn()
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -175,11 +237,12 @@ def main():
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(args.steps):
-        step()
+        step(timed=True)
     e.record()
     torch.cuda.synchronize()
     step_s = s.elapsed_time(e) / args.steps * 1e-3
-    log(f"step {step_s * 1e3:.3f} ms")
+    gemm_call_s = sum(a.elapsed_time(b) for a, b in gemm_ev) / len(gemm_ev) * 1e-3
+    log(f"step {step_s * 1e3:.3f} ms, mixed_gemm call {gemm_call_s * 1e6:.1f} us")
 
     work = algorithmic_work(w)
     stage_out = {}
@@ -198,9 +261,12 @@ def main():
     gemm = stage_out["mixed_gemm"]
     M, N, K = w["M"], w["N"], w["K"]
     ops = 2 * M * N * K
-    roofline = dict(bound="mfma", achieved=gemm["TOPS"], peak=INT8_PEAK / 1e12, unit="TOP/s",
-                    frac=gemm["TOPS"] * 1e12 / INT8_PEAK, traffic=None,
-                    kernel="mixed_gemm (k_gemm_blockwise)", algorithmic_ops_per_launch=ops)
+    achieved = ops / gemm_call_s / 1e12
+    roofline = dict(bound="mfma", achieved=achieved, peak=INT8_PEAK / 1e12, unit="TOP/s",
+                    frac=achieved * 1e12 / INT8_PEAK, traffic=measured_traffic(),
+                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_grouped",
+                    algorithmic_ops_per_launch=ops, launch_us=gemm_call_s * 1e6,
+                    algorithmic_bytes_per_launch=work["mixed_gemm"]["bytes"])
     qx = stage_out["quantize_x"]
     out = {
         "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
@@ -213,7 +279,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 MFMA / fp32 epilogue / fp64 sums",
+        "dtype": "int8",
         "data": "synthetic (seeded outlier-channel activations, Student-t weights, bf16)",
         "config": {"workload": "Llama-3-8B q_proj prefill layer: calibrate 8x2048 tokens, score/allocate/"
                                "quantize W 4096x4096, quantize X 2048x4096, mixed GEMM 2048x4096x4096 "

@@ -550,6 +550,327 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Decode path (M <= kGemvMaxRows): stream W once from HBM.
+//
+// A wavefront owns 64 W rows and one K-slice of at most kGemvMaxSlice
+// blocks. The rows' scale bytes of the whole slice are loaded once (aligned
+// dwords) into LDS. The slice's codes are walked in chunks of whole blocks
+// of one width class (8-bit: 4 blocks, 6-bit: 4, 4-bit: 8; 128, 96 and 128
+// bytes per row), each fetched with coalesced loads (consecutive lanes read
+// consecutive bytes of a row) one chunk ahead into registers, written to a
+// per-wave LDS tile with a padded row pitch and read back with lane = row.
+// The tokens' codes and scales are uniform across the wave and come through
+// scalar loads, issued for a whole chunk at a time. Block dot products are
+// exact in int32: 4-bit x 4-bit with v_dot8_i32_i4 on the packed nibbles,
+// 8-bit with v_dot4_i32_i8, 6-bit after widening both sides to bytes
+// (code * 4, the factor 16 folded into the scale). Each block adds
+// I_b * 2^(sa+sw) to an fp32 accumulator per token. K-slices write partial
+// rows that a second kernel adds in slice order, so the result does not
+// depend on scheduling.
+constexpr int kGemvMaxRows = 32;
+constexpr int kGemvMaxSlice = 64;   // blocks per K-slice (multiple of 8)
+constexpr int kGemvPitch = 144;     // 8-bit and 4-bit tiles: 128 bytes + 16 (conflict-free b128 reads)
+constexpr int kGemvPitch6 = 104;    // 6-bit tile: 96 bytes + 8 (conflict-free b64 reads)
+constexpr int kGemvScPitch = kGemvMaxSlice + 4;   // 17 dwords: conflict-free dword reads
+constexpr int kGemvTile = 64 * kGemvPitch;
+
+__device__ __forceinline__ uint32_t wide6(uint32_t g) {   // four 6-bit fields -> four bytes (code * 4)
+    return ((g << 2) & 0xFCu) | ((g << 4) & 0xFC00u) | ((g << 6) & 0xFC0000u) | ((g << 8) & 0xFC000000u);
+}
+
+// the 6-bit field group g (0..7) of a 24-byte block held as 6 words
+__device__ __forceinline__ uint32_t group6(const uint32_t w[6], int g) {
+    const int bit = 24 * g;
+    const uint32_t lo = w[bit >> 5], hi = (bit >> 5) + 1 < 6 ? w[(bit >> 5) + 1] : 0u;
+    return __builtin_amdgcn_alignbit(hi, lo, bit & 31);
+}
+
+// bytes o..o+7 of a byte string held as 32-bit words p[], reading only the
+// words up to index last (o >> 2 <= last)
+__device__ __forceinline__ uint64_t bytes8(const uint32_t *p, int32_t o, int32_t last) {
+    const int32_t d0 = o >> 2, sh = o & 3;
+    const int32_t i1 = d0 + 1 < last ? d0 + 1 : last, i2 = d0 + 2 < last ? d0 + 2 : last;
+    const uint64_t lo = ((uint64_t)p[i1] << 32) | p[d0];
+    return sh ? (lo >> (8 * sh)) | ((uint64_t)p[i2] << (64 - 8 * sh)) : lo;
+}
+
+struct GemvChunk {
+    int32_t cls;    // 8, 6 or 4
+    int32_t gb;     // first block (global index)
+    int32_t pb;     // first block within its class plane
+    int32_t nblk;   // blocks in the chunk
+};
+
+__device__ __forceinline__ GemvChunk gemv_chunk(int32_t gb, int32_t b1, int32_t n8, int32_t h6, int32_t nb) {
+    GemvChunk c;
+    int32_t end;
+    if (gb < n8) { c.cls = 8; c.pb = gb; end = n8; c.nblk = 4; }
+    else if (gb < h6) { c.cls = 6; c.pb = gb - n8; end = h6; c.nblk = 4; }
+    else { c.cls = 4; c.pb = gb - h6; end = nb; c.nblk = 8; }
+    end = end < b1 ? end : b1;
+    c.gb = gb;
+    c.nblk = gb + c.nblk < end ? c.nblk : end - gb;
+    return c;
+}
+
+// Coalesced fetch of one chunk of codes for 64 rows into registers. Lane
+// roles (row within a group of 8 rows, piece of the row) are fixed; load i
+// moves to the next group, so every address is a uniform base plus a 32-bit
+// lane offset. Pieces of rows past N or of blocks past the chunk re-read
+// the first bytes of the tile's first row (always valid) instead of
+// branching; they are staged but never used.
+//   4-bit: 8 lanes x 16 bytes per row, 8 loads
+//   8-bit: 8 lanes x 16 bytes per row, 8 loads
+//   6-bit: 8 lanes x 12 bytes (3 dword loads) per row, 8 x 3 loads
+__device__ __forceinline__ void gemv_fetch(const QView &W, int64_t row0, int32_t rows_left, const GemvChunk &c,
+                                           int lane, uint32_t R[32]) {
+    const int rs = lane >> 3, e = lane & 7;
+    if (c.cls == 6) {
+        const bool ok = (e >> 1) < c.nblk;
+        const uint8_t *base = W.q6 + row0 * W.ld6;
+        const uint32_t off = (uint32_t)(rs * W.ld6 + 12 * e + 24 * c.pb), step = (uint32_t)(8 * W.ld6);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t o = (ok && rs + 8 * i < rows_left) ? off + i * step : 0u;
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(base + o);
+            R[3 * i] = q[0]; R[3 * i + 1] = q[1]; R[3 * i + 2] = q[2];
+        }
+        return;
+    }
+    const bool c4 = c.cls == 4;
+    const bool ok = (c4 ? e : e >> 1) < c.nblk;
+    const uint8_t *base = c4 ? W.q4 + row0 * W.ld4 : reinterpret_cast<const uint8_t *>(W.q8) + row0 * W.ld8;
+    const int64_t ld = c4 ? W.ld4 : W.ld8;
+    const uint32_t off = (uint32_t)(rs * ld + 16 * e + (c4 ? 16 : 32) * c.pb), step = (uint32_t)(8 * ld);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t o = (ok && rs + 8 * i < rows_left) ? off + i * step : 0u;
+        const uint4 v = *reinterpret_cast<const uint4 *>(base + o);
+        R[4 * i] = v.x; R[4 * i + 1] = v.y; R[4 * i + 2] = v.z; R[4 * i + 3] = v.w;
+    }
+}
+
+// Registers -> LDS tile (row pitch kGemvPitch, or kGemvPitch6 for 6-bit),
+// mirroring the lane roles of gemv_fetch.
+__device__ __forceinline__ void gemv_stage(uint8_t *tile, int cls, int lane, const uint32_t R[32]) {
+    const int rs = lane >> 3, e = lane & 7;
+    if (cls == 6) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t *q = reinterpret_cast<uint32_t *>(tile + (rs + 8 * i) * kGemvPitch6 + 12 * e);
+            q[0] = R[3 * i]; q[1] = R[3 * i + 1]; q[2] = R[3 * i + 2];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint4 *>(tile + (rs + 8 * i) * kGemvPitch + 16 * e) =
+                make_uint4(R[4 * i], R[4 * i + 1], R[4 * i + 2], R[4 * i + 3]);
+    }
+}
+
+// One staged chunk against the tokens. FULL: the chunk has all its blocks,
+// so no per-block bound is tested and the tokens' loads of the chunk issue
+// together. swb: the row's W scale bytes of the chunk.
+template <int MT, bool FULL>
+__device__ __forceinline__ void gemv_chunk_dot(const int8_t *__restrict__ a8, int64_t la8,
+                                               const uint8_t *__restrict__ a6, int64_t la6,
+                                               const uint8_t *__restrict__ a4, int64_t la4,
+                                               const uint8_t *__restrict__ asc, int64_t las, int32_t M,
+                                               const GemvChunk &cur, const uint8_t *tile, uint64_t swb,
+                                               int lane, float acc[MT]) {
+    float sw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sw[j] = e8m0_to_f32((uint32_t)(swb >> (8 * j)) & 0xFFu);
+    const int32_t dl = (cur.gb + cur.nblk - 1) >> 2;   // last dword of the tokens' scale bytes
+    if (cur.cls == 4) {
+        uint4 w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 16 * j);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t >= M) break;
+            const uint8_t *ap = a4 + t * la4 + 16 * (int64_t)cur.pb;
+            uint4 a[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = *reinterpret_cast<const uint4 *>(ap + ((FULL || j < cur.nblk) ? 16 * j : 0));
+            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (!FULL && j >= cur.nblk) break;
+                int d = __builtin_amdgcn_sdot8((int)a[j].x, (int)w[j].x, 0, false);
+                d = __builtin_amdgcn_sdot8((int)a[j].y, (int)w[j].y, d, false);
+                d = __builtin_amdgcn_sdot8((int)a[j].z, (int)w[j].z, d, false);
+                d = __builtin_amdgcn_sdot8((int)a[j].w, (int)w[j].w, d, false);
+                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
+                acc[t] = __builtin_fmaf((float)d, sa * sw[j], acc[t]);
+            }
+        }
+    } else if (cur.cls == 8) {
+        uint4 w[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[j][0] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 32 * j);
+            w[j][1] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 32 * j + 16);
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t >= M) break;
+            const int8_t *ap = a8 + t * la8 + 32 * (int64_t)cur.pb;
+            uint4 a[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 *q = reinterpret_cast<const uint4 *>(ap + ((FULL || j < cur.nblk) ? 32 * j : 0));
+                a[j][0] = q[0]; a[j][1] = q[1];
+            }
+            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!FULL && j >= cur.nblk) break;
+                int d = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    d = __builtin_amdgcn_sdot4((int)a[j][h].x, (int)w[j][h].x, d, false);
+                    d = __builtin_amdgcn_sdot4((int)a[j][h].y, (int)w[j][h].y, d, false);
+                    d = __builtin_amdgcn_sdot4((int)a[j][h].z, (int)w[j][h].z, d, false);
+                    d = __builtin_amdgcn_sdot4((int)a[j][h].w, (int)w[j][h].w, d, false);
+                }
+                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
+                acc[t] = __builtin_fmaf((float)d, sa * sw[j], acc[t]);
+            }
+        }
+    } else {
+        uint32_t wb[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint8_t *wp = tile + lane * kGemvPitch6 + 24 * j;
+            const uint2 v0 = *reinterpret_cast<const uint2 *>(wp);
+            const uint2 v1 = *reinterpret_cast<const uint2 *>(wp + 8);
+            const uint2 v2 = *reinterpret_cast<const uint2 *>(wp + 16);
+            const uint32_t wr[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
+#pragma unroll
+            for (int g = 0; g < 8; ++g) wb[j][g] = wide6(group6(wr, g));
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t >= M) break;
+            const uint8_t *ap = a6 + t * la6 + 24 * (int64_t)cur.pb;
+            uint32_t ar[4][6];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t *q = reinterpret_cast<const uint32_t *>(ap + ((FULL || j < cur.nblk) ? 24 * j : 0));
+#pragma unroll
+                for (int i = 0; i < 6; ++i) ar[j][i] = q[i];
+            }
+            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!FULL && j >= cur.nblk) break;
+                int d = 0;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) d = __builtin_amdgcn_sdot4((int)wide6(group6(ar[j], g)), (int)wb[j][g], d, false);
+                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
+                acc[t] = __builtin_fmaf((float)d, sa * (sw[j] * 0.0625f), acc[t]);
+            }
+        }
+    }
+}
+
+template <int MT>
+__global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int64_t la8,
+                                             const uint8_t *__restrict__ a6, int64_t la6,
+                                             const uint8_t *__restrict__ a4, int64_t la4,
+                                             const uint8_t *__restrict__ asc, int64_t las, QView W, int32_t M,
+                                             int64_t N, int32_t n8, int32_t n6, int32_t nb, int32_t bps,
+                                             float *__restrict__ out, int64_t ldo, int64_t slice_stride) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kGemvTile];
+    __shared__ __attribute__((aligned(16))) uint32_t sct[64 * kGemvScPitch / 4];
+    const int lane = threadIdx.x;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const int32_t rows_left = N - row0 < 64 ? (int32_t)(N - row0) : 64;
+    const int32_t b0 = (int32_t)blockIdx.y * bps;
+    const int32_t b1 = b0 + bps < nb ? b0 + bps : nb;
+    const int32_t h6 = n8 + n6;
+
+    uint32_t R[32];
+    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
+    gemv_fetch(W, row0, rows_left, c, lane, R);
+
+    // the slice's W scale bytes: dwords b0/4 .. (b1-1)/4 of each row (b0 is a
+    // multiple of 8; scale rows are 4-byte aligned), 16 lanes per row
+    {
+        const int32_t nd = (b1 - b0 + 3) >> 2;
+        const int d = lane & 15, rq = lane >> 4;
+        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + row0 * W.lds + b0);
+        const int64_t ldw = W.lds >> 2;
+        uint32_t v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = rq + 4 * i;
+            v[i] = sp[(d < nd && r < rows_left) ? r * ldw + d : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sct[(rq + 4 * i) * (kGemvScPitch / 4) + d] = v[i];
+    }
+
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.f;
+    const uint32_t *my_sc = sct + lane * (kGemvScPitch / 4);
+    while (true) {
+        gemv_stage(tile, c.cls, lane, R);
+        __builtin_amdgcn_wave_barrier();
+        const GemvChunk cur = c;
+        const int32_t next = cur.gb + cur.nblk;
+        if (next < b1) {
+            c = gemv_chunk(next, b1, n8, h6, nb);
+            gemv_fetch(W, row0, rows_left, c, lane, R);
+        }
+        const uint64_t swb = bytes8(my_sc, cur.gb - b0, (next - 1 - b0) >> 2);
+        if (cur.nblk == (cur.cls == 4 ? 8 : 4))
+            gemv_chunk_dot<MT, true>(a8, la8, a6, la6, a4, la4, asc, las, M, cur, tile, swb, lane, acc);
+        else
+            gemv_chunk_dot<MT, false>(a8, la8, a6, la6, a4, la4, asc, las, M, cur, tile, swb, lane, acc);
+        if (next >= b1) break;
+        __builtin_amdgcn_wave_barrier();
+    }
+    const int64_t n = row0 + lane;
+    if (n >= N) return;
+    float *o = out + (int64_t)blockIdx.y * slice_stride + n;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t >= M) break;
+        o[t * ldo] = acc[t];
+    }
+}
+
+// Y[t, n] = sum over slices s (in order) of part[s][t][n]
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int32_t ns, int32_t M,
+                                                     int64_t N, float *__restrict__ Y, int64_t ldy) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int64_t t = i / N, n = i - t * N;
+    float v = 0.f;
+    for (int32_t s = 0; s < ns; ++s) v = v + part[(int64_t)s * M * N + i];
+    Y[t * ldy + n] = v;
+}
+
+struct GemvPlan {
+    int32_t nslices, bps;
+};
+
+GemvPlan gemv_plan(const mxs_qmat &A, const mxs_qmat &W) {
+    const int32_t nb = (int32_t)(A.K / 32);
+    const int64_t waves = ceil_div(W.rows, 64);
+    int64_t ns = ceil_div(8192, waves);            // a few rounds of waves over the machine
+    const int64_t max_ns = ceil_div(nb, 16);       // at least 16 blocks per slice
+    const int64_t min_ns = ceil_div(nb, kGemvMaxSlice);
+    ns = ns > max_ns ? max_ns : ns;
+    ns = ns < min_ns ? min_ns : ns;
+    const int32_t bps = (int32_t)(ceil_div(ceil_div(nb, ns), 8) * 8);
+    return GemvPlan{(int32_t)ceil_div(nb, bps), bps};
+}
+
 struct PrepLayout {
     int64_t Mp, Np, Kp;
     size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
@@ -573,11 +894,54 @@ PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
 }
 
 bool use_prefill(const mxs_qmat &A) { return A.rows >= kPrefillMinRows; }
+// The decode kernel addresses 64 W rows with 32-bit offsets, reads 4-bit
+// rows in 16-byte pieces and both operands' scale bytes as aligned dwords.
+bool use_gemv(const mxs_qmat &A, const mxs_qmat &W) {
+    const int64_t lim = ((int64_t)1 << 32) / 64;
+    auto al = [](const void *p, int64_t ld, int64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0 && ld % a == 0; };
+    return A.rows <= kGemvMaxRows && W.ld8 < lim && W.ld6 < lim && W.ld4 < lim && W.lds < lim &&
+           al(A.sc, A.lds, 4) && al(W.sc, W.lds, 4) && (W.n4 == 0 || al(W.q4, W.ld4, 16));
+}
+
+template <int MT>
+hipError_t launch_gemv_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
+    const GemvPlan P = gemv_plan(A, W);
+    const int64_t M = A.rows, N = W.rows;
+    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)P.nslices);
+    if (P.nslices == 1) {
+        hipLaunchKernelGGL((k_gemv<MT>), grid, dim3(64), 0, st, A.q8, A.ld8, A.q6, A.ld6, A.q4, A.ld4, A.sc, A.lds,
+                           view_of(W), (int32_t)M, N, A.n8, A.n6, (int32_t)(A.K / 32), P.bps, Y, ldy, (int64_t)0);
+        return hipGetLastError();
+    }
+    float *part = static_cast<float *>(ws);
+    hipLaunchKernelGGL((k_gemv<MT>), grid, dim3(64), 0, st, A.q8, A.ld8, A.q6, A.ld6, A.q4, A.ld4, A.sc, A.lds,
+                       view_of(W), (int32_t)M, N, A.n8, A.n6, (int32_t)(A.K / 32), P.bps, part, N, M * N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, part, P.nslices,
+                       (int32_t)M, N, Y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
+    const int64_t M = A.rows;
+    if (M <= 1) return launch_gemv_t<1>(A, W, Y, ldy, ws, st);
+    if (M <= 2) return launch_gemv_t<2>(A, W, Y, ldy, ws, st);
+    if (M <= 4) return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
+    if (M <= 8) return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
+    if (M <= 16) return launch_gemv_t<16>(A, W, Y, ldy, ws, st);
+    return launch_gemv_t<32>(A, W, Y, ldy, ws, st);
+}
 
 }  // namespace
 
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
-    if (!use_prefill(A) || W.rows == 0) return 0;
+    if (W.rows == 0 || A.rows == 0) return 0;
+    if (use_gemv(A, W)) {
+        const GemvPlan P = gemv_plan(A, W);
+        return P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+    }
+    if (!use_prefill(A)) return 0;
     return prep_layout(A, W).total;
 }
 
@@ -585,6 +949,7 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
                              void *ws, size_t, hipStream_t st) {
     const int64_t M = A.rows, N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
+    if (use_gemv(A, W)) return launch_gemv(A, W, Y, ldy, ws, st);
     if (!use_prefill(A)) {
         const dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
         hipLaunchKernelGGL(k_gemm_blockwise, grid, dim3(256), 0, st, view_of(A), view_of(W), M, N,

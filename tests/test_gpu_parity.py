@@ -211,7 +211,8 @@ def test_mixed_gemm(mx, orc, M, N, K, budget):
     gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N)
 
 
-@pytest.mark.parametrize("M,N,K,budget", [(200, 300, 1024, (500, 1500)), (64, 128, 8192, (300, 1000))])
+@pytest.mark.parametrize("M,N,K,budget", [(200, 300, 1024, (500, 1500)), (64, 128, 8192, (300, 1000)),
+                                          (3, 300, 1024, (500, 1500)), (20, 77, 4096, (300, 1000))])
 def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
     # per-block scales spread over +-2^12 so that many (row, group) pairs cannot
     # share one exponent: exercises the per-block path next to aligned groups
@@ -219,7 +220,7 @@ def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
     X = torch.randn(M, K, generator=g) * 2.0 ** torch.randint(-12, 13, (M, K // 32), generator=g).repeat_interleave(32, 1)
     W = torch.randn(N, K, generator=g) * 2.0 ** torch.randint(-12, 13, (N, K // 32), generator=g).repeat_interleave(32, 1)
     X[:, 40:72] = 0.0                                   # all-zero blocks inside groups
-    W[5, 100] = float("nan") if M == 200 else W[5, 100]  # one non-finite block
+    W[5, 100] = float("nan") if M in (200, 3) else W[5, 100]  # one non-finite block
     X, W = X.to(DEV).to(torch.bfloat16), W.to(DEV).to(torch.bfloat16)
     n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
     perm = torch.randperm(K, generator=g).to(torch.int32).to(DEV)
@@ -241,6 +242,29 @@ def test_mixed_gemm_fp32_tiny_layer(mx, orc):
 def test_mixed_gemm_q_proj_full_size_sampled(mx, orc):
     rows = np.array([0, 1, 2, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
     gemm_case(mx, orc, 2048, 4096, 4096, (500, 1500), seed=2000, sample_rows=rows)
+
+
+@pytest.mark.parametrize("N,K", [(28672, 8192), (8192, 28672)])
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_mixed_gemm_decode_full_size_sampled(mx, orc, M, N, K):
+    # decode shapes of the 70B MLP (gate/up fused 28672 x 8192, down 8192 x
+    # 28672) at batch 1/8/32: every token, a sample of output columns
+    seed = 3000 + M
+    gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+    X = synth.activations(M, K, seed + synth.ROLE_X, gains, device=DEV)
+    W = synth.weights(N, K, seed + synth.ROLE_W, device=DEV)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, 500, 1500)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    perm = torch.randperm(K, generator=g).to(torch.int32)
+    A = mx.mxs_quantize(X, perm.to(DEV), n8, n6, n4)
+    B = mx.mxs_quantize(W, perm.to(DEV), n8, n6, n4)
+    Y = mx.mxs_mixed_gemm(A, B).cpu().numpy().astype(np.float64)
+    cols = np.unique(np.concatenate([np.arange(0, 3), np.arange(N - 3, N),
+                                     torch.randint(0, N, (40,), generator=g).numpy()]))
+    A_ref = orc.quantize(host(X), perm.numpy(), n8, n6, n4)
+    B_ref = orc.quantize(host(W[torch.as_tensor(cols, device=DEV)]), perm.numpy(), n8, n6, n4)
+    Yref, Yabs = orc.mixed_gemm(A_ref, B_ref)
+    assert_gemm(Y[:, cols], Yref, Yabs, f"decode M={M} N={N} K={K}")
 
 
 def test_mixed_gemm_strided_output_and_determinism(mx, orc):
