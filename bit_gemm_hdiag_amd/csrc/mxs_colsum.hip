@@ -79,17 +79,15 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     if (col0 < K) {  // K % 32 == 0: a quad is either wholly in or wholly out
         const T *p = X + col0;
         int64_t r = r0 + g;
-        for (; r + 24 < r1; r += 32) {
-            float v0[8], v1[8], v2[8], v3[8];
-            load8<T, VEC>(p + r * ldx, v0);
-            load8<T, VEC>(p + (r + 8) * ldx, v1);
-            load8<T, VEC>(p + (r + 16) * ldx, v2);
-            load8<T, VEC>(p + (r + 24) * ldx, v3);
-            if (kScore) {
-                acc_residual_sq(v0, acc); acc_residual_sq(v1, acc);
-                acc_residual_sq(v2, acc); acc_residual_sq(v3, acc);
-            } else {
-                acc_sq(v0, acc); acc_sq(v1, acc); acc_sq(v2, acc); acc_sq(v3, acc);
+        // eight rows of the lane's chain in flight, consumed in row order
+        for (; r + 56 < r1; r += 64) {
+            float v[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) load8<T, VEC>(p + (r + 8 * u) * ldx, v[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (kScore) acc_residual_sq(v[u], acc);
+                else acc_sq(v[u], acc);
             }
         }
         for (; r < r1; r += 8) {

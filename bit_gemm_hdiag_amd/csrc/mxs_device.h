@@ -162,6 +162,13 @@ __device__ __forceinline__ void store_bytes(uint8_t *p, uint64_t w, int n) {
 
 // fp32 value 2^(byte - 127) of an E8M0 scale byte (0xFF -> +Inf, which turns
 // the all-zero codes of a non-finite block into NaN in any product).
+// Workgroup barrier for LDS hand-offs: waits only for this wave's LDS (and
+// scalar) operations, so global loads issued before it stay in flight.
+// (__syncthreads() also drains outstanding global loads.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
     return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
 }

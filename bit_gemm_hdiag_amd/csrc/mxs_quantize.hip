@@ -127,6 +127,83 @@ __global__ __launch_bounds__(256) void k_quant_gather_lds(const T *__restrict__ 
     }
 }
 
+// The same LDS-staged gather with rows streamed two ahead: each thread
+// holds its PPT 16-byte pieces of the next two rows in registers, so a row's
+// HBM latency overlaps the gathers and stores of the rows before it.
+// Requires 16-byte aligned rows.
+template <typename T, int PPT>
+__global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X, int64_t R, int64_t ldx,
+                                                         const int32_t *__restrict__ perm, Planes P) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int64_t K = P.K;
+    uint16_t *sperm = reinterpret_cast<uint16_t *>(lds);
+    u32x4 *srow = reinterpret_cast<u32x4 *>(lds + ((2 * K + 15) / 16) * 16);
+    const int tid = threadIdx.x;
+    for (int64_t j = tid; j < K; j += 256) {   // an index outside [0, K) is clamped
+        const uint32_t v = (uint32_t)perm[j];
+        sperm[j] = (uint16_t)(v < (uint32_t)K ? v : (uint32_t)K - 1u);
+    }
+    const int nvec = (int)(K * (int64_t)sizeof(T) / 16);
+    const int64_t G = gridDim.x;
+    u32x4 ra[PPT], rb[PPT];
+    auto fetch = [&](u32x4 (&r)[PPT], int64_t row) {
+        const u32x4 *x = reinterpret_cast<const u32x4 *>(X + row * ldx);
+#pragma unroll
+        for (int i = 0; i < PPT; ++i)
+            if (tid + 256 * i < nvec) r[i] = __builtin_nontemporal_load(x + tid + 256 * i);
+    };
+    auto stage = [&](const u32x4 (&r)[PPT]) {
+        lds_barrier();                              // the previous row's gathers are done
+#pragma unroll
+        for (int i = 0; i < PPT; ++i)
+            if (tid + 256 * i < nvec) srow[tid + 256 * i] = r[i];
+        lds_barrier();
+    };
+    const T *s = reinterpret_cast<const T *>(srow);
+    auto gather = [&](int64_t row) {
+        for (int64_t cg = tid; cg * 8 < K; cg += 256) {   // whole quads stay together
+            const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + cg * 8);
+            const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = load1<T>(s + (w[i] & 0xFFFFu));
+                v[2 * i + 1] = load1<T>(s + (w[i] >> 16));
+            }
+            emit(P, row, cg >> 2, (int)(cg & 3), v);
+        }
+    };
+    int64_t row = blockIdx.x;
+    if (row < R) fetch(ra, row);
+    if (row + G < R) fetch(rb, row + G);
+    while (row < R) {
+        stage(ra);
+        if (row + 2 * G < R) fetch(ra, row + 2 * G);
+        gather(row);
+        row += G;
+        if (row >= R) break;
+        stage(rb);
+        if (row + 2 * G < R) fetch(rb, row + 2 * G);
+        gather(row);
+        row += G;
+    }
+}
+
+template <typename T, int PPT>
+hipError_t launch_gather_pf(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
+                            int64_t lds_bytes, hipStream_t st) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_pf<T, PPT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+    if (e != hipSuccess) return e;
+    // enough workgroups to keep ~16 MB of rows in flight, limited by LDS
+    const int64_t per_cu = (160 * 1024) / lds_bytes;
+    int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
+    blocks = blocks < R ? blocks : R;
+    hipLaunchKernelGGL((k_quant_gather_pf<T, PPT>), dim3((unsigned)blocks), dim3(256), (size_t)lds_bytes, st, X, R,
+                       ldx, perm, P);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
                         hipStream_t st) {
@@ -141,6 +218,15 @@ hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Plan
         return hipGetLastError();
     }
     const int64_t lds_bytes = ((2 * P.K + 15) / 16) * 16 + P.K * (int64_t)sizeof(T);
+    const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
+    const int64_t ppt = ceil_div(P.K * (int64_t)sizeof(T) / 16, 256);
+    if (vec && lds_bytes <= kStageLds && P.K <= 65536 && ppt <= 16) {
+        if (ppt <= 1) return launch_gather_pf<T, 1>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 2) return launch_gather_pf<T, 2>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 4) return launch_gather_pf<T, 4>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 8) return launch_gather_pf<T, 8>(X, ldx, perm, P, R, lds_bytes, st);
+        return launch_gather_pf<T, 16>(X, ldx, perm, P, R, lds_bytes, st);
+    }
     if (lds_bytes <= kStageLds && P.K <= 65536) {
         int64_t blocks = R < 512 ? R : 512;   // each workgroup stages the permutation once
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_lds<T>),
