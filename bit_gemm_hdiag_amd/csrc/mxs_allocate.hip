@@ -12,6 +12,8 @@
 // 1.7e10 compares over the whole GPU; 8.2e8 at K = 28672, 1.7e7 at 4096)
 // whose partial counts are added with integer atomics (order-independent). The
 // perm output buffer holds the ranks until the last kernel overwrites it.
+// (A one-workgroup bitonic sort in LDS measured 54 us at K = 4096, against
+// 16 us for these three launches.)
 #include "mxs_device.h"
 #include "mxs_internal.h"
 

@@ -13,14 +13,16 @@
 //   whose offset is i mod 8, in row order from +0; chunk total
 //   ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); chunk totals added in chunk order.
 //
-// Mapping: a wavefront is 8 row groups x 8 lanes; lane (g, c) owns 8
-// consecutive columns (one 16-byte bf16 load per row) and the partial sum
-// p_g of its chunk, so each wave streams 8 rows x 64 columns per step and the
-// 4 waves of a workgroup cover 256 adjacent columns. The tree is three
-// cross-lane xor steps (8, 16, 32). Chunk totals go to a workspace and a
-// second kernel adds them in chunk order; a single chunk is written directly.
-// In the score kernel the 4 lanes of a quad hold one 32-column MXINT4 block
-// of a row, so the block maximum is two DPP steps.
+// Mapping: a wavefront is 8 row groups x 8 lanes; lane (g, c) owns CPL
+// consecutive columns (one load per row) and the partial sum p_g of its
+// chunk, so each wave streams 8 rows x 8 CPL columns per step and the 4 waves
+// of a workgroup cover 32 CPL adjacent columns. The tree is three cross-lane
+// xor steps (8, 16, 32). Chunk totals go to a workspace and a second kernel
+// adds them in chunk order; a single chunk is written directly.
+// CPL = 8 (16-byte bf16 loads): in the score kernel the 4 lanes of a quad
+// hold one 32-column MXINT4 block of a row, so the block maximum is two DPP
+// steps. (CPL = 4, with twice the waves and an 8-lane block maximum, measured
+// slower for the score at 4096 x 4096.)
 #include "mxs_device.h"
 #include "mxs_internal.h"
 
@@ -28,29 +30,70 @@ namespace mxs {
 
 namespace {
 
-constexpr int kWaveCols = 64;   // columns per wavefront
-constexpr int kWgCols = 256;    // columns per workgroup
+constexpr int kCpl = 8;   // columns per lane
 
-// Residual of 8 values of one row under uniform MXINT4 (the quad holds the
-// block), squared into the fp64 partial sums. d = v - c * 2^s is exact in
-// fp32 (fma with a power of two whose result is representable), its square
-// exact in fp64.
-__device__ __forceinline__ void acc_residual_sq(const float v[8], double acc[8]) {
-    int c[8];
-    BlockScale bs = quantize8(v, 4, c);
+template <typename T, bool VEC, int CPL>
+__device__ __forceinline__ void load_cols(const T *p, float v[CPL]) {
+    if constexpr (CPL == 8) {
+        load8<T, VEC>(p, v);
+    } else if constexpr (VEC && sizeof(T) == 2) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        v[0] = __uint_as_float(u[0] << 16); v[1] = __uint_as_float(u[0] & 0xFFFF0000u);
+        v[2] = __uint_as_float(u[1] << 16); v[3] = __uint_as_float(u[1] & 0xFFFF0000u);
+    } else if constexpr (VEC) {
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < CPL; ++i) v[i] = load1<T>(p + i);
+    }
+}
+
+// Max over the 8 lanes 8j .. 8j+7 (xor 1 and 2 by DPP quad permutes, xor 4
+// by a swizzle).
+__device__ __forceinline__ uint32_t oct_max_u32(uint32_t x) {
+    x = quad_max_u32(x);
+    const uint32_t y = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (4 << 10) | 0x1F);
+    return x > y ? x : y;
+}
+
+// Residual of CPL values of one row under uniform MXINT4 (the lanes of the
+// block hold the rest of it), squared into the fp64 partial sums.
+// d = v - c * 2^s is exact in fp32 (fma with a power of two whose result is
+// representable), its square exact in fp64.
+template <int CPL>
+__device__ __forceinline__ void acc_residual_sq(const float v[CPL], double acc[CPL]) {
+    int c[CPL];
+    BlockScale bs;
+    if constexpr (CPL == 8) {
+        bs = quantize8(v, 4, c);
+    } else {
+        uint32_t a = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+            a = a > b ? a : b;
+        }
+        bs = block_scale(oct_max_u32(a), 4);
+        const float cm = cmax_of(4);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) c[i] = bs.bad ? 0 : (int)code_of(v[i], bs.inv, cm);
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
         float d = __builtin_fmaf(-(float)c[i], bs.scale, v[i]);
         d = bs.bad ? __builtin_nanf("") : d;
-        double dd = (double)d;
+        const double dd = (double)d;
         acc[i] = __builtin_fma(dd, dd, acc[i]);
     }
 }
 
-__device__ __forceinline__ void acc_sq(const float v[8], double acc[8]) {
+template <int CPL>
+__device__ __forceinline__ void acc_sq(const float v[CPL], double acc[CPL]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        double x = (double)v[i];
+    for (int i = 0; i < CPL; ++i) {
+        const double x = (double)v[i];
         acc[i] = __builtin_fma(x, x, acc[i]);
     }
 }
@@ -59,7 +102,7 @@ __device__ __forceinline__ void acc_sq(const float v[8], double acc[8]) {
 // MODE 1: calibrate, single chunk: hdiag[k] += total
 // MODE 2: score, write chunk totals to part[chunk][K]
 // MODE 3: score, single chunk: score[k] = hdiag[k] * total
-template <typename T, bool VEC, int MODE>
+template <typename T, bool VEC, int MODE, int CPL>
 __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t M, int64_t K,
                                                 int64_t ldx, int64_t chunk0,
                                                 double *__restrict__ out,
@@ -68,39 +111,41 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 3;
-    const int64_t col0 = (int64_t)blockIdx.x * kWgCols + wave * kWaveCols + (lane & 7) * 8;
+    const int64_t col0 = (int64_t)blockIdx.x * (32 * CPL) + wave * (8 * CPL) + (lane & 7) * CPL;
     const int64_t r0 = (chunk0 + blockIdx.y) * kChunkRows;
     const int64_t r1 = r0 + kChunkRows < M ? r0 + kChunkRows : M;
 
-    double acc[8];
+    double acc[CPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.0;
 
-    if (col0 < K) {  // K % 32 == 0: a quad is either wholly in or wholly out
+    // K % 32 == 0: the lanes of one block are either all in or all out
+    // (their shuffles stay inside the wave's active block lanes)
+    if (col0 < K) {
         const T *p = X + col0;
         int64_t r = r0 + g;
         // eight rows of the lane's chain in flight, consumed in row order
         for (; r + 56 < r1; r += 64) {
-            float v[8][8];
+            float v[8][CPL];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) load8<T, VEC>(p + (r + 8 * u) * ldx, v[u]);
+            for (int u = 0; u < 8; ++u) load_cols<T, VEC, CPL>(p + (r + 8 * u) * ldx, v[u]);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                if (kScore) acc_residual_sq(v[u], acc);
-                else acc_sq(v[u], acc);
+                if (kScore) acc_residual_sq<CPL>(v[u], acc);
+                else acc_sq<CPL>(v[u], acc);
             }
         }
         for (; r < r1; r += 8) {
-            float v0[8];
-            load8<T, VEC>(p + r * ldx, v0);
-            if (kScore) acc_residual_sq(v0, acc);
-            else acc_sq(v0, acc);
+            float v0[CPL];
+            load_cols<T, VEC, CPL>(p + r * ldx, v0);
+            if (kScore) acc_residual_sq<CPL>(v0, acc);
+            else acc_sq<CPL>(v0, acc);
         }
     }
 
     // ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7)) across the row groups
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < CPL; ++i) {
         double x = acc[i];
         x = x + __shfl_xor(x, 8);
         x = x + __shfl_xor(x, 16);
@@ -112,13 +157,13 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     if (MODE == 0 || MODE == 2) {
         double *dst = out + (int64_t)blockIdx.y * K + col0;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) *reinterpret_cast<double2 *>(dst + i) = make_double2(acc[i], acc[i + 1]);
+        for (int i = 0; i < CPL; i += 2) *reinterpret_cast<double2 *>(dst + i) = make_double2(acc[i], acc[i + 1]);
     } else if (MODE == 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[col0 + i] = out[col0 + i] + acc[i];
+        for (int i = 0; i < CPL; ++i) out[col0 + i] = out[col0 + i] + acc[i];
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[col0 + i] = hdiag[col0 + i] * (0.0 + acc[i]);
+        for (int i = 0; i < CPL; ++i) out[col0 + i] = hdiag[col0 + i] * (0.0 + acc[i]);
     }
 }
 
@@ -127,44 +172,44 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
 // score: e = (init ? 0 : E[k]) + part[0][k] + ...; fin ? score = hdiag*e : E = e
 template <bool SCORE>
 __global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part, int64_t nch,
-                                                int64_t K, double *__restrict__ acc,
-                                                const double *__restrict__ hdiag,
-                                                double *__restrict__ score, int init, int fin) {
+                                                 int64_t K, double *__restrict__ acc,
+                                                 const double *__restrict__ hdiag,
+                                                 double *__restrict__ score, int init, int fin) {
     const int64_t k = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (k >= K) return;
     double e = (SCORE && init) ? 0.0 : acc[k];
-    int64_t c = 0;
-    // loads 16 chunks ahead of the (ordered) additions
-    for (; c + 16 <= nch; c += 16) {
-        double v[16];
+    // loads run up to 32 chunks ahead of the (ordered) additions
+    for (int64_t c = 0; c < nch; c += 32) {
+        double v[32];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = part[(c + u) * K + k];
+        for (int u = 0; u < 32; ++u)
+            if (c + u < nch) v[u] = part[(c + u) * K + k];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) e = e + v[u];
+        for (int u = 0; u < 32; ++u)
+            if (c + u < nch) e = e + v[u];
     }
-    for (; c < nch; ++c) e = e + part[c * K + k];
     if (SCORE && fin) score[k] = hdiag[k] * e;
     else acc[k] = e;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int CPL>
 hipError_t run_colsum(const T *X, int64_t M, int64_t K, int64_t ldx, bool score_mode,
                       double *result, const double *hdiag, double *ws, hipStream_t st) {
     const int64_t nch = ceil_div(M, kChunkRows);
     const dim3 block(256);
-    const unsigned gx = (unsigned)ceil_div(K, kWgCols);
+    const unsigned gx = (unsigned)ceil_div(K, 32 * CPL);
     if (nch == 0) return hipSuccess;
     if (nch == 1) {
-        if (score_mode) hipLaunchKernelGGL((k_colsum<T, VEC, 3>), dim3(gx, 1), block, 0, st, X, M, K, ldx, (int64_t)0, result, hdiag);
-        else hipLaunchKernelGGL((k_colsum<T, VEC, 1>), dim3(gx, 1), block, 0, st, X, M, K, ldx, (int64_t)0, result, hdiag);
+        if (score_mode) hipLaunchKernelGGL((k_colsum<T, VEC, 3, CPL>), dim3(gx, 1), block, 0, st, X, M, K, ldx, (int64_t)0, result, hdiag);
+        else hipLaunchKernelGGL((k_colsum<T, VEC, 1, CPL>), dim3(gx, 1), block, 0, st, X, M, K, ldx, (int64_t)0, result, hdiag);
         return hipGetLastError();
     }
     double *E = ws;                       // score: running column error
     double *part = score_mode ? ws + K : ws;
     for (int64_t c0 = 0; c0 < nch; c0 += kMaxChunksPerLaunch) {
         const int64_t n = nch - c0 < kMaxChunksPerLaunch ? nch - c0 : kMaxChunksPerLaunch;
-        if (score_mode) hipLaunchKernelGGL((k_colsum<T, VEC, 2>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
-        else hipLaunchKernelGGL((k_colsum<T, VEC, 0>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
+        if (score_mode) hipLaunchKernelGGL((k_colsum<T, VEC, 2, CPL>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
+        else hipLaunchKernelGGL((k_colsum<T, VEC, 0, CPL>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const unsigned gk = (unsigned)ceil_div(K, 64);
@@ -182,8 +227,8 @@ hipError_t dispatch_colsum(const void *X, int64_t M, int64_t K, int64_t ldx, boo
                            double *result, const double *hdiag, double *ws, hipStream_t st) {
     const T *x = static_cast<const T *>(X);
     const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((ldx * (int64_t)sizeof(T)) % 16 == 0);
-    if (vec) return run_colsum<T, true>(x, M, K, ldx, score_mode, result, hdiag, ws, st);
-    return run_colsum<T, false>(x, M, K, ldx, score_mode, result, hdiag, ws, st);
+    if (vec) return run_colsum<T, true, kCpl>(x, M, K, ldx, score_mode, result, hdiag, ws, st);
+    return run_colsum<T, false, kCpl>(x, M, K, ldx, score_mode, result, hdiag, ws, st);
 }
 
 }  // namespace

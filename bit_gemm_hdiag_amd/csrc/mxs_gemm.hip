@@ -335,34 +335,81 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
 //
 // Workgroup: 8 waves (4 x 2), tile 256 (A rows) x 128 (W rows); each wave
 // owns 64 x 64 outputs as 2 x 2 MFMA tiles (64 int32 + 64 fp32 accumulators
-// per lane, two waves per SIMD). K advances kSB = 4 blocks (128 bytes of
-// every row) per stage through two LDS buffers. Latency hiding:
-//  - global loads run one stage ahead: each thread loads its share of the
-//    next stage into registers while the current stage is computed and then
-//    stores it into the other buffer; one barrier per stage;
-//  - LDS fragment reads run one block ahead of the MFMAs that use them.
-// (Direct global->LDS loads measured ~1.7x slower into LDS on gfx950 than
-// this register path.) Within a stage, row r keeps its eight 16-byte chunks c
-// at slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS read pass (16
-// consecutive rows, same chunk) then cover all 16 16-byte bank groups of a
-// 256-byte row of banks.
-constexpr int kGBM = 256, kGBN = 128;    // workgroup tile
-constexpr int kSB = 4;                   // blocks per stage
-constexpr int kRowB = kSB * 32;          // stage bytes per row (128)
-constexpr int kStA = kGBM * kRowB;       // 32 KiB of A codes per stage
-constexpr int kStW = kGBN * kRowB;       // 16 KiB of W codes
-constexpr int kStCA = kSB * kGBM * 4;    //  4 KiB of A scales [blk][row]
-constexpr int kStCW = kSB * kGBN * 4;    //  2 KiB of W scales [blk][row]
-constexpr int kStage = kStA + kStW + kStCA + kStCW;
+// per lane, two waves per SIMD). Operands move from global memory straight
+// into LDS (global_load_lds_dwordx4), so no registers hold data in flight
+// and four stages can be in flight at once. (A version that staged through
+// registers one stage ahead ran 4-5 % slower at the q_proj and MLP shapes.)
+//
+// Stage = kDSB = 2 blocks (64 bytes of every row) plus their scales, 27 KiB;
+// a ring of five stage slots. Iteration s: wait for this wave's loads of
+// stage s (the loads of stages s+1 .. s+3 stay in flight), barrier (every
+// wave's loads of stage s have landed and every wave is done with stage
+// s-1), issue stage s+4 into the slot of stage s-1, compute s.
+// A DMA instruction writes 64 consecutive 16-byte LDS slots, lane by lane;
+// lanes pick their global chunk so that row r keeps chunk c at slot
+// c ^ ((r >> 2) & 3) of its 64 bytes: the 16 lanes of one LDS read pass
+// (16 consecutive rows, same chunk) then hit 16 distinct 16-byte bank groups.
+constexpr int kGBM = 256, kGBN = 128;        // workgroup tile
+constexpr int kDSB = 2;                      // blocks per stage
+constexpr int kDRow = kDSB * 32;             // 64 bytes per row per stage
+constexpr int kDStA = kGBM * kDRow;          // 16 KiB
+constexpr int kDStW = kGBN * kDRow;          //  8 KiB
+constexpr int kDStCA = kDSB * kGBM * 4;      //  2 KiB
+constexpr int kDStCW = kDSB * kGBN * 4;      //  1 KiB
+constexpr int kDSlot = kDStA + kDStW + kDStCA + kDStCW;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(512, 1) void k_gemm_grouped(
+__shared__ __attribute__((aligned(16))) int8_t g_dslot0[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot1[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot2[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot3[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot4[kDSlot];
+
+template <int SL>
+__device__ __forceinline__ int8_t *dslot() {
+    return SL == 0 ? g_dslot0 : (SL == 1 ? g_dslot1 : (SL == 2 ? g_dslot2 : (SL == 3 ? g_dslot3 : g_dslot4)));
+}
+
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
+}
+
+// One 16-byte-per-lane DMA into LDS at lds + 16 * lane. Issued from inline
+// assembly so that the compiler does not order the slot reads behind every
+// outstanding DMA (its wait model cannot separate the ring slots here); the
+// kernel waits for its own DMAs explicitly (vmcnt) before a barrier. The
+// instruction writes no VGPR; M0 carries the wave-uniform LDS base.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+
+struct DmaLanes {
+    const int8_t *a0, *a1, *w;   // this lane's global chunk addresses at stage 0
+    const float *c;              // scales (waves 0..2)
+    int64_t cstep;               // scale address step per stage
+    int oa0, oa1, ow, oc;        // wave-uniform LDS offsets inside a slot
+};
+
+template <int SL>
+__device__ __forceinline__ void dma_issue(const DmaLanes &D, int st, int nstage, bool has_c) {
+    const int s = st < nstage ? st : nstage - 1;      // past the end: reload the last stage
+    const uint32_t slot = lds_addr(dslot<SL>());
+    const int64_t kb = (int64_t)s * kDRow;
+    dma16(D.a0 + kb, slot + D.oa0);
+    dma16(D.a1 + kb, slot + D.oa1);
+    dma16(D.w + kb, slot + D.ow);
+    if (has_c) dma16(D.c + s * D.cstep, slot + D.oc);
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm_dma(
     const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
     const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
     int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy) {
-    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
@@ -377,67 +424,54 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
     const int64_t gsz = tilesM - first_m < 8 ? tilesM - first_m : 8;
     const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
     const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
-    const int nstage = (nb + kSB - 1) / kSB;
+    const int nstage = (nb + kDSB - 1) / kDSB;
     const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
 
-    // this thread's share of a stage: 16-byte chunk `ch` of the 128 stage
-    // bytes of A rows lr + 64 i (i < 4) and W rows lr + 64 i (i < 2), plus
-    // one 16-byte piece of the scales (threads < 384)
-    const int lr = tid >> 3, ch = tid & 7;
-    const int8_t *gA = Aq + (m0 + lr) * Kp + ch * 16;
-    const int8_t *gW = Wq + (n0 + lr) * Kp + ch * 16;
-    const int dA = lr * kRowB + ((ch ^ ((lr >> 1) & 7)) << 4);     // + 64 i rows (same swizzle)
-    const int dW = kStA + lr * kRowB + ((ch ^ ((lr >> 1) & 7)) << 4);
-    // scales: threads 0..255 -> A [blk = tid / 64][rows 4 (tid % 64) ..],
-    // threads 256..383 -> W [blk = (tid - 256) / 32][rows 4 ((tid - 256) % 32) ..]
-    const bool hasC = tid < 384;
-    const float *gC = tid < 256 ? csA + (tid >> 6) * Mp + m0 + 4 * (tid & 63)
-                                : csW + ((tid - 256) >> 5) * Np + n0 + 4 * ((tid - 256) & 31);
-    const int64_t cstride = tid < 256 ? kSB * Mp : kSB * Np;
-    const int dC = tid < 256 ? kStA + kStW + tid * 16 : kStA + kStW + kStCA + (tid - 256) * 16;
-
-    // prefetch registers: this thread's share of one stage
-#define MXS_LOAD(S_, st_)                                                                      \
-    do {                                                                                       \
-        const int st__ = (st_) < nstage ? (st_) : nstage - 1;   /* past the end: reload */    \
-        const int64_t kb__ = (int64_t)st__ * kRowB;                                            \
-        a0##S_ = *reinterpret_cast<const uint4 *>(gA + kb__);                                  \
-        a1##S_ = *reinterpret_cast<const uint4 *>(gA + 64 * Kp + kb__);                        \
-        a2##S_ = *reinterpret_cast<const uint4 *>(gA + 128 * Kp + kb__);                       \
-        a3##S_ = *reinterpret_cast<const uint4 *>(gA + 192 * Kp + kb__);                       \
-        w0##S_ = *reinterpret_cast<const uint4 *>(gW + kb__);                                  \
-        w1##S_ = *reinterpret_cast<const uint4 *>(gW + 64 * Kp + kb__);                        \
-        if (hasC) c##S_ = *reinterpret_cast<const float4 *>(gC + st__ * cstride);              \
-    } while (0)
-#define MXS_STORE(S_, buf_)                                                                    \
-    do {                                                                                       \
-        int8_t *base__ = smem + (buf_) * kStage;                                               \
-        *reinterpret_cast<uint4 *>(base__ + dA) = a0##S_;                                      \
-        *reinterpret_cast<uint4 *>(base__ + dA + 64 * kRowB) = a1##S_;                         \
-        *reinterpret_cast<uint4 *>(base__ + dA + 128 * kRowB) = a2##S_;                        \
-        *reinterpret_cast<uint4 *>(base__ + dA + 192 * kRowB) = a3##S_;                        \
-        *reinterpret_cast<uint4 *>(base__ + dW) = w0##S_;                                      \
-        *reinterpret_cast<uint4 *>(base__ + dW + 64 * kRowB) = w1##S_;                         \
-        if (hasC) *reinterpret_cast<float4 *>(base__ + dC) = c##S_;                            \
-    } while (0)
-    uint4 a00, a10, a20, a30, w00, w10;
-    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f);
-
-    // LDS offsets of this lane's MFMA fragments (stage-relative), per block
-    int offA[kSB][2], offW[kSB][2];
-#pragma unroll
-    for (int blk = 0; blk < kSB; ++blk)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = 2 * blk + h;
-            const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
-            offA[blk][i] = ra * kRowB + ((c ^ ((ra >> 1) & 7)) << 4);
-            offW[blk][i] = kStA + rw * kRowB + ((c ^ ((rw >> 1) & 7)) << 4);
+    // DMA roles: A rows 32 wave .. +31 (two instructions of 16 rows), W rows
+    // 16 wave .. +15; waves 0, 1: A scales of block 0 / 1; wave 2: W scales
+    DmaLanes D;
+    {
+        const int rsub = lane >> 2, sl = lane & 3;
+        const int ra0 = 32 * wave + rsub, ra1 = ra0 + 16, rw = 16 * wave + rsub;
+        D.a0 = Aq + (m0 + ra0) * Kp + ((sl ^ ((ra0 >> 2) & 3)) << 4);
+        D.a1 = Aq + (m0 + ra1) * Kp + ((sl ^ ((ra1 >> 2) & 3)) << 4);
+        D.w = Wq + (n0 + rw) * Kp + ((sl ^ ((rw >> 2) & 3)) << 4);
+        D.oa0 = 32 * wave * kDRow;
+        D.oa1 = D.oa0 + 16 * kDRow;
+        D.ow = kDStA + 16 * wave * kDRow;
+        if (wave < 2) {
+            D.c = csA + (int64_t)wave * Mp + m0 + 4 * lane;
+            D.cstep = kDSB * Mp;
+            D.oc = kDStA + kDStW + wave * (kGBM * 4);
+        } else {
+            D.c = csW + (int64_t)(lane >> 5) * Np + n0 + 4 * (lane & 31);
+            D.cstep = kDSB * Np;
+            D.oc = kDStA + kDStW + kDStCA;
         }
+    }
+    const bool has_c = wave < 3;
+
+    // LDS offset of this lane's fragment of block blk: fb ^ (blk << 5)
+    int fbA[2], fbW[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
+        fbA[i] = ra * kDRow + ((h ^ ((ra >> 2) & 3)) << 4);
+        fbW[i] = kDStA + rw * kDRow + ((h ^ ((rw >> 2) & 3)) << 4);
+    }
 
     float acc[2][2][16];
     v16i I[2][2];
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    // two zero B operands the compiler cannot see through, so the four
+    // restart MFMAs stay distinct and write the accumulators in place
+    v4i zb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        zb[j] = v4i{z, z, z, z};
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -448,31 +482,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
         }
 
     bool aligned = true;
-    // MFMAs and epilogues of one stage out of LDS buffer `buf`
-    auto compute = [&](int st, int buf) {
-        const int8_t *sbase = smem + buf * kStage;
-        const float *sCA = reinterpret_cast<const float *>(sbase + kStA + kStW);
-        const float *sCW = sCA + kSB * kGBM;
+    auto compute = [&](int st, const int8_t *sbase) {
+        const float *sCA = reinterpret_cast<const float *>(sbase + kDStA + kDStW);
+        const float *sCW = sCA + kDSB * kGBM;
         v4i fa[2], fw[2], na[2], nw[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            na[i] = *reinterpret_cast<const v4i *>(sbase + offA[0][i]);
-            nw[i] = *reinterpret_cast<const v4i *>(sbase + offW[0][i]);
+            na[i] = *reinterpret_cast<const v4i *>(sbase + fbA[i]);
+            nw[i] = *reinterpret_cast<const v4i *>(sbase + fbW[i]);
         }
 #pragma unroll
-        for (int blk = 0; blk < kSB; ++blk) {
-            const int b = st * kSB + blk;
+        for (int blk = 0; blk < kDSB; ++blk) {
+            const int b = st * kDSB + blk;
 #pragma unroll
             for (int i = 0; i < 2; ++i) { fa[i] = na[i]; fw[i] = nw[i]; }
-            if (blk + 1 < kSB) {
+            if (blk + 1 < kDSB) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    na[i] = *reinterpret_cast<const v4i *>(sbase + offA[blk + 1][i]);
-                    nw[i] = *reinterpret_cast<const v4i *>(sbase + offW[blk + 1][i]);
+                    na[i] = *reinterpret_cast<const v4i *>(sbase + (fbA[i] ^ ((blk + 1) << 5)));
+                    nw[i] = *reinterpret_cast<const v4i *>(sbase + (fbW[i] ^ ((blk + 1) << 5)));
                 }
             }
             if (b >= nb) break;
-            // window position of block b (scalar selects: no table lookups)
             const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
             const int hi = b >= h1 ? nb : (b >= h0 ? h1 : h0);
             const int off = b - lo;
@@ -488,8 +519,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fw[j], I[i][j], 0, 0, 0);
-            // an aligned window has one scale per row for all its blocks, so
-            // the scales of its last block serve the whole window
             if (last || !aligned) {
                 float cw[2];
 #pragma unroll
@@ -507,33 +536,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm_grouped(
                                 acc[i][j][4 * q + e] = __builtin_fmaf((float)I[i][j][4 * q + e], sa * cw[j], acc[i][j][4 * q + e]);
                         }
                     }
+                // restart the integer sums with a zero-product MFMA (C = 0):
+                // the matrix core has slack here, the vector ALU has none
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) I[i][j] = zero;
+                    for (int j = 0; j < 2; ++j)
+                        I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
             }
         }
     };
 
-    MXS_LOAD(0, 0);
-    MXS_STORE(0, 0);
-    __syncthreads();
-    // iteration st: prefetch stage st + 1 into registers, compute stage st
-    // from buffer st & 1, then store the prefetched stage into the other buffer
-    for (int st = 0; st < nstage; st += 2) {
-        if (st + 1 < nstage) MXS_LOAD(0, st + 1);
-        compute(st, 0);
-        if (st + 1 >= nstage) break;
-        MXS_STORE(0, 1);
-        __syncthreads();
-        if (st + 2 < nstage) MXS_LOAD(0, st + 2);
-        compute(st + 1, 1);
-        if (st + 2 >= nstage) break;
-        MXS_STORE(0, 0);
-        __syncthreads();
+    // own loads of stage s done once at most two later stages are in flight
+#define MXS_DSTEP(s_, CUR, NXT)                                                               \
+    do {                                                                                      \
+        if ((s_) >= nstage) goto done;                                                        \
+        if (has_c) __builtin_amdgcn_s_waitcnt(0x0F70 | 12); /* vmcnt(12) */                   \
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | 9);        /* vmcnt(9) */                    \
+        lds_barrier();                                                                        \
+        dma_issue<NXT>(D, (s_) + 4, nstage, has_c);                                           \
+        compute((s_), dslot<CUR>());                                                          \
+    } while (0)
+
+    dma_issue<0>(D, 0, nstage, has_c);
+    dma_issue<1>(D, 1, nstage, has_c);
+    dma_issue<2>(D, 2, nstage, has_c);
+    dma_issue<3>(D, 3, nstage, has_c);
+    for (int s = 0; s < nstage; s += 5) {
+        MXS_DSTEP(s, 0, 4);
+        MXS_DSTEP(s + 1, 1, 0);
+        MXS_DSTEP(s + 2, 2, 1);
+        MXS_DSTEP(s + 3, 3, 2);
+        MXS_DSTEP(s + 4, 4, 3);
     }
-#undef MXS_LOAD
-#undef MXS_STORE
+done:
+#undef MXS_DSTEP
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -882,7 +920,7 @@ PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
     PrepLayout L;
     L.Mp = ceil_div(A.rows, kGBM) * kGBM;
     L.Np = ceil_div(W.rows, kGBN) * kGBN;
-    L.Kp = ceil_div(A.K, 32 * kSB) * (32 * kSB);   // whole stages (prep pads the tail)
+    L.Kp = ceil_div(A.K, 128) * 128;   // whole 4-block units (prep pads the tail)
     const int64_t nbp = L.Kp / 32;
     size_t off = 0;
     L.a_codes = off; off = align256(off + (size_t)L.Mp * L.Kp);
@@ -972,11 +1010,7 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    // more than 64 KiB of LDS needs the opt-in (idempotent, per call)
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_grouped),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)ntiles), dim3(512), 2 * kStage, st, ac, acs, wc, wcs,
+    hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
                        M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
     return hipGetLastError();
 }
