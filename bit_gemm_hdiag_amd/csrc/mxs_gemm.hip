@@ -606,7 +606,8 @@ done:
 // I_b * 2^(sa+sw) to an fp32 accumulator per token. K-slices write partial
 // rows that a second kernel adds in slice order, so the result does not
 // depend on scheduling.
-constexpr int kGemvMaxRows = 32;
+constexpr int kGemvMaxRows = 32;   // decode path: up to 32 tokens
+constexpr int kGemvVecRows = 8;    // up to 8 tokens on the vector ALU, above on the matrix cores
 constexpr int kGemvMaxSlice = 64;   // blocks per K-slice (multiple of 8)
 constexpr int kGemvPitch = 144;     // 8-bit and 4-bit tiles: 128 bytes + 16 (conflict-free b128 reads)
 constexpr int kGemvPitch6 = 104;    // 6-bit tile: 96 bytes + 8 (conflict-free b64 reads)
@@ -882,6 +883,185 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode with the matrix cores (kGemvMaxRows < M <= 32 in the dispatcher).
+//
+// Per output the vector kernel above spends ~7 operations per token and
+// block; here one v_mfma_i32_32x32x32_i8 yields a 32 token x 32 row tile of
+// exact block sums and the per-block epilogue costs 3 operations per output
+// for all 32 tokens. The W side is fetched and staged exactly as in k_gemv
+// (a wave owns 64 rows: two 32-row tiles). The tokens' codes of the K-slice
+// are unpacked once per workgroup into LDS as MFMA bytes (8-bit codes as is,
+// 6-bit codes * 4, 4-bit codes * 16; tokens past M are zero), together with
+// their scales times the inverse of that factor. W fragments are unpacked
+// from the staged tile the same way and in the same k order, so each block
+// sum is exact.
+constexpr int kGmBlocks = 16;      // K-slice length (blocks) of the MFMA decode kernel
+
+// 16 MFMA bytes (one k-half) of a 4-bit block half held as two dwords: the
+// low nibbles of each dword, then its high nibbles, each as code * 16
+__device__ __forceinline__ v4i unpack4_half(uint32_t w0, uint32_t w1) {
+    return v4i{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u), (int)((w1 << 4) & 0xF0F0F0F0u),
+               (int)(w1 & 0xF0F0F0F0u)};
+}
+
+// 16 MFMA bytes of a 6-bit block half: four 24-bit groups of 4 codes starting
+// at bit 0 of w[0..2] (96 bits), each as code * 4
+__device__ __forceinline__ v4i unpack6_half(const uint32_t w[3]) {
+    const uint32_t g0 = w[0] & 0xFFFFFFu;
+    const uint32_t g1 = __builtin_amdgcn_alignbit(w[1], w[0], 24) & 0xFFFFFFu;
+    const uint32_t g2 = __builtin_amdgcn_alignbit(w[2], w[1], 16) & 0xFFFFFFu;
+    const uint32_t g3 = w[2] >> 8;
+    return v4i{(int)wide6(g0), (int)wide6(g1), (int)wide6(g2), (int)wide6(g3)};
+}
+
+__global__ __launch_bounds__(256) void k_gemv_mfma(QView A, QView W, int32_t M, int64_t N, int32_t n8,
+                                                   int32_t n6, int32_t nb, int32_t bps,
+                                                   float *__restrict__ out, int64_t ldo, int64_t slice_stride) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[4][kGemvTile];
+    __shared__ __attribute__((aligned(16))) uint32_t sct[4][64 * kGemvScPitch / 4];
+    __shared__ __attribute__((aligned(16))) int8_t sA[kGmBlocks][32][32];   // [blk][token][k byte], halves swizzled
+    __shared__ __attribute__((aligned(16))) float sSA[kGmBlocks][32];       // token scales * fold
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+    const int64_t left = N - row0;
+    const int32_t rows_left = left < 64 ? (left < 0 ? 0 : (int32_t)left) : 64;
+    const int32_t b0 = (int32_t)blockIdx.y * bps;
+    const int32_t b1 = b0 + bps < nb ? b0 + bps : nb;
+    const int32_t h6 = n8 + n6;
+    const int64_t frow0 = rows_left > 0 ? row0 : 0;   // waves past N address row 0 (results dropped)
+
+    // tokens' blocks b0 .. b1-1 -> LDS (two (token, block) items per thread)
+    for (int it = tid; it < 32 * kGmBlocks; it += 256) {
+        const int t = it & 31, j = it >> 5;
+        const int32_t b = b0 + j;
+        if (b >= b1) continue;
+        v4i lo = v4i{0, 0, 0, 0}, hi = v4i{0, 0, 0, 0};
+        float sa = 0.f;
+        if (t < M) {
+            const uint32_t byte = A.sc[t * A.lds + b];
+            if (b < n8) {
+                const uint4 *q = reinterpret_cast<const uint4 *>(A.q8 + t * A.ld8 + 32 * (int64_t)b);
+                const uint4 x = q[0], y = q[1];
+                lo = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+                hi = v4i{(int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                sa = e8m0_to_f32(byte);
+            } else if (b < h6) {
+                const uint32_t *q = reinterpret_cast<const uint32_t *>(A.q6 + t * A.ld6 + 24 * (int64_t)(b - n8));
+                const uint32_t w0[3] = {q[0], q[1], q[2]}, w1[3] = {q[3], q[4], q[5]};
+                lo = unpack6_half(w0);
+                hi = unpack6_half(w1);
+                sa = e8m0_to_f32(byte) * 0.25f;
+            } else {
+                const uint2 *q = reinterpret_cast<const uint2 *>(A.q4 + t * A.ld4 + 16 * (int64_t)(b - h6));
+                const uint2 x = q[0], y = q[1];
+                lo = unpack4_half(x.x, x.y);
+                hi = unpack4_half(y.x, y.y);
+                sa = e8m0_to_f32(byte) * 0.0625f;
+            }
+        }
+        const int sw = (t >> 3) & 1;   // half h of token t sits at slot h ^ sw
+        *reinterpret_cast<v4i *>(&sA[j][t][16 * sw]) = lo;
+        *reinterpret_cast<v4i *>(&sA[j][t][16 * (1 - sw)]) = hi;
+        sSA[j][t] = sa;
+    }
+
+    uint8_t *my_tile = tile[wave];
+    uint32_t *my_sct = sct[wave];
+    uint32_t R[32];
+    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
+    gemv_fetch(W, frow0, rows_left, c, lane, R);
+    {
+        const int32_t nd = (b1 - b0 + 3) >> 2;
+        const int d = lane & 15, rq = lane >> 4;
+        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + frow0 * W.lds + b0);
+        const int64_t ldw = W.lds >> 2;
+        uint32_t v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = rq + 4 * i;
+            v[i] = sp[(d < nd && r < rows_left) ? r * ldw + d : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) my_sct[(rq + 4 * i) * (kGemvScPitch / 4) + d] = v[i];
+    }
+    __syncthreads();   // tokens staged
+
+    float acc[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const uint32_t *row_sc[2] = {my_sct + l32 * (kGemvScPitch / 4), my_sct + (32 + l32) * (kGemvScPitch / 4)};
+    const int aslot = 16 * (h ^ ((l32 >> 3) & 1));
+    while (true) {
+        gemv_stage(my_tile, c.cls, lane, R);
+        __builtin_amdgcn_wave_barrier();
+        const GemvChunk cur = c;
+        const int32_t next = cur.gb + cur.nblk;
+        if (next < b1) {
+            c = gemv_chunk(next, b1, n8, h6, nb);
+            gemv_fetch(W, frow0, rows_left, c, lane, R);
+        }
+        uint64_t swb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) swb[i] = bytes8(row_sc[i], cur.gb - b0, (next - 1 - b0) >> 2);
+        const float wfold = cur.cls == 8 ? 1.f : (cur.cls == 6 ? 0.25f : 0.0625f);
+        for (int j = 0; j < cur.nblk; ++j) {
+            const int jb = cur.gb - b0 + j;   // block within the slice
+            const v4i fa = *reinterpret_cast<const v4i *>(&sA[jb][l32][aslot]);
+            v4i fw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = i * 32 + l32;
+                if (cur.cls == 4) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(my_tile + r * kGemvPitch + 16 * j + 8 * h);
+                    fw[i] = unpack4_half(v.x, v.y);
+                } else if (cur.cls == 8) {
+                    fw[i] = *reinterpret_cast<const v4i *>(my_tile + r * kGemvPitch + 32 * j + 16 * h);
+                } else {
+                    const uint32_t *q = reinterpret_cast<const uint32_t *>(my_tile + r * kGemvPitch6 + 24 * j + 12 * h);
+                    const uint32_t w[3] = {q[0], q[1], q[2]};
+                    fw[i] = unpack6_half(w);
+                }
+            }
+            v16i I[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) I[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fw[i], zero, 0, 0, 0);
+            float sw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) sw[i] = e8m0_to_f32((uint32_t)(swb[i] >> (8 * j)) & 0xFFu) * wfold;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4_t sa = *reinterpret_cast<const f32x4_t *>(&sSA[jb][8 * q + 4 * h]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][4 * q + r] = __builtin_fmaf((float)I[i][4 * q + r], sa[r] * sw[i], acc[i][4 * q + r]);
+            }
+        }
+        if (next >= b1) break;
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t n = row0 + i * 32 + l32;
+        if (n >= N) continue;
+        float *o = out + (int64_t)blockIdx.y * slice_stride + n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 8 * q + 4 * h + r;
+                if (t < M) o[t * ldo] = acc[i][4 * q + r];
+            }
+    }
+}
+
 // Y[t, n] = sum over slices s (in order) of part[s][t][n]
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int32_t ns, int32_t M,
                                                      int64_t N, float *__restrict__ Y, int64_t ldy) {
@@ -961,14 +1141,38 @@ hipError_t launch_gemv_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t
     return hipGetLastError();
 }
 
+GemvPlan gemv_mfma_plan(const mxs_qmat &A, const mxs_qmat &W) {
+    const int32_t nb = (int32_t)(A.K / 32);
+    const int64_t wgs = ceil_div(W.rows, 256);
+    int64_t ns = ceil_div(2048, wgs);               // ~8 workgroups per CU in total
+    const int64_t min_ns = ceil_div(nb, kGmBlocks);
+    ns = ns < min_ns ? min_ns : ns;
+    int32_t bps = (int32_t)(ceil_div(ceil_div(nb, ns), 8) * 8);
+    bps = bps > kGmBlocks ? kGmBlocks : bps;
+    return GemvPlan{(int32_t)ceil_div(nb, bps), bps};
+}
+
+hipError_t launch_gemv_mfma(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
+    const GemvPlan P = gemv_mfma_plan(A, W);
+    const int64_t M = A.rows, N = W.rows;
+    const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)P.nslices);
+    float *dst = P.nslices == 1 ? Y : static_cast<float *>(ws);
+    hipLaunchKernelGGL(k_gemv_mfma, grid, dim3(256), 0, st, view_of(A), view_of(W), (int32_t)M, N, A.n8, A.n6,
+                       (int32_t)(A.K / 32), P.bps, dst, P.nslices == 1 ? ldy : N, P.nslices == 1 ? (int64_t)0 : M * N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || P.nslices == 1) return e;
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, dst, P.nslices,
+                       (int32_t)M, N, Y, ldy);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
     const int64_t M = A.rows;
+    if (M > kGemvVecRows) return launch_gemv_mfma(A, W, Y, ldy, ws, st);
     if (M <= 1) return launch_gemv_t<1>(A, W, Y, ldy, ws, st);
     if (M <= 2) return launch_gemv_t<2>(A, W, Y, ldy, ws, st);
     if (M <= 4) return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
-    if (M <= 8) return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
-    if (M <= 16) return launch_gemv_t<16>(A, W, Y, ldy, ws, st);
-    return launch_gemv_t<32>(A, W, Y, ldy, ws, st);
+    return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
 }
 
 }  // namespace
@@ -976,7 +1180,7 @@ hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t l
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
     if (W.rows == 0 || A.rows == 0) return 0;
     if (use_gemv(A, W)) {
-        const GemvPlan P = gemv_plan(A, W);
+        const GemvPlan P = A.rows > kGemvVecRows ? gemv_mfma_plan(A, W) : gemv_plan(A, W);
         return P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
     }
     if (!use_prefill(A)) return 0;
