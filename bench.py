@@ -19,6 +19,9 @@ profiles/ and is reported only while the GEMM source is unchanged since.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-probe   (a plain device copy of known size, to
                                        scale the HBM byte counters)
+       python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
+                                       and 32 tokens: one JSON line per case, GB/s
+                                       of packed W + scale bytes against HBM peak)
 """
 from __future__ import annotations
 
@@ -73,6 +76,32 @@ def copy_probe(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_each_way": COPY_BYTES, "dispatches": 3}), flush=True)
+
+
+def decode_cases(mx, synth, torch, reps=20):
+    """70B MLP decode GEMMs (up 28672 x 8192, down 8192 x 28672, 5/15/80 %)."""
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[4]
+    for li, lay in enumerate(cfg["layers"]):
+        N, K = lay["N"], lay["K"]
+        bp8, bp6 = lay["budget"]
+        seed = 4000 + 100 * li
+        gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+        Wt = synth.weights(N, K, seed + synth.ROLE_W, device=dev)
+        n8, n6, n4 = mx.mxs_budget_blocks(K, bp8, bp6)
+        perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(dev)
+        Wq = mx.mxs_quantize(Wt, perm, n8, n6, n4)
+        del Wt
+        wbytes = N * (32 * n8 + 24 * n6 + 16 * n4 + K // 32)
+        for M in cfg["Ms"]:
+            X = synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev)
+            Aq = mx.mxs_quantize(X, perm, n8, n6, n4)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(Aq, Wq)), dtype=torch.uint8, device=dev)
+            t = time_stage(torch, lambda: mx.mxs_mixed_gemm(Aq, Wq, Y, ws=ws), reps)
+            print(json.dumps({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": t * 1e6,
+                              "w_bytes": wbytes, "GBps": wbytes / t / 1e9, "hbm_frac": wbytes / t / HBM_PEAK}),
+                  flush=True)
 
 
 def build_workload(mx, synth, torch, dev):
@@ -196,6 +225,7 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -209,6 +239,9 @@ def main():
         return
     import bit_gemm_hdiag_amd as mx
     from bit_gemm_hdiag_amd import synth
+    if args.decode:
+        decode_cases(mx, synth, torch)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -16,9 +16,12 @@ LIB = os.path.join(OUT_DIR, "libmxsens.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["mxs_colsum.hip", "mxs_allocate.hip", "mxs_quantize.hip", "mxs_gemm.hip", "mxs_api.hip"]
-# packed fp32 instructions are disabled for all device code
+# packed fp32 instructions are disabled for all device code; common-code
+# sinking is off because merging the tails of per-width branches turned
+# register arrays of the decode kernels into scratch memory
 FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-simplifycfg-sink-common=false",
          "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -589,9 +589,11 @@ done:
 }
 
 // ---------------------------------------------------------------------------
-// Decode path (M <= kGemvMaxRows): stream W once from HBM.
+// Decode path (M <= kGemvMaxRows tokens): stream W once from HBM. Up to
+// kGemvVecRows tokens use the vector kernel below (k_gemv), more tokens the
+// matrix-core kernel further down (k_decode).
 //
-// A wavefront owns 64 W rows and one K-slice of at most kGemvMaxSlice
+// k_gemv: a wavefront owns 64 W rows and one K-slice of at most kGemvMaxSlice
 // blocks. The rows' scale bytes of the whole slice are loaded once (aligned
 // dwords) into LDS. The slice's codes are walked in chunks of whole blocks
 // of one width class (8-bit: 4 blocks, 6-bit: 4, 4-bit: 8; 128, 96 and 128
@@ -607,7 +609,7 @@ done:
 // rows that a second kernel adds in slice order, so the result does not
 // depend on scheduling.
 constexpr int kGemvMaxRows = 32;   // decode path: up to 32 tokens
-constexpr int kGemvVecRows = 8;    // up to 8 tokens on the vector ALU, above on the matrix cores
+constexpr int kGemvVecRows = 4;    // up to 4 tokens on the vector ALU, above on the matrix cores
 constexpr int kGemvMaxSlice = 64;   // blocks per K-slice (multiple of 8)
 constexpr int kGemvPitch = 144;     // 8-bit and 4-bit tiles: 128 bytes + 16 (conflict-free b128 reads)
 constexpr int kGemvPitch6 = 104;    // 6-bit tile: 96 bytes + 8 (conflict-free b64 reads)
@@ -884,19 +886,24 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
 }
 
 // ---------------------------------------------------------------------------
-// Decode with the matrix cores (kGemvMaxRows < M <= 32 in the dispatcher).
+// Decode with the matrix cores.
 //
-// Per output the vector kernel above spends ~7 operations per token and
-// block; here one v_mfma_i32_32x32x32_i8 yields a 32 token x 32 row tile of
-// exact block sums and the per-block epilogue costs 3 operations per output
-// for all 32 tokens. The W side is fetched and staged exactly as in k_gemv
-// (a wave owns 64 rows: two 32-row tiles). The tokens' codes of the K-slice
-// are unpacked once per workgroup into LDS as MFMA bytes (8-bit codes as is,
-// 6-bit codes * 4, 4-bit codes * 16; tokens past M are zero), together with
-// their scales times the inverse of that factor. W fragments are unpacked
-// from the staged tile the same way and in the same k order, so each block
-// sum is exact.
-constexpr int kGmBlocks = 16;      // K-slice length (blocks) of the MFMA decode kernel
+// One v_mfma_i32_32x32x32_i8 yields a 32 token x 32 row tile of exact block
+// sums; the per-block epilogue (convert, scale, accumulate) then runs only
+// over the tiles' token rows below M, so its cost grows with ceil(M / 8) and
+// not with the 32-token tile. Codes enter the MFMA as bytes (8-bit as is,
+// 6-bit * 4, 4-bit * 16, the factor folded into the scales); W fragments and
+// token fragments are unpacked in registers in the same k order.
+//
+// A workgroup of four waves owns 64 W rows and one K range of 4 * bpw
+// blocks; wave w takes the w-th quarter of it, so the four partial sums of a
+// row meet in LDS (added in wave order) instead of in global memory. W
+// chunks are fetched and staged per wave as in k_gemv; the W scale bytes and
+// the tokens' scales (times the fold factor) of the whole range are staged
+// once per workgroup; the tokens' code fragments are loaded with the W
+// chunk, one chunk ahead. Ranges of different workgroups write partial rows
+// that k_gemv_reduce adds in range order.
+constexpr int kDecMaxBpw = 32;     // blocks per wave (a multiple of 8)
 
 // 16 MFMA bytes (one k-half) of a 4-bit block half held as two dwords: the
 // low nibbles of each dword, then its high nibbles, each as code * 16
@@ -915,79 +922,100 @@ __device__ __forceinline__ v4i unpack6_half(const uint32_t w[3]) {
     return v4i{(int)wide6(g0), (int)wide6(g1), (int)wide6(g2), (int)wide6(g3)};
 }
 
-__global__ __launch_bounds__(256) void k_gemv_mfma(QView A, QView W, int32_t M, int64_t N, int32_t n8,
-                                                   int32_t n6, int32_t nb, int32_t bps,
-                                                   float *__restrict__ out, int64_t ldo, int64_t slice_stride) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[4][kGemvTile];
-    __shared__ __attribute__((aligned(16))) uint32_t sct[4][64 * kGemvScPitch / 4];
-    __shared__ __attribute__((aligned(16))) int8_t sA[kGmBlocks][32][32];   // [blk][token][k byte], halves swizzled
-    __shared__ __attribute__((aligned(16))) float sSA[kGmBlocks][32];       // token scales * fold
+struct DecLds {                    // byte offsets into the dynamic LDS
+    int wsc, wsc_pitch, asc, total;
+};
+
+__host__ __device__ inline DecLds dec_lds(int bpw) {
+    DecLds L;
+    L.wsc = 4 * kGemvTile;                     // after the four W tiles
+    L.wsc_pitch = 4 * bpw + 4;                 // bytes per W row (pitch/4 odd: conflict-free dword reads)
+    L.asc = L.wsc + 64 * L.wsc_pitch;
+    L.total = L.asc + 4 * bpw * 32 * 4;        // [block][token] floats
+    return L;
+}
+
+// token fragment loads of one chunk (lane: token l % 32, k-half l / 32).
+// Branch-free: lanes of tokens past M read token 0 and blocks past the chunk
+// read its first block; those values meet zero token scales or are never
+// used.
+__device__ __forceinline__ void dec_fetch_a(const QView &A, int32_t M, const GemvChunk &c, int t, int h,
+                                            uint32_t RA[16]) {
+    const int64_t tr = t < M ? t : 0;
+    if (c.cls == 4) {
+        const uint8_t *base = A.q4 + tr * A.ld4 + 16 * (int64_t)c.pb + 8 * h;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(base + 16 * (j < c.nblk ? j : 0));
+            RA[2 * j] = v.x; RA[2 * j + 1] = v.y;
+        }
+    } else if (c.cls == 8) {
+        const int8_t *base = A.q8 + tr * A.ld8 + 32 * (int64_t)c.pb + 16 * h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(base + 32 * (j < c.nblk ? j : 0));
+            RA[4 * j] = v.x; RA[4 * j + 1] = v.y; RA[4 * j + 2] = v.z; RA[4 * j + 3] = v.w;
+        }
+    } else {
+        const uint8_t *base = A.q6 + tr * A.ld6 + 24 * (int64_t)c.pb + 12 * h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(base + 24 * (j < c.nblk ? j : 0));
+            RA[3 * j] = q[0]; RA[3 * j + 1] = q[1]; RA[3 * j + 2] = q[2];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int64_t N, int32_t n8, int32_t n6,
+                                                int32_t nb, int32_t bpw, float *__restrict__ out, int64_t ldo,
+                                                int64_t slice_stride) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dlds[];
+    const DecLds L = dec_lds(bpw);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
-    const int64_t left = N - row0;
-    const int32_t rows_left = left < 64 ? (left < 0 ? 0 : (int32_t)left) : 64;
-    const int32_t b0 = (int32_t)blockIdx.y * bps;
-    const int32_t b1 = b0 + bps < nb ? b0 + bps : nb;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const int32_t rows_left = N - row0 < 64 ? (int32_t)(N - row0) : 64;
+    const int32_t g0 = (int32_t)blockIdx.y * 4 * bpw;                  // workgroup range [g0, g1)
+    const int32_t g1 = g0 + 4 * bpw < nb ? g0 + 4 * bpw : nb;
+    const int32_t b0 = g0 + wave * bpw < g1 ? g0 + wave * bpw : g1;     // this wave's quarter
+    const int32_t b1 = b0 + bpw < g1 ? b0 + bpw : g1;
     const int32_t h6 = n8 + n6;
-    const int64_t frow0 = rows_left > 0 ? row0 : 0;   // waves past N address row 0 (results dropped)
+    uint8_t *my_tile = dlds + wave * kGemvTile;
+    uint8_t *wsc = dlds + L.wsc;
+    float *asc = reinterpret_cast<float *>(dlds + L.asc);
 
-    // tokens' blocks b0 .. b1-1 -> LDS (two (token, block) items per thread)
-    for (int it = tid; it < 32 * kGmBlocks; it += 256) {
-        const int t = it & 31, j = it >> 5;
-        const int32_t b = b0 + j;
-        if (b >= b1) continue;
-        v4i lo = v4i{0, 0, 0, 0}, hi = v4i{0, 0, 0, 0};
-        float sa = 0.f;
-        if (t < M) {
-            const uint32_t byte = A.sc[t * A.lds + b];
-            if (b < n8) {
-                const uint4 *q = reinterpret_cast<const uint4 *>(A.q8 + t * A.ld8 + 32 * (int64_t)b);
-                const uint4 x = q[0], y = q[1];
-                lo = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
-                hi = v4i{(int)y.x, (int)y.y, (int)y.z, (int)y.w};
-                sa = e8m0_to_f32(byte);
-            } else if (b < h6) {
-                const uint32_t *q = reinterpret_cast<const uint32_t *>(A.q6 + t * A.ld6 + 24 * (int64_t)(b - n8));
-                const uint32_t w0[3] = {q[0], q[1], q[2]}, w1[3] = {q[3], q[4], q[5]};
-                lo = unpack6_half(w0);
-                hi = unpack6_half(w1);
-                sa = e8m0_to_f32(byte) * 0.25f;
-            } else {
-                const uint2 *q = reinterpret_cast<const uint2 *>(A.q4 + t * A.ld4 + 16 * (int64_t)(b - h6));
-                const uint2 x = q[0], y = q[1];
-                lo = unpack4_half(x.x, x.y);
-                hi = unpack4_half(y.x, y.y);
-                sa = e8m0_to_f32(byte) * 0.0625f;
-            }
-        }
-        const int sw = (t >> 3) & 1;   // half h of token t sits at slot h ^ sw
-        *reinterpret_cast<v4i *>(&sA[j][t][16 * sw]) = lo;
-        *reinterpret_cast<v4i *>(&sA[j][t][16 * (1 - sw)]) = hi;
-        sSA[j][t] = sa;
-    }
-
-    uint8_t *my_tile = tile[wave];
-    uint32_t *my_sct = sct[wave];
-    uint32_t R[32];
-    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
-    gemv_fetch(W, frow0, rows_left, c, lane, R);
+    // W scale bytes of the range (aligned dwords: g0 is a multiple of 32)
     {
-        const int32_t nd = (b1 - b0 + 3) >> 2;
-        const int d = lane & 15, rq = lane >> 4;
-        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + frow0 * W.lds + b0);
+        const int32_t nd = (g1 - g0 + 3) >> 2;
+        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + row0 * W.lds + g0);
         const int64_t ldw = W.lds >> 2;
-        uint32_t v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = rq + 4 * i;
-            v[i] = sp[(d < nd && r < rows_left) ? r * ldw + d : 0];
+        for (int it = tid; it < 64 * nd; it += 256) {
+            const int r = it / nd, d = it - r * nd;
+            const uint32_t v = sp[r < rows_left ? r * ldw + d : 0];
+            *reinterpret_cast<uint32_t *>(wsc + r * L.wsc_pitch + 4 * d) = v;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) my_sct[(rq + 4 * i) * (kGemvScPitch / 4) + d] = v[i];
     }
-    __syncthreads();   // tokens staged
+    // tokens' scales of the range, times the MFMA byte factor's inverse; zero past M
+    for (int it = tid; it < 32 * 4 * bpw; it += 256) {
+        const int t = it & 31, j = it >> 5;
+        const int32_t b = g0 + j;
+        float v = 0.f;
+        if (t < M && b < g1) {
+            const float fold = b < n8 ? 1.f : (b < h6 ? 0.25f : 0.0625f);
+            v = e8m0_to_f32(A.sc[t * A.lds + b]) * fold;
+        }
+        asc[j * 32 + t] = v;
+    }
+
+    uint32_t R[32], RA[16];
+    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
+    const bool work = b0 < b1;
+    if (work) {
+        gemv_fetch(W, row0, rows_left, c, lane, R);
+        dec_fetch_a(A, M, c, l32, h, RA);
+    }
+    __syncthreads();   // scales staged
 
     float acc[2][16];
 #pragma unroll
@@ -995,35 +1023,49 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(QView A, QView W, int32_t M, 
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const uint32_t *row_sc[2] = {my_sct + l32 * (kGemvScPitch / 4), my_sct + (32 + l32) * (kGemvScPitch / 4)};
-    const int aslot = 16 * (h ^ ((l32 >> 3) & 1));
-    while (true) {
+    const int qmax = (M + 7) >> 3;
+    const uint32_t *row_sc[2] = {reinterpret_cast<const uint32_t *>(wsc + l32 * L.wsc_pitch),
+                                 reinterpret_cast<const uint32_t *>(wsc + (32 + l32) * L.wsc_pitch)};
+    while (work) {
         gemv_stage(my_tile, c.cls, lane, R);
+        uint32_t CA[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) CA[i] = RA[i];
         __builtin_amdgcn_wave_barrier();
         const GemvChunk cur = c;
         const int32_t next = cur.gb + cur.nblk;
         if (next < b1) {
             c = gemv_chunk(next, b1, n8, h6, nb);
-            gemv_fetch(W, frow0, rows_left, c, lane, R);
+            gemv_fetch(W, row0, rows_left, c, lane, R);
+            dec_fetch_a(A, M, c, l32, h, RA);
         }
         uint64_t swb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) swb[i] = bytes8(row_sc[i], cur.gb - b0, (next - 1 - b0) >> 2);
+        for (int i = 0; i < 2; ++i) swb[i] = bytes8(row_sc[i], cur.gb - g0, (next - 1 - g0) >> 2);
         const float wfold = cur.cls == 8 ? 1.f : (cur.cls == 6 ? 0.25f : 0.0625f);
-        for (int j = 0; j < cur.nblk; ++j) {
-            const int jb = cur.gb - b0 + j;   // block within the slice
-            const v4i fa = *reinterpret_cast<const v4i *>(&sA[jb][l32][aslot]);
-            v4i fw[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = i * 32 + l32;
-                if (cur.cls == 4) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(my_tile + r * kGemvPitch + 16 * j + 8 * h);
+        for (int j = 0; j < 8; ++j) {
+            if (j >= cur.nblk) break;
+            if (cur.cls != 4 && j >= 4) break;
+            v4i fa, fw[2];
+            if (cur.cls == 4) {
+                fa = unpack4_half(CA[2 * j], CA[2 * j + 1]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(my_tile + (i * 32 + l32) * kGemvPitch + 16 * j + 8 * h);
                     fw[i] = unpack4_half(v.x, v.y);
-                } else if (cur.cls == 8) {
-                    fw[i] = *reinterpret_cast<const v4i *>(my_tile + r * kGemvPitch + 32 * j + 16 * h);
-                } else {
-                    const uint32_t *q = reinterpret_cast<const uint32_t *>(my_tile + r * kGemvPitch6 + 24 * j + 12 * h);
+                }
+            } else if (cur.cls == 8) {
+                fa = v4i{(int)CA[(4 * j) & 15], (int)CA[(4 * j + 1) & 15], (int)CA[(4 * j + 2) & 15], (int)CA[(4 * j + 3) & 15]};
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    fw[i] = *reinterpret_cast<const v4i *>(my_tile + (i * 32 + l32) * kGemvPitch + 32 * j + 16 * h);
+            } else {
+                const uint32_t wa[3] = {CA[(3 * j) & 15], CA[(3 * j + 1) & 15], CA[(3 * j + 2) & 15]};
+                fa = unpack6_half(wa);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t *q = reinterpret_cast<const uint32_t *>(my_tile + (i * 32 + l32) * kGemvPitch6 + 24 * j + 12 * h);
                     const uint32_t w[3] = {q[0], q[1], q[2]};
                     fw[i] = unpack6_half(w);
                 }
@@ -1034,9 +1076,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(QView A, QView W, int32_t M, 
             float sw[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) sw[i] = e8m0_to_f32((uint32_t)(swb[i] >> (8 * j)) & 0xFFu) * wfold;
+            const float *sa_blk = asc + (cur.gb - g0 + j) * 32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x4_t sa = *reinterpret_cast<const f32x4_t *>(&sSA[jb][8 * q + 4 * h]);
+                if (q >= qmax) break;
+                const f32x4_t sa = *reinterpret_cast<const f32x4_t *>(sa_blk + 8 * q + 4 * h);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -1047,18 +1091,33 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(QView A, QView W, int32_t M, 
         if (next >= b1) break;
         __builtin_amdgcn_wave_barrier();
     }
+
+    // the four waves' sums of each output, added in wave order
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(dlds);   // [wave][q][i][r][lane], the W tiles are free now
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q >= qmax) break;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(((wave * 4 + q) * 2 + i) * 4 + r) * 64 + lane] = acc[i][4 * q + r];
+    }
+    __syncthreads();
+    // wave w finishes token group q = w (tokens 8w .. 8w+7)
+    const int q = wave;
+    if (q >= qmax) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t n = row0 + i * 32 + l32;
-        if (n >= N) continue;
-        float *o = out + (int64_t)blockIdx.y * slice_stride + n;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int r = 0; r < 4; ++r) {
+            float v = red[(((0 * 4 + q) * 2 + i) * 4 + r) * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 8 * q + 4 * h + r;
-                if (t < M) o[t * ldo] = acc[i][4 * q + r];
-            }
+            for (int w = 1; w < 4; ++w) v = v + red[(((w * 4 + q) * 2 + i) * 4 + r) * 64 + lane];
+            const int t = 8 * q + 4 * h + r;
+            if (n < N && t < M) out[(int64_t)blockIdx.y * slice_stride + t * ldo + n] = v;
+        }
     }
 }
 
@@ -1141,25 +1200,36 @@ hipError_t launch_gemv_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t
     return hipGetLastError();
 }
 
-GemvPlan gemv_mfma_plan(const mxs_qmat &A, const mxs_qmat &W) {
+// Decode plan: blocks per wave (bpw) and the number of K ranges. Ranges of
+// 4 * bpw blocks; enough workgroups for ~3 per CU, but few enough ranges
+// that the partial rows (8 M N bytes per range, written and read back) stay
+// small next to W.
+GemvPlan decode_plan(const mxs_qmat &A, const mxs_qmat &W) {
     const int32_t nb = (int32_t)(A.K / 32);
-    const int64_t wgs = ceil_div(W.rows, 256);
-    int64_t ns = ceil_div(2048, wgs);               // ~8 workgroups per CU in total
-    const int64_t min_ns = ceil_div(nb, kGmBlocks);
-    ns = ns < min_ns ? min_ns : ns;
-    int32_t bps = (int32_t)(ceil_div(ceil_div(nb, ns), 8) * 8);
-    bps = bps > kGmBlocks ? kGmBlocks : bps;
-    return GemvPlan{(int32_t)ceil_div(nb, bps), bps};
+    const int64_t tiles = ceil_div(W.rows, 64);
+    const int64_t row_bytes = 32 * (int64_t)A.n8 + 24 * (int64_t)A.n6 + 16 * (int64_t)A.n4 + nb;
+    int64_t ns = ceil_div(768, tiles);
+    const int64_t cap = (row_bytes / 8) / (8 * (A.rows > 0 ? A.rows : 1));   // partials <= ~1/8 of W
+    ns = ns > cap ? cap : ns;
+    ns = ns < 1 ? 1 : ns;
+    int32_t bpw = (int32_t)(ceil_div(ceil_div(nb, 4 * ns), 8) * 8);
+    bpw = bpw > kDecMaxBpw ? kDecMaxBpw : bpw;
+    return GemvPlan{(int32_t)ceil_div(nb, 4 * bpw), bpw};
 }
 
-hipError_t launch_gemv_mfma(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
-    const GemvPlan P = gemv_mfma_plan(A, W);
+hipError_t launch_decode(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
+    const GemvPlan P = decode_plan(A, W);
     const int64_t M = A.rows, N = W.rows;
-    const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)P.nslices);
+    const DecLds L = dec_lds(P.bps);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_decode),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(kDecMaxBpw).total);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)P.nslices);
     float *dst = P.nslices == 1 ? Y : static_cast<float *>(ws);
-    hipLaunchKernelGGL(k_gemv_mfma, grid, dim3(256), 0, st, view_of(A), view_of(W), (int32_t)M, N, A.n8, A.n6,
-                       (int32_t)(A.K / 32), P.bps, dst, P.nslices == 1 ? ldy : N, P.nslices == 1 ? (int64_t)0 : M * N);
-    hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL(k_decode, grid, dim3(256), (size_t)L.total, st, view_of(A), view_of(W), (int32_t)M, N, A.n8,
+                       A.n6, (int32_t)(A.K / 32), P.bps, dst, P.nslices == 1 ? ldy : N,
+                       P.nslices == 1 ? (int64_t)0 : M * N);
+    e = hipGetLastError();
     if (e != hipSuccess || P.nslices == 1) return e;
     hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, dst, P.nslices,
                        (int32_t)M, N, Y, ldy);
@@ -1168,11 +1238,10 @@ hipError_t launch_gemv_mfma(const mxs_qmat &A, const mxs_qmat &W, float *Y, int6
 
 hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
     const int64_t M = A.rows;
-    if (M > kGemvVecRows) return launch_gemv_mfma(A, W, Y, ldy, ws, st);
+    if (M > kGemvVecRows) return launch_decode(A, W, Y, ldy, ws, st);
     if (M <= 1) return launch_gemv_t<1>(A, W, Y, ldy, ws, st);
     if (M <= 2) return launch_gemv_t<2>(A, W, Y, ldy, ws, st);
-    if (M <= 4) return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
-    return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
+    return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
 }
 
 }  // namespace
@@ -1180,8 +1249,11 @@ hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t l
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
     if (W.rows == 0 || A.rows == 0) return 0;
     if (use_gemv(A, W)) {
-        const GemvPlan P = A.rows > kGemvVecRows ? gemv_mfma_plan(A, W) : gemv_plan(A, W);
-        return P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+        const GemvPlan P = decode_plan(A, W);
+        const GemvPlan Q = gemv_plan(A, W);
+        const size_t a = P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+        const size_t b = Q.nslices > 1 ? (size_t)Q.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+        return a > b ? a : b;
     }
     if (!use_prefill(A)) return 0;
     return prep_layout(A, W).total;
