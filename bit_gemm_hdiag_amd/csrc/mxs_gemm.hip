@@ -1121,14 +1121,23 @@ __global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int
     }
 }
 
-// Y[t, n] = sum over slices s (in order) of part[s][t][n]
+// Y[t, n] = sum over slices s (in order) of part[s][t][n]; loads run eight
+// slices ahead of the ordered additions
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int32_t ns, int32_t M,
                                                      int64_t N, float *__restrict__ Y, int64_t ldy) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)M * N) return;
-    const int64_t t = i / N, n = i - t * N;
+    const int64_t t = i / N, n = i - t * N, stride = (int64_t)M * N;
     float v = 0.f;
-    for (int32_t s = 0; s < ns; ++s) v = v + part[(int64_t)s * M * N + i];
+    int32_t s = 0;
+    for (; s + 8 <= ns; s += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = part[(int64_t)(s + u) * stride + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v = v + x[u];
+    }
+    for (; s < ns; ++s) v = v + part[(int64_t)s * stride + i];
     Y[t * ldy + n] = v;
 }
 
