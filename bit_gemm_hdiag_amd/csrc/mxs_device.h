@@ -123,6 +123,47 @@ __device__ __forceinline__ BlockScale quantize8(const float v[8], int m, int c[8
     return bs;
 }
 
+// Quantise the 8 values a lane holds and pack their codes for width m
+// (4: bits 4i.., 32 bits; 6: bits 6i.., 48 bits; 8: byte i, 64 bits), the
+// layout of pack4 / pack6 / pack8 below; `byte` receives the block's E8M0
+// byte. All 4 lanes of the quad must be active.
+// fma(v, 2^-s, 1.5 * 2^23) rounds v / 2^s to nearest even into the low
+// mantissa bits (v / 2^s is exact and |v / 2^s| < 2^7, so the sum stays in
+// the binade [2^23, 2^24) whose ulp is 1); the symmetric clamp is a median
+// against 1.5 * 2^23 -+ cmax; the low byte of the float's bits is then the
+// two's-complement code. A non-finite block's codes are 0.
+__device__ __forceinline__ uint32_t nib4(uint32_t x) {   // four code bytes -> 16 bits
+    const uint32_t y = (x & 0x000F000Fu) | ((x >> 4) & 0x00F000F0u);
+    return (y & 0xFFu) | ((y >> 8) & 0xFF00u);
+}
+__device__ __forceinline__ uint32_t six4(uint32_t x) {   // four code bytes -> 24 bits
+    const uint32_t u = (x & 0x003F003Fu) | ((x >> 2) & 0x0FC00FC0u);
+    return (u & 0xFFFu) | ((u >> 4) & 0xFFF000u);
+}
+__device__ __forceinline__ uint64_t quantize_pack8(const float v[8], int m, uint32_t &byte) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+        a = a > b ? a : b;
+    }
+    a = quad_max_u32(a);
+    const BlockScale bs = block_scale(a, m);
+    byte = bs.byte;
+    const float magic = 12582912.0f, cm = cmax_of(m);
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        b[i] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], bs.inv, magic), magic - cm, magic + cm));
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+    const uint32_t hi = __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu);
+    uint64_t w;
+    if (m == 8) w = lo | ((uint64_t)hi << 32);
+    else if (m == 6) w = six4(lo) | ((uint64_t)six4(hi) << 24);
+    else w = nib4(lo) | (nib4(hi) << 16);
+    return bs.bad ? 0 : w;
+}
+
 // ---------------------------------------------------------------- packing
 // 4-bit: code i in bits 4i..4i+3 (byte h = c_2h | c_2h+1 << 4).
 __device__ __forceinline__ uint32_t pack4(const int c[8]) {

@@ -295,8 +295,14 @@ __device__ __forceinline__ uint32_t spread6(uint32_t g) {
 __global__ __launch_bounds__(256) void k_mx_prep(QView A, QView W, int64_t M, int64_t N, int64_t groups_a,
                                                  int32_t n8, int32_t n6, int32_t n4, XPlan P,
                                                  int8_t *__restrict__ outA, int8_t *__restrict__ outW) {
-    const bool is_a = blockIdx.x < groups_a * P.ns;
-    const int64_t id = is_a ? blockIdx.x : blockIdx.x - groups_a * P.ns;
+    // records in (matrix, group, stage) order; workgroups are dealt
+    // round-robin to the 8 XCDs, so XCD x takes the x-th eighth of the
+    // records: consecutive stages of a group (the same rows, adjacent bytes
+    // of each 128-byte line) then share one L2
+    int64_t t = blockIdx.x;
+    if (gridDim.x % 8 == 0) t = (t % 8) * (gridDim.x / 8) + t / 8;
+    const bool is_a = t < groups_a * P.ns;
+    const int64_t id = is_a ? t : t - groups_a * P.ns;
     const int64_t g = id / P.ns;
     const int32_t s = (int32_t)(id % P.ns);
     const QView &Q = is_a ? A : W;

@@ -34,16 +34,16 @@ struct Planes {
 
 __device__ __forceinline__ void emit(const Planes &P, int64_t row, int64_t blk, int q, const float v[8]) {
     const int m = blk < P.n8 ? 8 : (blk < (int64_t)P.n8 + P.n6 ? 6 : 4);
-    int c[8];
-    BlockScale bs = quantize8(v, m, c);
+    uint32_t byte;
+    const uint64_t w = quantize_pack8(v, m, byte);
     if (m == 8) {
-        store_bytes(reinterpret_cast<uint8_t *>(P.q8) + row * P.ld8 + 32 * blk + 8 * q, pack8(c), 8);
+        store_bytes(reinterpret_cast<uint8_t *>(P.q8) + row * P.ld8 + 32 * blk + 8 * q, w, 8);
     } else if (m == 6) {
-        store_bytes(P.q6 + row * P.ld6 + 24 * (blk - P.n8) + 6 * q, pack6(c), 6);
+        store_bytes(P.q6 + row * P.ld6 + 24 * (blk - P.n8) + 6 * q, w, 6);
     } else {
-        store_bytes(P.q4 + row * P.ld4 + 16 * (blk - P.n8 - P.n6) + 4 * q, pack4(c), 4);
+        store_bytes(P.q4 + row * P.ld4 + 16 * (blk - P.n8 - P.n6) + 4 * q, w, 4);
     }
-    if (q == 0) P.sc[row * P.lds + blk] = (uint8_t)bs.byte;
+    if (q == 0) P.sc[row * P.lds + blk] = (uint8_t)byte;
 }
 
 template <typename T, bool VEC>
