@@ -7,9 +7,11 @@ MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128). Inputs are
 resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
-(2 M N K per step over the step time); per-stage times, TOPS and GB/s are
-in `stages`; `roofline` is for the dominant kernel; `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the same step.
+(2 M N K per step over the step time) with mxs_mixed_gemm (int8 block sums);
+per-stage times, TOPS and GB/s are in `stages`; `roofline` is for the
+dominant kernel; `variant_mx` repeats the step with mxs_mixed_gemm_mx
+(prefill on the block-scaled fp6 matrix cores); `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same step.
 
 The dominant kernel's roofline uses the mixed_gemm call's own duration,
 timed with HIP events on its stream inside every timed step; its HBM
@@ -49,9 +51,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per mixed_gemm call from the stored counter summary, or None
-    when the summary is missing or the GEMM source changed since it was taken."""
+def measured_traffic(key="traffic_bytes_per_call"):
+    """HBM bytes per mixed_gemm call (key traffic_bytes_per_call_mx: per
+    mixed_gemm_mx call) from the stored counter summary, or None when the
+    summary is missing or the GEMM source changed since it was taken."""
     try:
         kv = {}
         with open(GEMM_TRAFFIC) as f:
@@ -63,7 +66,7 @@ def measured_traffic():
             sha = hashlib.sha256(f.read()).hexdigest()
         if kv.get("source_sha256") != sha:
             return None
-        return float(kv["traffic_bytes_per_call"])
+        return float(kv[key])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -132,21 +135,25 @@ def build_workload(mx, synth, torch, dev):
     w["Wq"] = mx.qmat_alloc(N, K, n8, n6, n4, dev)
     w["Y"] = torch.empty((M, N), dtype=torch.float32, device=dev)
     w["ws_g"] = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(w["Aq"], w["Wq"])), **u8)
+    w["ws_gx"] = torch.empty(max(1, mx.mxs_mixed_gemm_mx_workspace(w["Aq"], w["Wq"])), **u8)
     T, H, D = cfg["kv"]["T"], cfg["kv"]["H"], cfg["kv"]["D"]
     w["kc"] = [torch.empty((T, H, D // 2), **u8) for _ in range(2)]
     w["ks"] = [torch.empty((T, H, D // 32), **u8) for _ in range(2)]
     return w
 
 
-def stage_fns(mx, w):
+def stage_fns(mx, w, variant=False):
+    """The step's stages; with variant=True the GEMM stage is mixed_gemm_mx."""
     n8, n6, n4 = w["blocks"]
+    gemm = ((lambda: mx.mxs_mixed_gemm_mx(w["Aq"], w["Wq"], w["Y"], ws=w["ws_gx"])) if variant
+            else (lambda: mx.mxs_mixed_gemm(w["Aq"], w["Wq"], w["Y"], ws=w["ws_g"])))
     return [
         ("calibrate", lambda: (w["hdiag"].zero_(), mx.mxs_calibrate(w["Xc"], w["hdiag"], ws=w["ws_cal"]))),
         ("score", lambda: mx.mxs_score(w["W"], w["hdiag"], w["score"], ws=w["ws_sc"])),
         ("allocate", lambda: mx.mxs_allocate(w["score"], w["bp8"], w["bp6"], w["bits"], w["perm"])),
         ("quantize_w", lambda: mx.mxs_quantize(w["W"], w["perm"], n8, n6, n4, out=w["Wq"])),
         ("quantize_x", lambda: mx.mxs_quantize(w["X"], w["perm"], n8, n6, n4, out=w["Aq"])),
-        ("mixed_gemm", lambda: mx.mxs_mixed_gemm(w["Aq"], w["Wq"], w["Y"], ws=w["ws_g"])),
+        ("mixed_gemm", gemm),
         ("quantize_kv", lambda: (mx.mxs_quantize_kv(w["Kc"], w["kc"][0], w["ks"][0]),
                                  mx.mxs_quantize_kv(w["Vc"], w["kc"][1], w["ks"][1]))),
     ]
@@ -248,48 +255,58 @@ def main():
     torch.cuda.set_device(dev)
     log("building workload")
     w = build_workload(mx, synth, torch, dev)
+
+    def run_steps(stages):
+        """Warm up, then time args.steps whole steps; the GEMM call is also
+        timed with events on its own inside every timed step."""
+        gemm_ev = []
+
+        def step(timed=False):
+            for name, fn in stages:
+                if timed and name == "mixed_gemm":
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn()
+                    b.record()
+                    gemm_ev.append((a, b))
+                else:
+                    fn()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            step(timed=True)
+        e.record()
+        torch.cuda.synchronize()
+        step_s = s.elapsed_time(e) / args.steps * 1e-3
+        gemm_s = sum(a.elapsed_time(b) for a, b in gemm_ev) / len(gemm_ev) * 1e-3
+        return step_s, gemm_s
+
     stages = stage_fns(mx, w)
-
-    gemm_ev = []
-
-    def step(timed=False):
-        for name, fn in stages:
-            if timed and name == "mixed_gemm":
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn()
-                b.record()
-                gemm_ev.append((a, b))
-            else:
-                fn()
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(args.steps):
-        step(timed=True)
-    e.record()
-    torch.cuda.synchronize()
-    step_s = s.elapsed_time(e) / args.steps * 1e-3
-    gemm_call_s = sum(a.elapsed_time(b) for a, b in gemm_ev) / len(gemm_ev) * 1e-3
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    step_s, gemm_call_s = run_steps(stages)
     log(f"step {step_s * 1e3:.3f} ms, mixed_gemm call {gemm_call_s * 1e6:.1f} us")
+    log("the same step with mixed_gemm_mx")
+    step_x, gemm_x = run_steps(stage_fns(mx, w, variant=True))
+    log(f"step {step_x * 1e3:.3f} ms, mixed_gemm_mx call {gemm_x * 1e6:.1f} us")
 
     work = algorithmic_work(w)
     stage_out = {}
-    for name, fn in stages:
+    for name, fn in stages + [("mixed_gemm_mx", stage_fns(mx, w, variant=True)[5][1])]:
         t = time_stage(torch, fn, args.stage_reps)
+        wk = work["mixed_gemm" if name == "mixed_gemm_mx" else name]
         d = dict(ms=t * 1e3)
-        if "bytes" in work[name]:
-            d["GBps"] = work[name]["bytes"] / t / 1e9
-            d["hbm_frac"] = work[name]["bytes"] / t / HBM_PEAK
-        if "ops" in work[name]:
-            d["TOPS"] = work[name]["ops"] / t / 1e12
-            d["fp6_mfma_frac"] = work[name]["ops"] / t / FP6_PEAK
-            d["int8_mfma_frac"] = work[name]["ops"] / t / INT8_PEAK
+        if "bytes" in wk:
+            d["GBps"] = wk["bytes"] / t / 1e9
+            d["hbm_frac"] = wk["bytes"] / t / HBM_PEAK
+        if "ops" in wk:
+            d["TOPS"] = wk["ops"] / t / 1e12
+            d["int8_mfma_frac"] = wk["ops"] / t / INT8_PEAK
+            if name == "mixed_gemm_mx":
+                d["fp6_mfma_frac"] = wk["ops"] / t / FP6_PEAK
         stage_out[name] = d
         log(name, json.dumps(d))
 
@@ -297,12 +314,17 @@ def main():
     M, N, K = w["M"], w["N"], w["K"]
     ops = 2 * M * N * K
     achieved = ops / gemm_call_s / 1e12
-    roofline = dict(bound="mfma", achieved=achieved, peak=FP6_PEAK / 1e12, unit="TFLOP/s",
-                    frac=achieved * 1e12 / FP6_PEAK, traffic=measured_traffic(),
-                    kernel="mixed_gemm call: k_mx_prep + k_gemm_mx (fp6 E2M3 block-scaled MFMA)",
+    roofline = dict(bound="mfma", achieved=achieved, peak=INT8_PEAK / 1e12, unit="TOP/s",
+                    frac=achieved * 1e12 / INT8_PEAK, traffic=measured_traffic(),
+                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_dma (int8 MFMA)",
                     algorithmic_ops_per_launch=ops, launch_us=gemm_call_s * 1e6,
-                    int8_peak_frac=achieved * 1e12 / INT8_PEAK,
                     algorithmic_bytes_per_launch=work["mixed_gemm"]["bytes"])
+    ach_x = ops / gemm_x / 1e12
+    variant = {"entry": "mxs_mixed_gemm_mx (prefill on the block-scaled fp6 MFMA: k_mx_prep + k_gemm_mx)",
+               "value": ops / step_x / 1e12, "ms_per_step": step_x * 1e3, "launch_us": gemm_x * 1e6,
+               "achieved": ach_x, "unit": "TFLOP/s", "peak": FP6_PEAK / 1e12,
+               "frac": ach_x * 1e12 / FP6_PEAK, "int8_peak_frac": ach_x * 1e12 / INT8_PEAK,
+               "traffic": measured_traffic("traffic_bytes_per_call_mx")}
     qx = stage_out["quantize_x"]
     out = {
         "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
@@ -315,7 +337,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp6",
+        "dtype": "int8",
         "data": "synthetic (seeded outlier-channel activations, Student-t weights, bf16)",
         "config": {"workload": "Llama-3-8B q_proj prefill layer: calibrate 8x2048 tokens, score/allocate/"
                                "quantize W 4096x4096, quantize X 2048x4096, mixed GEMM 2048x4096x4096 "
@@ -326,6 +348,7 @@ def main():
                           "kv": stage_out["quantize_kv"]["GBps"]},
         "stages": stage_out,
         "roofline": roofline,
+        "variant_mx": variant,
     }
     if not args.no_cpu:
         log("cpu baseline (oracle)")

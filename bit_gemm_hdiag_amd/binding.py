@@ -59,6 +59,8 @@ def _load():
         "mxs_quantize": (S, [P, c_int32, c_int64, P, POINTER(_QMat), P]),
         "mxs_mixed_gemm_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
         "mxs_mixed_gemm": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
+        "mxs_mixed_gemm_mx_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
+        "mxs_mixed_gemm_mx": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
         "mxs_quantize_kv": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -71,7 +73,7 @@ _lib = _load()
 EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_blocks",
             "mxs_calibrate_workspace", "mxs_score_workspace", "mxs_calibrate", "mxs_score",
             "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
-            "mxs_quantize_kv")
+            "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv")
 
 
 def _check(status: int, where: str):
@@ -240,8 +242,7 @@ def mxs_mixed_gemm_workspace(A: QMat, W: QMat) -> int:
     return int(_lib.mxs_mixed_gemm_workspace(ctypes.byref(a), ctypes.byref(w)))
 
 
-def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
-    """Y [M, N] fp32 = Qa(X) Qw(W)^T with per-block MX scales."""
+def _gemm(fn, wsfn, name, A: QMat, W: QMat, Y, ws) -> torch.Tensor:
     dev = A.sc.device
     if Y is None:
         Y = torch.empty((A.rows, W.rows), dtype=torch.float32, device=dev)
@@ -249,10 +250,24 @@ def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> 
         raise TypeError("Y must be fp32")
     py, ldy = _dev2d(Y, "Y")
     a, w = A.c_struct(), W.c_struct()
-    p, n = _workspace(int(_lib.mxs_mixed_gemm_workspace(ctypes.byref(a), ctypes.byref(w))), dev, ws)
-    _check(_lib.mxs_mixed_gemm(ctypes.byref(a), ctypes.byref(w), py, ldy, p, n, _stream(dev)),
-           "mxs_mixed_gemm")
+    p, n = _workspace(int(wsfn(ctypes.byref(a), ctypes.byref(w))), dev, ws)
+    _check(fn(ctypes.byref(a), ctypes.byref(w), py, ldy, p, n, _stream(dev)), name)
     return Y
+
+
+def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """Y [M, N] fp32 = Qa(X) Qw(W)^T with per-block MX scales."""
+    return _gemm(_lib.mxs_mixed_gemm, _lib.mxs_mixed_gemm_workspace, "mxs_mixed_gemm", A, W, Y, ws)
+
+
+def mxs_mixed_gemm_mx_workspace(A: QMat, W: QMat) -> int:
+    a, w = A.c_struct(), W.c_struct()
+    return int(_lib.mxs_mixed_gemm_mx_workspace(ctypes.byref(a), ctypes.byref(w)))
+
+
+def mxs_mixed_gemm_mx(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """The same product, prefill on the block-scaled fp6 matrix cores."""
+    return _gemm(_lib.mxs_mixed_gemm_mx, _lib.mxs_mixed_gemm_mx_workspace, "mxs_mixed_gemm_mx", A, W, Y, ws)
 
 
 def mxs_quantize_kv(kv: torch.Tensor, codes=None, scales=None):

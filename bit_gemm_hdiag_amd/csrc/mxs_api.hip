@@ -152,26 +152,47 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W) {
     return mxs::gemm_workspace(*A, *W);
 }
 
-mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy, void *ws,
-                          size_t ws_bytes, hipStream_t stream) {
+// Argument checks shared by both GEMM entry points.
+static mxs_status check_gemm(const mxs_qmat *A, const mxs_qmat *W, const float *Y, int64_t ldy, const void *ws,
+                             size_t ws_bytes, size_t need, const char *name) {
     mxs_status s = check_qmat(A, "A");
     if (s != MXS_OK) return s;
     if ((s = check_qmat(W, "W")) != MXS_OK) return s;
     if (A->K != W->K || A->n8 != W->n8 || A->n6 != W->n6 || A->n4 != W->n4)
-        return fail(MXS_ERR_SHAPE, "mixed_gemm: A and W differ in K or block counts");
-    if (ldy < W->rows || (!Y && A->rows > 0 && W->rows > 0)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "mixed_gemm: Y NULL or ldy < N");
+        return fail(MXS_ERR_SHAPE, "%s: A and W differ in K or block counts", name);
+    if (ldy < W->rows || (!Y && A->rows > 0 && W->rows > 0)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: Y NULL or ldy < N", name);
     // operand loads are 16/4/8-byte vector loads per row
     const mxs_qmat *q[2] = {A, W};
     for (const mxs_qmat *m : q) {
         if ((m->n8 && (!aligned(m->q8, 16) || m->ld8 % 16)) || (m->n6 && (!aligned(m->q6, 4) || m->ld6 % 4)) ||
             (m->n4 && (!aligned(m->q4, 8) || m->ld4 % 8)))
-            return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm: planes need q8/ld8 16-byte, q6/ld6 4-byte and q4/ld4 8-byte alignment");
+            return fail(MXS_ERR_UNSUPPORTED, "%s: planes need q8/ld8 16-byte, q6/ld6 4-byte and q4/ld4 8-byte alignment", name);
     }
-    if (A->rows > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm: more than 4194304 rows in A");
-    const size_t need = mxs::gemm_workspace(*A, *W);
+    if (A->rows > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "%s: more than 4194304 rows in A", name);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
-        return fail(MXS_ERR_WORKSPACE, "mixed_gemm: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+        return fail(MXS_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", name, need, ws ? ws_bytes : 0);
+    return MXS_OK;
+}
+
+mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    const size_t need = A && W ? mxs::gemm_workspace(*A, *W) : 0;
+    const mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm");
+    if (s != MXS_OK) return s;
     return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm");
+}
+
+size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W) {
+    if (!A || !W) return 0;
+    return mxs::gemm_workspace_mx(*A, *W);
+}
+
+mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    const size_t need = A && W ? mxs::gemm_workspace_mx(*A, *W) : 0;
+    const mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm_mx");
+    if (s != MXS_OK) return s;
+    return device_status(mxs::launch_mixed_gemm_mx(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm_mx");
 }
 
 mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H, int64_t D,

@@ -7,14 +7,19 @@
 // with no dequantisation pass. A (tokens) and W (weights) share the channel
 // permutation, so block b of both operands has the same width m.
 //
-// The one dense contraction of the method runs on the matrix cores. Up to 32
-// tokens (decode) it is bound by streaming W and uses int8 MFMAs on the
-// codes (v_mfma_i32_32x32x32_i8 takes exactly one 32-deep MXINT block, so
-// each MFMA yields the exact integer block sums I_b of a 32x32 output tile;
-// codes enter as bytes: 8-bit as is, 6-bit times 4, 4-bit times 16, the
-// factor folded back into the block scale; every term I_b * 2^(sa+sw) is
-// exact in fp32). Prefill runs on the block-scaled micro-float MFMAs, which
-// apply the E8M0 scales in hardware (see the prefill section).
+// The one dense contraction of the method runs on the int8 matrix cores:
+// v_mfma_i32_32x32x32_i8 takes exactly one 32-deep MXINT block, so each MFMA
+// yields the exact integer block sums I_b of a 32x32 output tile. Codes enter
+// the MFMA as bytes: 8-bit codes as is, 6-bit codes times 4 and 4-bit codes
+// times 16 (the field lands in the top bits of the byte, which is a free sign
+// extension); the factor is folded back into the block scale. Every block
+// term I_b * 2^(sa+sw) is exact in fp32 (|I_b| < 2^24, power-of-two scale);
+// only the fp32 accumulation across blocks rounds. This is mxs_mixed_gemm.
+//
+// mxs_mixed_gemm_mx runs the same product's prefill (64 or more tokens) on
+// the block-scaled micro-float matrix cores instead, which apply the E8M0
+// scales in hardware (see the section "Prefill variant on the block-scaled
+// matrix cores"); below 64 tokens both use the kernels of mxs_mixed_gemm.
 //
 // Layout of the 32x32x32 i8 MFMA on a 64-lane wavefront: lane l supplies row
 // (l mod 32) of A and column (l mod 32) of B, 16 bytes each from k-half
@@ -146,25 +151,235 @@ QView view_of(const mxs_qmat &q) {
 }
 
 // ---------------------------------------------------------------------------
-// Helpers of the prefill path below.
+// Prefill path (M >= kPrefillMinRows): operand preparation + grouped GEMM.
+//
+// The per-block epilogue above costs 3 VALU operations per output and block,
+// six times the MFMA time of the block. The prefill path removes it by exact
+// exponent alignment over groups = aligned windows of kG consecutive blocks.
+// If a window lies inside one width class and a row's nonzero blocks in it
+// have scale exponents within F of each other (F = 4, 2, 0 for 4-, 6-, 8-bit
+// codes: the headroom an int8 byte has over the code), code c of block b is
+// stored as c << (s_b - base) with base = max s_b - F; aligned A and W rows
+// make the int32 MFMA sum over the window exact, times 2^(base_a + base_w):
+// one epilogue per window. Other rows keep c << F with scale 2^(s_b - F) and
+// the wave takes one epilogue per block for that window. Window sums stay
+// below 2^24 (16 * 32 * 127^2), so the int32 -> fp32 conversion is exact and
+// only the fp32 accumulation across windows rounds.
+//
+// Prepared operand (workspace), per matrix with R rows padded to Rp and K
+// padded to Kp = whole windows:
+//   codes int8 [Rp, Kp]   shifted codes, natural k order inside each block
+//   cs    f32  [nbp, Rp]  code scale of (row, block); negative when the
+//                         row's window is not aligned; -Inf for a NaN/Inf block
+// Padding rows and blocks hold zero codes and scale +1.
+constexpr int kG = 16;              // blocks per alignment window
 constexpr int kPrefillMinRows = 64; // smaller M uses the per-block kernel
+
+__device__ __forceinline__ int sext(uint32_t v, int bits) {
+    return (int)(v << (32 - bits)) >> (32 - bits);
+}
+
+// codes c[0..31] of block `b` (global block index) of row r
+__device__ __forceinline__ void unpack_block(const QView &Q, int64_t r, int64_t b, int cls,
+                                             int32_t n8, int32_t n6, int c[32]) {
+    if (cls == 8) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(Q.q8 + r * Q.ld8 + 32 * b);
+        const uint4 x = p[0], y = p[1];
+        const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 2] >> (8 * (i & 3))) & 255u, 8);
+    } else if (cls == 6) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(Q.q6 + r * Q.ld6 + 24 * (b - n8));
+        uint32_t w[7];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) w[i] = p[i];
+        w[6] = 0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            // 24-bit group g starts at bit 24 g of the 192-bit little-endian stream
+            const int bit = 24 * g;
+            const uint32_t grp = __builtin_amdgcn_alignbit(w[(bit >> 5) + 1], w[bit >> 5], bit & 31);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[4 * g + j] = sext((grp >> (6 * j)) & 63u, 6);
+        }
+    } else {
+        const uint2 *p = reinterpret_cast<const uint2 *>(Q.q4 + r * Q.ld4 + 16 * (b - n8 - n6));
+        const uint2 x = p[0], y = p[1];
+        const uint32_t w[4] = {x.x, x.y, y.x, y.y};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 3] >> (4 * (i & 7))) & 15u, 4);
+    }
+}
+
+// One workgroup prepares a 64-row x 16-block window of one matrix: thread t
+// takes block t % 16 of rows t / 16 + 16 i (reads and code writes run along
+// the row), the window reduction is a 16-lane butterfly, and the scales are
+// transposed through LDS so that they are written 64 rows at a time.
+struct PrepJob {
+    QView Q;
+    int64_t R, Rp;
+    int8_t *codes;
+    float *cs;
+    int64_t tiles_r;      // Rp / 64
+};
+
+// Windows start at the first block of each width class: window j of class
+// segment [lo, hi) covers blocks lo + kG j .. min(hi, lo + kG (j + 1)) - 1.
+struct Segs {
+    int32_t lo[3], hi[3], F[3], cls[3];
+    int32_t win_base[4];   // prefix count of windows per segment
+};
+
+__host__ __device__ inline Segs make_segs(int32_t n8, int32_t n6, int32_t n4) {
+    Segs S;
+    const int32_t n[3] = {n8, n6, n4};
+    int32_t lo = 0, wb = 0;
+    for (int i = 0; i < 3; ++i) {
+        S.lo[i] = lo;
+        S.hi[i] = lo + n[i];
+        S.F[i] = i == 0 ? 0 : (i == 1 ? 2 : 4);
+        S.cls[i] = i == 0 ? 8 : (i == 1 ? 6 : 4);
+        S.win_base[i] = wb;
+        wb += (n[i] + kG - 1) / kG;
+        lo += n[i];
+    }
+    S.win_base[3] = wb;
+    return S;
+}
+
+// One workgroup prepares a 64-row x (one window) tile of one matrix: thread t
+// takes block t % 16 of the window for rows t / 16 + 16 i (reads and code
+// writes run along the row), the window reduction is a 16-lane butterfly, and
+// the scales are transposed through LDS to be written 64 rows at a time.
+// Prepared rows are padded to a multiple of 16 blocks with zero codes.
+__global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64_t ntiles_a, int64_t K,
+                                                   int64_t Kp, Segs S) {
+    __shared__ float s_cs[kG][64];
+    const bool is_a = blockIdx.x < ntiles_a;
+    const PrepJob &J = is_a ? ja : jw;
+    const int64_t tile = is_a ? blockIdx.x : blockIdx.x - ntiles_a;
+    const int64_t rt = tile % J.tiles_r, win = tile / J.tiles_r;   // win < windows + pad windows
+    const int tid = threadIdx.x, blk = tid & 15;
+    const int64_t nb = K / 32, nbp = Kp / 32;
+    int sg = 0;
+    int64_t b;
+    bool real_blk;
+    if (win < S.win_base[3]) {
+        sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : 2);
+        b = S.lo[sg] + (win - S.win_base[sg]) * kG + blk;
+        real_blk = b < S.hi[sg];
+    } else {   // padding blocks nb .. nbp - 1, 16 per pad window
+        b = nb + (win - S.win_base[3]) * kG + blk;
+        real_blk = false;
+    }
+    const int cls = S.cls[sg], F = S.F[sg];
+    const bool in_range = b < nbp;
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+        const int lr = (tid >> 4) + 16 * i;
+        const int64_t r = rt * 64 + lr;
+        const bool real = real_blk && r < J.R;
+        int c[32];
+        int s = 0;
+        bool bad = false, nz = false;
+        if (real) {
+            unpack_block(J.Q, r, b, cls, S.hi[0], S.hi[1] - S.hi[0], c);
+            const uint32_t byte = J.Q.sc[r * J.Q.lds + b];
+            bad = byte == 0xFFu;
+            s = (int)byte - 127;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) nz |= c[k] != 0;
+            if (bad) nz = false;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) c[k] = 0;
+        }
+        int smax = nz ? s : -100000, smin = nz ? s : 100000, anybad = bad;
+#pragma unroll
+        for (int off = 1; off < kG; off <<= 1) {
+            smax = max(smax, __shfl_xor(smax, off));
+            smin = min(smin, __shfl_xor(smin, off));
+            anybad |= __shfl_xor(anybad, off);
+        }
+        const bool allzero = smax == -100000;
+        const bool aligned = !anybad && (allzero || smax - smin <= F);
+        const int base = allzero ? 0 : smax - F;
+        const int shift = aligned ? (nz ? s - base : 0) : F;
+        float scale;
+        if (!real) scale = 1.0f;
+        else if (bad) scale = -__builtin_inff();
+        else scale = aligned ? __builtin_ldexpf(1.0f, base) : -__builtin_ldexpf(1.0f, s - F);
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v |= (((uint32_t)c[4 * k + j] << shift) & 255u) << (8 * j);
+            w[k] = v;
+        }
+        if (in_range && (real_blk || b >= nb)) {
+            uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * b);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+        s_cs[blk][lr] = scale;
+    }
+    __syncthreads();
+    {
+        const int bb = tid >> 4, part = tid & 15;
+        const int64_t ob = b - blk + bb;   // block of this transposed slice
+        const bool ok = win < S.win_base[3] ? ob < S.hi[sg] : ob < nbp;
+        if (ok) {
+            const float4 v = *reinterpret_cast<const float4 *>(&s_cs[bb][4 * part]);
+            *reinterpret_cast<float4 *>(J.cs + ob * J.Rp + rt * 64 + 4 * part) = v;
+        }
+    }
+}
+
+// Grouped int8 GEMM over prepared operands.
+//
+// Workgroup: 8 waves (4 x 2), tile 256 (A rows) x 128 (W rows); each wave
+// owns 64 x 64 outputs as 2 x 2 MFMA tiles (64 int32 + 64 fp32 accumulators
+// per lane, two waves per SIMD). Operands move from global memory straight
+// into LDS (global_load_lds_dwordx4), so no registers hold data in flight
+// and four stages can be in flight at once. (A version that staged through
+// registers one stage ahead ran 4-5 % slower at the q_proj and MLP shapes.)
+//
+// Stage = kDSB = 2 blocks (64 bytes of every row) plus their scales, 27 KiB;
+// a ring of five stage slots. Iteration s: wait for this wave's loads of
+// stage s (the loads of stages s+1 .. s+3 stay in flight), barrier (every
+// wave's loads of stage s have landed and every wave is done with stage
+// s-1), issue stage s+4 into the slot of stage s-1, compute s.
+// A DMA instruction writes 64 consecutive 16-byte LDS slots, lane by lane;
+// lanes pick their global chunk so that row r keeps chunk c at slot
+// c ^ ((r >> 2) & 3) of its 64 bytes: the 16 lanes of one LDS read pass
+// (16 consecutive rows, same chunk) then hit 16 distinct 16-byte bank groups.
+constexpr int kGBM = 256, kGBN = 128;        // workgroup tile
+constexpr int kDSB = 2;                      // blocks per stage
+constexpr int kDRow = kDSB * 32;             // 64 bytes per row per stage
+constexpr int kDStA = kGBM * kDRow;          // 16 KiB
+constexpr int kDStW = kGBN * kDRow;          //  8 KiB
+constexpr int kDStCA = kDSB * kGBM * 4;      //  2 KiB
+constexpr int kDStCW = kDSB * kGBN * 4;      //  1 KiB
+constexpr int kDSlot = kDStA + kDStW + kDStCA + kDStCW;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediate that waits until at most n vector memory loads are
-// outstanding (expcnt and lgkmcnt left at their maxima)
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+__shared__ __attribute__((aligned(16))) int8_t g_dslot0[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot1[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot2[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot3[kDSlot];
+__shared__ __attribute__((aligned(16))) int8_t g_dslot4[kDSlot];
+
+template <int SL>
+__device__ __forceinline__ int8_t *dslot() {
+    return SL == 0 ? g_dslot0 : (SL == 1 ? g_dslot1 : (SL == 2 ? g_dslot2 : (SL == 3 ? g_dslot3 : g_dslot4)));
+}
 
 // LDS byte address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
 }
-
-// loads from an LDS byte address
-typedef __attribute__((address_space(3))) const v4i lds_v4i_t;
-__device__ __forceinline__ v4i lds_v4(uint32_t a) { return *reinterpret_cast<lds_v4i_t *>((uintptr_t)a); }
-typedef __attribute__((address_space(3))) const int lds_i32_t;
-__device__ __forceinline__ int lds_i32(uint32_t a) { return *reinterpret_cast<lds_i32_t *>((uintptr_t)a); }
 
 // One 16-byte-per-lane DMA into LDS at lds + 16 * lane. Issued from inline
 // assembly so that the compiler does not order the slot reads behind every
@@ -178,8 +393,220 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
                  : "memory", "m0");
 }
 
+struct DmaLanes {
+    const int8_t *a0, *a1, *w;   // this lane's global chunk addresses at stage 0
+    const float *c;              // scales (waves 0..2)
+    int64_t cstep;               // scale address step per stage
+    int oa0, oa1, ow, oc;        // wave-uniform LDS offsets inside a slot
+};
+
+template <int SL>
+__device__ __forceinline__ void dma_issue(const DmaLanes &D, int st, int nstage, bool has_c) {
+    const int s = st < nstage ? st : nstage - 1;      // past the end: reload the last stage
+    const uint32_t slot = lds_addr(dslot<SL>());
+    const int64_t kb = (int64_t)s * kDRow;
+    dma16(D.a0 + kb, slot + D.oa0);
+    dma16(D.a1 + kb, slot + D.oa1);
+    dma16(D.w + kb, slot + D.ow);
+    if (has_c) dma16(D.c + s * D.cstep, slot + D.oc);
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm_dma(
+    const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
+    const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
+    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+
+    // tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
+    // takes a contiguous run of tiles; runs sweep groups of 8 row-tiles
+    const int64_t tilesM = Mp / kGBM, tilesN = Np / kGBN, ntiles = tilesM * tilesN;
+    int64_t t = blockIdx.x;
+    if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+    const int64_t per_group = 8 * tilesN;
+    const int64_t gid = t / per_group, first_m = gid * 8;
+    const int64_t gsz = tilesM - first_m < 8 ? tilesM - first_m : 8;
+    const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
+    const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
+    const int nstage = (nb + kDSB - 1) / kDSB;
+    const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
+
+    // DMA roles: A rows 32 wave .. +31 (two instructions of 16 rows), W rows
+    // 16 wave .. +15; waves 0, 1: A scales of block 0 / 1; wave 2: W scales
+    DmaLanes D;
+    {
+        const int rsub = lane >> 2, sl = lane & 3;
+        const int ra0 = 32 * wave + rsub, ra1 = ra0 + 16, rw = 16 * wave + rsub;
+        D.a0 = Aq + (m0 + ra0) * Kp + ((sl ^ ((ra0 >> 2) & 3)) << 4);
+        D.a1 = Aq + (m0 + ra1) * Kp + ((sl ^ ((ra1 >> 2) & 3)) << 4);
+        D.w = Wq + (n0 + rw) * Kp + ((sl ^ ((rw >> 2) & 3)) << 4);
+        D.oa0 = 32 * wave * kDRow;
+        D.oa1 = D.oa0 + 16 * kDRow;
+        D.ow = kDStA + 16 * wave * kDRow;
+        if (wave < 2) {
+            D.c = csA + (int64_t)wave * Mp + m0 + 4 * lane;
+            D.cstep = kDSB * Mp;
+            D.oc = kDStA + kDStW + wave * (kGBM * 4);
+        } else {
+            D.c = csW + (int64_t)(lane >> 5) * Np + n0 + 4 * (lane & 31);
+            D.cstep = kDSB * Np;
+            D.oc = kDStA + kDStW + kDStCA;
+        }
+    }
+    const bool has_c = wave < 3;
+
+    // LDS offset of this lane's fragment of block blk: fb ^ (blk << 5)
+    int fbA[2], fbW[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
+        fbA[i] = ra * kDRow + ((h ^ ((ra >> 2) & 3)) << 4);
+        fbW[i] = kDStA + rw * kDRow + ((h ^ ((rw >> 2) & 3)) << 4);
+    }
+
+    float acc[2][2][16];
+    v16i I[2][2];
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    // two zero B operands the compiler cannot see through, so the four
+    // restart MFMAs stay distinct and write the accumulators in place
+    v4i zb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        zb[j] = v4i{z, z, z, z};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            I[i][j] = zero;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        }
+
+    bool aligned = true;
+    auto compute = [&](int st, const int8_t *sbase) {
+        const float *sCA = reinterpret_cast<const float *>(sbase + kDStA + kDStW);
+        const float *sCW = sCA + kDSB * kGBM;
+        v4i fa[2], fw[2], na[2], nw[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            na[i] = *reinterpret_cast<const v4i *>(sbase + fbA[i]);
+            nw[i] = *reinterpret_cast<const v4i *>(sbase + fbW[i]);
+        }
+#pragma unroll
+        for (int blk = 0; blk < kDSB; ++blk) {
+            const int b = st * kDSB + blk;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) { fa[i] = na[i]; fw[i] = nw[i]; }
+            if (blk + 1 < kDSB) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    na[i] = *reinterpret_cast<const v4i *>(sbase + (fbA[i] ^ ((blk + 1) << 5)));
+                    nw[i] = *reinterpret_cast<const v4i *>(sbase + (fbW[i] ^ ((blk + 1) << 5)));
+                }
+            }
+            if (b >= nb) break;
+            const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
+            const int hi = b >= h1 ? nb : (b >= h0 ? h1 : h0);
+            const int off = b - lo;
+            const bool first = (off % kG) == 0;
+            const bool last = (off % kG) == kG - 1 || b == hi - 1;
+            if (first) {
+                const float va = sCA[blk * kGBM + wm * 64 + lane];
+                const float vw = sCW[blk * kGBN + wn * 64 + lane];
+                aligned = __all(va > 0.f && vw > 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fw[j], I[i][j], 0, 0, 0);
+            if (last || !aligned) {
+                float cw[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) cw[j] = __builtin_fabsf(sCW[blk * kGBN + wn * 64 + j * 32 + l32]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sCA + blk * kGBM + wm * 64 + i * 32 + 8 * q + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float sa = __builtin_fabsf(v[e]);
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                acc[i][j][4 * q + e] = __builtin_fmaf((float)I[i][j][4 * q + e], sa * cw[j], acc[i][j][4 * q + e]);
+                        }
+                    }
+                // restart the integer sums with a zero-product MFMA (C = 0):
+                // the matrix core has slack here, the vector ALU has none
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
+            }
+        }
+    };
+
+    // own loads of stage s done once at most two later stages are in flight
+#define MXS_DSTEP(s_, CUR, NXT)                                                               \
+    do {                                                                                      \
+        if ((s_) >= nstage) goto done;                                                        \
+        if (has_c) __builtin_amdgcn_s_waitcnt(0x0F70 | 12); /* vmcnt(12) */                   \
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | 9);        /* vmcnt(9) */                    \
+        lds_barrier();                                                                        \
+        dma_issue<NXT>(D, (s_) + 4, nstage, has_c);                                           \
+        compute((s_), dslot<CUR>());                                                          \
+    } while (0)
+
+    dma_issue<0>(D, 0, nstage, has_c);
+    dma_issue<1>(D, 1, nstage, has_c);
+    dma_issue<2>(D, 2, nstage, has_c);
+    dma_issue<3>(D, 3, nstage, has_c);
+    for (int s = 0; s < nstage; s += 5) {
+        MXS_DSTEP(s, 0, 4);
+        MXS_DSTEP(s + 1, 1, 0);
+        MXS_DSTEP(s + 2, 2, 1);
+        MXS_DSTEP(s + 3, 3, 2);
+        MXS_DSTEP(s + 4, 4, 3);
+    }
+done:
+#undef MXS_DSTEP
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 32 + l32;
+            if (col >= N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * q + 4 * h + r;
+                    if (row < M) Y[row * ldy + col] = acc[i][j][4 * q + r];
+                }
+        }
+}
+
 // ---------------------------------------------------------------------------
-// Prefill path on the block-scaled matrix cores.
+// Helpers of the block-scaled prefill variant below.
+// s_waitcnt immediate that waits until at most n vector memory loads are
+// outstanding (expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// loads from an LDS byte address
+typedef __attribute__((address_space(3))) const v4i lds_v4i_t;
+__device__ __forceinline__ v4i lds_v4(uint32_t a) { return *reinterpret_cast<lds_v4i_t *>((uintptr_t)a); }
+typedef __attribute__((address_space(3))) const int lds_i32_t;
+__device__ __forceinline__ int lds_i32(uint32_t a) { return *reinterpret_cast<lds_i32_t *>((uintptr_t)a); }
+
+// ---------------------------------------------------------------------------
+// Prefill variant on the block-scaled matrix cores (mxs_mixed_gemm_mx).
 //
 // gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 multiplies two 64-deep slabs of
 // OCP micro-float elements and applies one E8M0 scale per 32 elements of
@@ -1144,7 +1571,27 @@ GemvPlan gemv_plan(const mxs_qmat &A, const mxs_qmat &W) {
     return GemvPlan{(int32_t)ceil_div(nb, bps), bps};
 }
 
+struct PrepLayout {
+    int64_t Mp, Np, Kp;
+    size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
+};
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
+    PrepLayout L;
+    L.Mp = ceil_div(A.rows, kGBM) * kGBM;
+    L.Np = ceil_div(W.rows, kGBN) * kGBN;
+    L.Kp = ceil_div(A.K, 128) * 128;   // whole 4-block units (prep pads the tail)
+    const int64_t nbp = L.Kp / 32;
+    size_t off = 0;
+    L.a_codes = off; off = align256(off + (size_t)L.Mp * L.Kp);
+    L.w_codes = off; off = align256(off + (size_t)L.Np * L.Kp);
+    L.a_cs = off;    off = align256(off + (size_t)nbp * L.Mp * 4);
+    L.w_cs = off;    off = align256(off + (size_t)nbp * L.Np * 4);
+    L.total = off;
+    return L;
+}
 
 bool use_prefill(const mxs_qmat &A) { return A.rows >= kPrefillMinRows; }
 // The decode kernel addresses 64 W rows with 32-bit offsets, reads 4-bit
@@ -1253,17 +1700,38 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
     return hipGetLastError();
 }
 
+
+// Decode (up to 32 tokens) and 33..63 tokens take the same kernels in both
+// entry points; they differ in the prefill kernels only.
+size_t decode_workspace(const mxs_qmat &A, const mxs_qmat &W) {
+    const GemvPlan P = decode_plan(A, W);
+    const GemvPlan Q = gemv_plan(A, W);
+    const size_t a = P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+    const size_t b = Q.nslices > 1 ? (size_t)Q.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
+    return a > b ? a : b;
+}
+
+hipError_t launch_small(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
+    const int64_t M = A.rows, N = W.rows;
+    if (use_gemv(A, W)) return launch_gemv(A, W, Y, ldy, ws, st);
+    const dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
+    hipLaunchKernelGGL(k_gemm_blockwise, grid, dim3(256), 0, st, view_of(A), view_of(W), M, N, A.n8, A.n6, A.n4, Y,
+                       ldy);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
     if (W.rows == 0 || A.rows == 0) return 0;
-    if (use_gemv(A, W)) {
-        const GemvPlan P = decode_plan(A, W);
-        const GemvPlan Q = gemv_plan(A, W);
-        const size_t a = P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
-        const size_t b = Q.nslices > 1 ? (size_t)Q.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
-        return a > b ? a : b;
-    }
+    if (use_gemv(A, W)) return decode_workspace(A, W);
+    if (!use_prefill(A)) return 0;
+    return prep_layout(A, W).total;
+}
+
+size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W) {
+    if (W.rows == 0 || A.rows == 0) return 0;
+    if (use_gemv(A, W)) return decode_workspace(A, W);
     if (!use_prefill(A)) return 0;
     return mx_layout(A, W).total;
 }
@@ -1272,13 +1740,34 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
                              void *ws, size_t, hipStream_t st) {
     const int64_t M = A.rows, N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
-    if (use_gemv(A, W)) return launch_gemv(A, W, Y, ldy, ws, st);
-    if (!use_prefill(A)) {
-        const dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
-        hipLaunchKernelGGL(k_gemm_blockwise, grid, dim3(256), 0, st, view_of(A), view_of(W), M, N,
-                           A.n8, A.n6, A.n4, Y, ldy);
-        return hipGetLastError();
-    }
+    if (!use_prefill(A) || use_gemv(A, W)) return launch_small(A, W, Y, ldy, ws, st);
+    const PrepLayout L = prep_layout(A, W);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int8_t *ac = reinterpret_cast<int8_t *>(base + L.a_codes);
+    int8_t *wc = reinterpret_cast<int8_t *>(base + L.w_codes);
+    float *acs = reinterpret_cast<float *>(base + L.a_cs);
+    float *wcs = reinterpret_cast<float *>(base + L.w_cs);
+    const Segs S = make_segs(A.n8, A.n6, A.n4);
+    const int64_t nb = A.K / 32, nbp = L.Kp / 32;
+    const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
+    PrepJob ja{view_of(A), M, L.Mp, ac, acs, L.Mp / 64};
+    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
+    const int64_t ta = ja.tiles_r * windows, tw = jw.tiles_r * windows;
+    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
+    hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
+                                void *ws, size_t, hipStream_t st) {
+    const int64_t M = A.rows, N = W.rows;
+    if (M == 0 || N == 0) return hipSuccess;
+    if (!use_prefill(A) || use_gemv(A, W)) return launch_small(A, W, Y, ldy, ws, st);
     return launch_mx(A, W, Y, ldy, ws, st);
 }
 

@@ -30,9 +30,13 @@ hipError_t launch_allocate(const double *score, int64_t K, int32_t c8, int32_t c
 hipError_t launch_quantize(const void *X, mxs_dtype dt, int64_t ldx, const int32_t *perm,
                            const mxs_qmat &out, hipStream_t st);
 
-// mixed GEMM (mxs_gemm.hip)
+// mixed GEMM (mxs_gemm.hip): int8 block sums with fp32 scale epilogues, and
+// the variant on the block-scaled fp6 matrix cores (prefill kernels only)
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W);
 hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
                              void *ws, size_t ws_bytes, hipStream_t st);
+size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W);
+hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
+                                void *ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace mxs

@@ -196,10 +196,30 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W);
  * sum |A||W|). Y: [M, ldy] fp32 device output, ldy >= N.
  * ws: >= mxs_mixed_gemm_workspace(A, W) bytes (NULL if that is 0).
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K or block counts differ, ldy < N),
- * MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ * MXS_ERR_UNSUPPORTED (plane pointers or strides not 16/4/8-byte aligned
+ * for q8/q6/q4, more than 4194304 rows in A), MXS_ERR_WORKSPACE,
+ * MXS_ERR_DEVICE.
  */
 mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by mxs_mixed_gemm_mx for these shapes (may be 0). */
+size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W);
+
+/*
+ * The same product as mxs_mixed_gemm, with the prefill kernels (64 or more
+ * rows in A) on the block-scaled micro-float matrix cores, which apply one
+ * E8M0 scale per 32 elements of every row and column inside the instruction
+ * (the MX format's shared block scale, [NL] §1). Codes are re-encoded exactly
+ * as fp6 E2M3 elements (a 4-bit code as one element, a 6- or 8-bit code as
+ * two digits whose weight goes into the scale byte); every product and each
+ * 64-element partial sum is exact, only the fp32 accumulation rounds (once
+ * per instruction). Up to 63 rows it runs the kernels of mxs_mixed_gemm.
+ * Arguments, layout, ownership, stream semantics and errors as for
+ * mxs_mixed_gemm, with ws >= mxs_mixed_gemm_mx_workspace(A, W) bytes.
+ */
+mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * KV-cache quantisation (W4A4KV4, [NL] §4 and [REV] "Validation": keys and

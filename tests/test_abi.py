@@ -133,14 +133,21 @@ def test_quantize_and_gemm_errors(lib):
     assert q(FAKE, 0, 64, None, ctypes.byref(qm(ld6=10)), None) == -2         # ld6 < 24 n6
     assert q(FAKE, 0, 64, None, ctypes.byref(qm(q4=None)), None) == -1        # missing plane
     assert q(FAKE, 0, 64, None, None, None) == -1
-    g = lib.mxs_mixed_gemm
-    g.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_size_t, P]
-    A, W = qm(rows=8), qm(rows=16, n6=0, n4=2)
-    assert g(ctypes.byref(A), ctypes.byref(W), FAKE, 16, None, 0, None) == -2  # block counts differ
-    W2 = qm(rows=16)
-    assert g(ctypes.byref(A), ctypes.byref(W2), FAKE, 8, None, 0, None) == -2  # ldy < N
-    A3 = qm(rows=8, q4=0x20004)                                                 # misaligned 4-bit plane
-    assert g(ctypes.byref(A3), ctypes.byref(W2), FAKE, 16, None, 0, None) == -6
+    for g in (lib.mxs_mixed_gemm, lib.mxs_mixed_gemm_mx):
+        g.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_size_t, P]
+        A, W = qm(rows=8), qm(rows=16, n6=0, n4=2)
+        assert g(ctypes.byref(A), ctypes.byref(W), FAKE, 16, None, 0, None) == -2  # block counts differ
+        W2 = qm(rows=16)
+        assert g(ctypes.byref(A), ctypes.byref(W2), FAKE, 8, None, 0, None) == -2  # ldy < N
+        A3 = qm(rows=8, q4=0x20004)                                                 # misaligned 4-bit plane
+        assert g(ctypes.byref(A3), ctypes.byref(W2), FAKE, 16, None, 0, None) == -6
+        A4 = qm(rows=128)                                                           # prefill needs a workspace
+        assert g(ctypes.byref(A4), ctypes.byref(W2), FAKE, 16, None, 0, None) == -4
+    for wsf in (lib.mxs_mixed_gemm_workspace, lib.mxs_mixed_gemm_mx_workspace):
+        wsf.argtypes = [P, P]
+        wsf.restype = ctypes.c_size_t
+        assert wsf(ctypes.byref(qm(rows=128)), ctypes.byref(qm(rows=16))) > 0
+        assert wsf(ctypes.byref(qm(rows=0)), ctypes.byref(qm(rows=16))) == 0
     kv = lib.mxs_quantize_kv
     kv.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
     assert kv(FAKE, 1, 4, 8, 100, FAKE, FAKE, None) == -2

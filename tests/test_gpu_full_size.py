@@ -43,7 +43,11 @@ def check_gemm(Y, Yref, Yabs, what):
     assert ok.all(), f"{what}: {int((~ok).sum())} outputs off"
 
 
-def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12, n_sample_cols=48):
+GEMMS = ["mxs_mixed_gemm", "mxs_mixed_gemm_mx"]
+
+
+def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12, n_sample_cols=48,
+                   entry="mxs_mixed_gemm"):
     """calibrate -> score -> allocate -> quantize W and X -> mixed GEMM, each against the oracle."""
     gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
     Xc = synth.activations(calib_rows, K, seed + synth.ROLE_CALIB, gains, device=DEV)
@@ -70,7 +74,7 @@ def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12,
 
     X = synth.activations(M, K, seed + synth.ROLE_X, gains, device=DEV)
     A = mx.mxs_quantize(X, perm, n8, n6, n4)
-    Y = mx.mxs_mixed_gemm(A, B).cpu().numpy().astype(np.float64)
+    Y = getattr(mx, entry)(A, B).cpu().numpy().astype(np.float64)
     g = torch.Generator(device="cpu").manual_seed(seed)
     rows = np.unique(np.concatenate([[0, M - 1], torch.randint(0, M, (n_sample_rows,), generator=g).numpy()]))
     cols = np.unique(np.concatenate([[0, N - 1], torch.randint(0, N, (n_sample_cols,), generator=g).numpy()]))
@@ -85,16 +89,18 @@ def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12,
 # Llama-3-8B MLP, 4096 tokens: gate/up 14336 x 4096 at 3/10/87 %, down
 # 4096 x 14336 at 8/20/72 %; calibration over 8 x 2048 tokens
 @pytest.mark.parametrize("N,K,budget", [(14336, 4096, (300, 1000)), (4096, 14336, (800, 2000))])
-def test_mlp_layer_full_size(mx, orc, N, K, budget):
-    layer_pipeline(mx, orc, 4096, N, K, budget, 8 * 2048, seed=3000 + K)
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mlp_layer_full_size(mx, orc, N, K, budget, entry):
+    layer_pipeline(mx, orc, 4096, N, K, budget, 8 * 2048, seed=3000 + K, entry=entry)
 
 
 # Llama-2-70B layer shapes at 2048 prefill tokens, 5/15/80 %: k_proj (1024 x
 # 8192) and down_proj (8192 x 28672); calibration here over 2048 tokens (the
 # full 128 x 2048-token calibration volume is checked below on a column slice)
 @pytest.mark.parametrize("N,K", [(1024, 8192), (8192, 28672)])
-def test_70b_layer_full_size(mx, orc, N, K):
-    layer_pipeline(mx, orc, 2048, N, K, (500, 1500), 2048, seed=5000 + N)
+@pytest.mark.parametrize("entry", GEMMS)
+def test_70b_layer_full_size(mx, orc, N, K, entry):
+    layer_pipeline(mx, orc, 2048, N, K, (500, 1500), 2048, seed=5000 + N, entry=entry)
 
 
 def test_70b_calibration_volume_column_slice(mx, orc):

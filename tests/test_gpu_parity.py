@@ -187,13 +187,18 @@ def test_allocate(mx, orc, K, budget):
 
 
 # ----------------------------------------------------------------------- GEMM
-def gemm_case(mx, orc, M, N, K, budget, seed, dtype=torch.bfloat16, sample_rows=None):
+# both entry points: int8 block sums with fp32 epilogues, and the variant on
+# the block-scaled fp6 matrix cores (prefill kernels only)
+GEMMS = ["mxs_mixed_gemm", "mxs_mixed_gemm_mx"]
+
+
+def gemm_case(mx, orc, M, N, K, budget, seed, dtype=torch.bfloat16, sample_rows=None, entry="mxs_mixed_gemm"):
     Xc, X, W = layer(K, N, M, 512, seed, dtype)
     n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
     perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(DEV)
     A = mx.mxs_quantize(X, perm, n8, n6, n4)
     B = mx.mxs_quantize(W, perm, n8, n6, n4)
-    Y = mx.mxs_mixed_gemm(A, B)
+    Y = getattr(mx, entry)(A, B)
     rows = np.arange(M) if sample_rows is None else sample_rows
     A_ref = orc.quantize(host(X[torch.as_tensor(rows, device=DEV)]), perm.cpu().numpy(), n8, n6, n4)
     B_ref = orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4)
@@ -206,14 +211,18 @@ def gemm_case(mx, orc, M, N, K, budget, seed, dtype=torch.bfloat16, sample_rows=
                                           (1, 300, 8192, (500, 1500)), (8, 130, 8192, (500, 1500)),
                                           (32, 96, 8192, (500, 1500)), (130, 64, 4096, (300, 1000)),
                                           (129, 257, 14336, (800, 2000)), (40, 50, 96, (0, 0)),
-                                          (33, 65, 512, (10000, 0)), (33, 65, 512, (0, 10000))])
-def test_mixed_gemm(mx, orc, M, N, K, budget):
-    gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N)
+                                          (33, 65, 512, (10000, 0)), (33, 65, 512, (0, 10000)),
+                                          (300, 130, 480, (3100, 4000)), (100, 70, 352, (0, 0)),
+                                          (70, 64, 288, (10000, 0)), (66, 129, 224, (0, 10000))])
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm(mx, orc, M, N, K, budget, entry):
+    gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N, entry=entry)
 
 
 @pytest.mark.parametrize("M,N,K,budget", [(200, 300, 1024, (500, 1500)), (64, 128, 8192, (300, 1000)),
                                           (3, 300, 1024, (500, 1500)), (20, 77, 4096, (300, 1000))])
-def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget, entry):
     # per-block scales spread over +-2^12 so that many (row, group) pairs cannot
     # share one exponent: exercises the per-block path next to aligned groups
     g = torch.Generator(device="cpu").manual_seed(M + N)
@@ -226,7 +235,7 @@ def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
     perm = torch.randperm(K, generator=g).to(torch.int32).to(DEV)
     A = mx.mxs_quantize(X, perm, n8, n6, n4)
     B = mx.mxs_quantize(W, perm, n8, n6, n4)
-    Y = mx.mxs_mixed_gemm(A, B).cpu().numpy().astype(np.float64)
+    Y = getattr(mx, entry)(A, B).cpu().numpy().astype(np.float64)
     Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), perm.cpu().numpy(), n8, n6, n4),
                                 orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4))
     nan_ref = np.isnan(Yref)
@@ -234,14 +243,16 @@ def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget):
     assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), "spread")
 
 
-def test_mixed_gemm_fp32_tiny_layer(mx, orc):
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_fp32_tiny_layer(mx, orc, entry):
     cfg = synth.CONFIGS[1]
-    gemm_case(mx, orc, cfg["M"], cfg["N"], cfg["K"], cfg["budget"], seed=1000, dtype=torch.float32)
+    gemm_case(mx, orc, cfg["M"], cfg["N"], cfg["K"], cfg["budget"], seed=1000, dtype=torch.float32, entry=entry)
 
 
-def test_mixed_gemm_q_proj_full_size_sampled(mx, orc):
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_q_proj_full_size_sampled(mx, orc, entry):
     rows = np.array([0, 1, 2, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
-    gemm_case(mx, orc, 2048, 4096, 4096, (500, 1500), seed=2000, sample_rows=rows)
+    gemm_case(mx, orc, 2048, 4096, 4096, (500, 1500), seed=2000, sample_rows=rows, entry=entry)
 
 
 @pytest.mark.parametrize("N,K", [(28672, 8192), (8192, 28672)])
@@ -267,14 +278,16 @@ def test_mixed_gemm_decode_full_size_sampled(mx, orc, M, N, K):
     assert_gemm(Y[:, cols], Yref, Yabs, f"decode M={M} N={N} K={K}")
 
 
-def test_mixed_gemm_strided_output_and_determinism(mx, orc):
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_strided_output_and_determinism(mx, orc, entry):
     Xc, X, W = layer(1024, 160, 70, 256, 77)
     perm = torch.arange(1024, dtype=torch.int32, device=DEV)
     A = mx.mxs_quantize(X, perm, 1, 6, 25)
     B = mx.mxs_quantize(W, perm, 1, 6, 25)
     Ybig = torch.full((70, 200), 7.0, device=DEV)
-    mx.mxs_mixed_gemm(A, B, Y=Ybig[:, 10:170])
-    Y2 = mx.mxs_mixed_gemm(A, B)
+    gemm = getattr(mx, entry)
+    gemm(A, B, Y=Ybig[:, 10:170])
+    Y2 = gemm(A, B)
     assert torch.equal(Ybig[:, 10:170], Y2)
     assert (Ybig[:, :10] == 7).all() and (Ybig[:, 170:] == 7).all()
     Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), None, 1, 6, 25), orc.quantize(host(W), None, 1, 6, 25))
