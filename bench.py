@@ -8,7 +8,9 @@ resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
 (2 M N K per step over the step time) with mxs_mixed_gemm (int8 block sums);
-per-stage times, TOPS and GB/s are in `stages`; `roofline` is for the
+per-stage times, TOPS and GB/s are in `stages` (`ms` from back-to-back
+calls through the Python binding, `graph_ms` from the same calls replayed
+from one HIP graph, i.e. without the Python launch path); `roofline` is for the
 dominant kernel; `variant_mx` repeats the step with mxs_mixed_gemm_mx
 (prefill on the block-scaled fp6 matrix cores); `cpu_baseline` is the CPU
 oracle timed on a bounded sample of the same step.
@@ -23,7 +25,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                                        scale the HBM byte counters)
        python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
                                        and 32 tokens: one JSON line per case, GB/s
-                                       of packed W + scale bytes against HBM peak)
+                                       of packed W + scale bytes against HBM peak,
+                                       from calls replayed from a HIP graph; `us`
+                                       is the same calls made eagerly)
 """
 from __future__ import annotations
 
@@ -102,9 +106,12 @@ def decode_cases(mx, synth, torch, reps=20):
             Aq = mx.mxs_quantize(X, perm, n8, n6, n4)
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ws = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(Aq, Wq)), dtype=torch.uint8, device=dev)
-            t = time_stage(torch, lambda: mx.mxs_mixed_gemm(Aq, Wq, Y, ws=ws), reps)
+            fn = lambda: mx.mxs_mixed_gemm(Aq, Wq, Y, ws=ws)
+            t = time_stage(torch, fn, reps)
+            tg = time_graph(torch, fn, reps)
             print(json.dumps({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": t * 1e6,
-                              "w_bytes": wbytes, "GBps": wbytes / t / 1e9, "hbm_frac": wbytes / t / HBM_PEAK}),
+                              "graph_us": tg * 1e6, "w_bytes": wbytes, "GBps": wbytes / tg / 1e9,
+                              "hbm_frac": wbytes / tg / HBM_PEAK, "eager_hbm_frac": wbytes / t / HBM_PEAK}),
                   flush=True)
 
 
@@ -188,6 +195,26 @@ def time_stage(torch, fn, reps):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps * 1e-3
+
+
+def time_graph(torch, fn, reps):
+    """Mean time per call of reps back-to-back calls replayed from one HIP
+    graph: the device time of the calls without the Python launch path."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (2 * reps) * 1e-3
 
 
 def cpu_baseline(w, torch, min_seconds=10.0, max_reps=20):
@@ -297,11 +324,13 @@ def main():
     stage_out = {}
     for name, fn in stages + [("mixed_gemm_mx", stage_fns(mx, w, variant=True)[5][1])]:
         t = time_stage(torch, fn, args.stage_reps)
+        tg = time_graph(torch, fn, args.stage_reps)
         wk = work["mixed_gemm" if name == "mixed_gemm_mx" else name]
-        d = dict(ms=t * 1e3)
+        d = dict(ms=t * 1e3, graph_ms=tg * 1e3)
         if "bytes" in wk:
             d["GBps"] = wk["bytes"] / t / 1e9
             d["hbm_frac"] = wk["bytes"] / t / HBM_PEAK
+            d["graph_hbm_frac"] = wk["bytes"] / tg / HBM_PEAK
         if "ops" in wk:
             d["TOPS"] = wk["ops"] / t / 1e12
             d["int8_mfma_frac"] = wk["ops"] / t / INT8_PEAK

@@ -182,9 +182,10 @@ def mxs_allocate(score: torch.Tensor, bp8: int, bp6: int, bits=None, perm=None):
     return bits, perm
 
 
-@dataclass
+@dataclass(frozen=True)
 class QMat:
-    """Planes of a matrix quantised with one bit map (see mxs_qmat)."""
+    """Planes of a matrix quantised with one bit map (see mxs_qmat). Frozen:
+    the C struct is built once, on first use, and reused by every call."""
     rows: int
     K: int
     n8: int
@@ -196,14 +197,20 @@ class QMat:
     sc: torch.Tensor
 
     def c_struct(self) -> _QMat:
+        q = self.__dict__.get("_c")
+        if q is not None:
+            return q
+
         def ld(t, width):
             return t.stride(0) if t.numel() else max(width, 1)
         for t in (self.q8, self.q6, self.q4, self.sc):
             if t.numel() and t.stride(1) != 1:
                 raise ValueError("planes need unit column stride")
-        return _QMat(self.rows, self.K, self.n8, self.n6, self.n4, 0,
-                     _ptr(self.q8), ld(self.q8, 32 * self.n8), _ptr(self.q6), ld(self.q6, 24 * self.n6),
-                     _ptr(self.q4), ld(self.q4, 16 * self.n4), _ptr(self.sc), ld(self.sc, self.K // 32))
+        q = _QMat(self.rows, self.K, self.n8, self.n6, self.n4, 0,
+                  _ptr(self.q8), ld(self.q8, 32 * self.n8), _ptr(self.q6), ld(self.q6, 24 * self.n6),
+                  _ptr(self.q4), ld(self.q4, 16 * self.n4), _ptr(self.sc), ld(self.sc, self.K // 32))
+        object.__setattr__(self, "_c", q)
+        return q
 
     def rows_slice(self, r0: int, r1: int) -> "QMat":
         return QMat(r1 - r0, self.K, self.n8, self.n6, self.n4, self.q8[r0:r1], self.q6[r0:r1],
@@ -249,9 +256,12 @@ def _gemm(fn, wsfn, name, A: QMat, W: QMat, Y, ws) -> torch.Tensor:
     if Y.dtype != torch.float32:
         raise TypeError("Y must be fp32")
     py, ldy = _dev2d(Y, "Y")
-    a, w = A.c_struct(), W.c_struct()
-    p, n = _workspace(int(wsfn(ctypes.byref(a), ctypes.byref(w))), dev, ws)
-    _check(fn(ctypes.byref(a), ctypes.byref(w), py, ldy, p, n, _stream(dev)), name)
+    a, w = ctypes.byref(A.c_struct()), ctypes.byref(W.c_struct())
+    if ws is None:
+        p, n = _workspace(int(wsfn(a, w)), dev, None)
+    else:
+        p, n = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check(fn(a, w, py, ldy, p, n, _stream(dev)), name)
     return Y
 
 

@@ -1007,38 +1007,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(const int8_t *__restrict__ P
 // kGemvVecRows tokens use the vector kernel below (k_gemv), more tokens the
 // matrix-core kernel further down (k_decode).
 //
-// k_gemv: a wavefront owns 64 W rows and one K-slice of at most kGemvMaxSlice
-// blocks. The rows' scale bytes of the whole slice are loaded once (aligned
-// dwords) into LDS. The slice's codes are walked in chunks of whole blocks
-// of one width class (8-bit: 4 blocks, 6-bit: 4, 4-bit: 8; 128, 96 and 128
-// bytes per row), each fetched with coalesced loads (consecutive lanes read
-// consecutive bytes of a row) one chunk ahead into registers, written to a
-// per-wave LDS tile with a padded row pitch and read back with lane = row.
-// The tokens' codes and scales are uniform across the wave and come through
-// scalar loads, issued for a whole chunk at a time. Block dot products are
-// exact in int32: 4-bit x 4-bit with v_dot8_i32_i4 on the packed nibbles,
-// 8-bit with v_dot4_i32_i8, 6-bit after widening both sides to bytes
-// (code * 4, the factor 16 folded into the scale). Each block adds
-// I_b * 2^(sa+sw) to an fp32 accumulator per token. K-slices write partial
-// rows that a second kernel adds in slice order, so the result does not
-// depend on scheduling.
+// k_gemv: a wavefront owns 64 W rows and one slice of one width class (two
+// chunks: 8 blocks of 8 or 6 bits, or 16 blocks of 4 bits). It issues every
+// load of the slice at once: the rows' and tokens' scale bytes, then the
+// codes, each row group of 8 rows with one coalesced 16-byte load per lane
+// (lane e of a row reads one piece of it: a whole 4-bit block or half an
+// 8- or 6-bit block), and the tokens' matching pieces. No code bytes pass
+// through LDS, so occupancy is set by registers and each wave keeps 16 KiB
+// of W in flight. Block dot products are exact in int32: 4-bit x 4-bit with
+// v_dot8_i32_i4 on the packed nibbles, 8-bit with v_dot4_i32_i8, 6-bit after
+// widening both sides to bytes (code * 4, the factor 16 folded into the
+// scale); the two lanes holding the halves of an 8- or 6-bit block add their
+// sums (one DPP add). Each block adds I_b * 2^(sa+sw) to an fp32 accumulator
+// per row and token; the eight lanes of a row are summed in a fixed butterfly
+// at the end. Slices write partial rows that a second kernel adds in slice
+// order, so the result does not depend on scheduling.
 constexpr int kGemvMaxRows = 32;   // decode path: up to 32 tokens
 constexpr int kGemvVecRows = 4;    // up to 4 tokens on the vector ALU, above on the matrix cores
-constexpr int kGemvMaxSlice = 64;   // blocks per K-slice (multiple of 8)
 constexpr int kGemvPitch = 144;     // 8-bit and 4-bit tiles: 128 bytes + 16 (conflict-free b128 reads)
 constexpr int kGemvPitch6 = 104;    // 6-bit tile: 96 bytes + 8 (conflict-free b64 reads)
-constexpr int kGemvScPitch = kGemvMaxSlice + 4;   // 17 dwords: conflict-free dword reads
 constexpr int kGemvTile = 64 * kGemvPitch;
 
 __device__ __forceinline__ uint32_t wide6(uint32_t g) {   // four 6-bit fields -> four bytes (code * 4)
     return ((g << 2) & 0xFCu) | ((g << 4) & 0xFC00u) | ((g << 6) & 0xFC0000u) | ((g << 8) & 0xFC000000u);
-}
-
-// the 6-bit field group g (0..7) of a 24-byte block held as 6 words
-__device__ __forceinline__ uint32_t group6(const uint32_t w[6], int g) {
-    const int bit = 24 * g;
-    const uint32_t lo = w[bit >> 5], hi = (bit >> 5) + 1 < 6 ? w[(bit >> 5) + 1] : 0u;
-    return __builtin_amdgcn_alignbit(hi, lo, bit & 31);
 }
 
 // bytes o..o+7 of a byte string held as 32-bit words p[], reading only the
@@ -1072,38 +1063,38 @@ __device__ __forceinline__ GemvChunk gemv_chunk(int32_t gb, int32_t b1, int32_t 
 // Coalesced fetch of one chunk of codes for 64 rows into registers. Lane
 // roles (row within a group of 8 rows, piece of the row) are fixed; load i
 // moves to the next group, so every address is a uniform base plus a 32-bit
-// lane offset. Pieces of rows past N or of blocks past the chunk re-read
-// the first bytes of the tile's first row (always valid) instead of
-// branching; they are staged but never used.
-//   4-bit: 8 lanes x 16 bytes per row, 8 loads
-//   8-bit: 8 lanes x 16 bytes per row, 8 loads
-//   6-bit: 8 lanes x 12 bytes (3 dword loads) per row, 8 x 3 loads
+// lane offset. Every width takes one 16-byte load per row group:
+//   4-bit: 8 lanes x 16 bytes per row (lane e: block e of the chunk)
+//   8-bit: 8 lanes x 16 bytes per row (lane e: half e & 1 of block e / 2)
+//   6-bit: 8 lanes x 12 bytes per row (lane e: half e & 1 of block e / 2);
+//          the load covers bytes 0..15 of the block for the first half and
+//          bytes 8..23 for the second, so it never leaves the block, and
+//          piece6 picks the three words of the half.
+// Row group i lands in R[4 i .. 4 i + 3]. Pieces of rows past N or of
+// blocks past the chunk re-read the first bytes of the tile's first row
+// (always valid) instead of branching; they are never used.
 __device__ __forceinline__ void gemv_fetch(const QView &W, int64_t row0, int32_t rows_left, const GemvChunk &c,
                                            int lane, uint32_t R[32]) {
     const int rs = lane >> 3, e = lane & 7;
-    if (c.cls == 6) {
-        const bool ok = (e >> 1) < c.nblk;
-        const uint8_t *base = W.q6 + row0 * W.ld6;
-        const uint32_t off = (uint32_t)(rs * W.ld6 + 12 * e + 24 * c.pb), step = (uint32_t)(8 * W.ld6);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t o = (ok && rs + 8 * i < rows_left) ? off + i * step : 0u;
-            const uint32_t *q = reinterpret_cast<const uint32_t *>(base + o);
-            R[3 * i] = q[0]; R[3 * i + 1] = q[1]; R[3 * i + 2] = q[2];
-        }
-        return;
-    }
-    const bool c4 = c.cls == 4;
+    const bool c4 = c.cls == 4, c6 = c.cls == 6;
     const bool ok = (c4 ? e : e >> 1) < c.nblk;
-    const uint8_t *base = c4 ? W.q4 + row0 * W.ld4 : reinterpret_cast<const uint8_t *>(W.q8) + row0 * W.ld8;
-    const int64_t ld = c4 ? W.ld4 : W.ld8;
-    const uint32_t off = (uint32_t)(rs * ld + 16 * e + (c4 ? 16 : 32) * c.pb), step = (uint32_t)(8 * ld);
+    const int64_t ld = c4 ? W.ld4 : c6 ? W.ld6 : W.ld8;
+    const uint8_t *base = (c4 ? W.q4 : c6 ? W.q6 : reinterpret_cast<const uint8_t *>(W.q8)) + row0 * ld;
+    const uint32_t pos = c4 ? 16 * (c.pb + e) : c6 ? 24 * c.pb + 12 * e - 4 * (e & 1) : 32 * c.pb + 16 * e;
+    const uint32_t off = (uint32_t)(rs * ld) + pos, step = (uint32_t)(8 * ld);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t o = (ok && rs + 8 * i < rows_left) ? off + i * step : 0u;
         const uint4 v = *reinterpret_cast<const uint4 *>(base + o);
         R[4 * i] = v.x; R[4 * i + 1] = v.y; R[4 * i + 2] = v.z; R[4 * i + 3] = v.w;
     }
+}
+
+// the three words of a 6-bit half block held as a 16-byte load (see gemv_fetch)
+__device__ __forceinline__ void piece6(const uint32_t r[4], bool second, uint32_t w[3]) {
+    w[0] = second ? r[1] : r[0];
+    w[1] = second ? r[2] : r[1];
+    w[2] = second ? r[3] : r[2];
 }
 
 // Registers -> LDS tile (row pitch kGemvPitch, or kGemvPitch6 for 6-bit),
@@ -1113,8 +1104,10 @@ __device__ __forceinline__ void gemv_stage(uint8_t *tile, int cls, int lane, con
     if (cls == 6) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            uint32_t w[3];
+            piece6(&R[4 * i], e & 1, w);
             uint32_t *q = reinterpret_cast<uint32_t *>(tile + (rs + 8 * i) * kGemvPitch6 + 12 * e);
-            q[0] = R[3 * i]; q[1] = R[3 * i + 1]; q[2] = R[3 * i + 2];
+            q[0] = w[0]; q[1] = w[1]; q[2] = w[2];
         }
     } else {
 #pragma unroll
@@ -1124,110 +1117,202 @@ __device__ __forceinline__ void gemv_stage(uint8_t *tile, int cls, int lane, con
     }
 }
 
-// One staged chunk against the tokens. FULL: the chunk has all its blocks,
-// so no per-block bound is tested and the tokens' loads of the chunk issue
-// together. swb: the row's W scale bytes of the chunk.
-template <int MT, bool FULL>
-__device__ __forceinline__ void gemv_chunk_dot(const int8_t *__restrict__ a8, int64_t la8,
+// Token pieces of one chunk: the same bytes of every token row as the lane's
+// W piece, loaded the same way (see gemv_fetch). Pieces past the chunk
+// re-read the row's first bytes.
+template <int MT>
+__device__ __forceinline__ void gemv_fetch_tok(const int8_t *__restrict__ a8, int64_t la8,
                                                const uint8_t *__restrict__ a6, int64_t la6,
-                                               const uint8_t *__restrict__ a4, int64_t la4,
-                                               const uint8_t *__restrict__ asc, int64_t las, int32_t M,
-                                               const GemvChunk &cur, const uint8_t *tile, uint64_t swb,
-                                               int lane, float acc[MT]) {
+                                               const uint8_t *__restrict__ a4, int64_t la4, int32_t M,
+                                               const GemvChunk &c, int lane, uint32_t T[MT][4]) {
+    const int e = lane & 7;
+    const bool c4 = c.cls == 4, c6 = c.cls == 6;
+    const bool ok = (c4 ? e : e >> 1) < c.nblk;
+    const int64_t ld = c4 ? la4 : c6 ? la6 : la8;
+    const uint8_t *base = c4 ? a4 : c6 ? a6 : reinterpret_cast<const uint8_t *>(a8);
+    const uint32_t pos = !ok ? 0u : c4 ? 16 * (c.pb + e) : c6 ? 24 * c.pb + 12 * e - 4 * (e & 1) : 32 * c.pb + 16 * e;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t >= M) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(base + t * ld + pos);
+        T[t][0] = v.x; T[t][1] = v.y; T[t][2] = v.z; T[t][3] = v.w;
+    }
+}
+
+// 16 6-bit codes (three words) -> four words of bytes (code * 4)
+__device__ __forceinline__ void wide6x16(const uint32_t w[3], uint32_t b[4]) {
+    b[0] = wide6(w[0]);
+    b[1] = wide6(__builtin_amdgcn_alignbit(w[1], w[0], 24));
+    b[2] = wide6(__builtin_amdgcn_alignbit(w[2], w[1], 16));
+    b[3] = wide6(w[2] >> 8);
+}
+
+// v summed over the eight lanes of its group (lane ^ 4, ^ 2, ^ 1); every
+// lane of the group ends with the same value
+__device__ __forceinline__ float sum8(float v) {
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));           // xor 4
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)); // xor 2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)); // xor 1
+    return v;
+}
+
+// Slices of the vector kernel: each width class is cut into runs of
+// kVecChunks chunks (8- and 6-bit chunks hold 4 blocks, 4-bit chunks 8), in
+// the order 8-bit, 6-bit, 4-bit; slice s of a wave is blockIdx.y.
+constexpr int kVecChunks = 2;
+constexpr int kVecScW = 6;   // dwords of staged scale bytes per row (20 used)
+
+struct VecSlices {
+    int32_t s8, s6, s4;
+};
+
+__host__ __device__ inline VecSlices vec_slices(int32_t n8, int32_t n6, int32_t n4) {
+    const int32_t p8 = 4 * kVecChunks, p4 = 8 * kVecChunks;
+    return VecSlices{(n8 + p8 - 1) / p8, (n6 + p8 - 1) / p8, (n4 + p4 - 1) / p4};
+}
+
+// slice s -> width class, first block (global and within the class plane)
+// and block count
+__device__ __forceinline__ GemvChunk vec_slice(int32_t s, int32_t n8, int32_t n6, int32_t n4, VecSlices S) {
+    GemvChunk c;
+    const int32_t p8 = 4 * kVecChunks, p4 = 8 * kVecChunks;
+    if (s < S.s8) {
+        c.cls = 8; c.pb = s * p8; c.gb = c.pb; c.nblk = min(p8, n8 - c.pb);
+    } else if (s < S.s8 + S.s6) {
+        c.cls = 6; c.pb = (s - S.s8) * p8; c.gb = n8 + c.pb; c.nblk = min(p8, n6 - c.pb);
+    } else {
+        c.cls = 4; c.pb = (s - S.s8 - S.s6) * p4; c.gb = n8 + n6 + c.pb; c.nblk = min(p4, n4 - c.pb);
+    }
+    return c;
+}
+
+// chunk j of a slice
+__device__ __forceinline__ GemvChunk vec_chunk(const GemvChunk &sl, int j) {
+    const int32_t bpc = sl.cls == 4 ? 8 : 4;
+    GemvChunk c = sl;
+    c.gb += j * bpc;
+    c.pb += j * bpc;
+    c.nblk = min(bpc, max(0, sl.nblk - j * bpc));
+    return c;
+}
+
+// One chunk against the tokens: lane (rs, e) dots its piece of rows
+// rs + 8 g with the tokens' piece. 4-bit pieces are whole blocks; 8- and
+// 6-bit pieces are half blocks, whose integer sums the two lanes of a pair
+// add before the even lane scales the block sum. scw / sca: the slice's
+// staged scale bytes (W rows, tokens), chunk block k at byte o + k.
+template <int MT, int CLS>
+__device__ __forceinline__ void vec_dot(const GemvChunk &c, int32_t o, int32_t M, int lane, const uint32_t R[32],
+                                        const uint32_t T[MT][4], const uint8_t *scw, const uint8_t *sca,
+                                        float acc[MT][8]) {
+    const int rs = lane >> 3, e = lane & 7;
+    const int pblk = CLS == 4 ? e : e >> 1;
+    const bool on = pblk < c.nblk && (CLS == 4 || (e & 1) == 0);
+    const int col = on ? o + pblk : 0;
     float sw[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sw[j] = e8m0_to_f32((uint32_t)(swb >> (8 * j)) & 0xFFu);
-    const int32_t dl = (cur.gb + cur.nblk - 1) >> 2;   // last dword of the tokens' scale bytes
-    if (cur.cls == 4) {
-        uint4 w[8];
+    for (int g = 0; g < 8; ++g) sw[g] = e8m0_to_f32(scw[(rs + 8 * g) * 4 * kVecScW + col]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 16 * j);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t >= M) break;
-            const uint8_t *ap = a4 + t * la4 + 16 * (int64_t)cur.pb;
-            uint4 a[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = *reinterpret_cast<const uint4 *>(ap + ((FULL || j < cur.nblk) ? 16 * j : 0));
-            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (!FULL && j >= cur.nblk) break;
-                int d = __builtin_amdgcn_sdot8((int)a[j].x, (int)w[j].x, 0, false);
-                d = __builtin_amdgcn_sdot8((int)a[j].y, (int)w[j].y, d, false);
-                d = __builtin_amdgcn_sdot8((int)a[j].z, (int)w[j].z, d, false);
-                d = __builtin_amdgcn_sdot8((int)a[j].w, (int)w[j].w, d, false);
-                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
-                acc[t] = __builtin_fmaf((float)d, sa * sw[j], acc[t]);
-            }
-        }
-    } else if (cur.cls == 8) {
-        uint4 w[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            w[j][0] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 32 * j);
-            w[j][1] = *reinterpret_cast<const uint4 *>(tile + lane * kGemvPitch + 32 * j + 16);
+    for (int t = 0; t < MT; ++t) {
+        if (t >= M) break;
+        const float sa = e8m0_to_f32(sca[t * 4 * kVecScW + col]) * (CLS == 6 ? 0.0625f : 1.0f);
+        uint32_t ab[4];
+        if (CLS == 6) {
+            uint32_t aw[3];
+            piece6(T[t], e & 1, aw);
+            wide6x16(aw, ab);
         }
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t >= M) break;
-            const int8_t *ap = a8 + t * la8 + 32 * (int64_t)cur.pb;
-            uint4 a[4][2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 *q = reinterpret_cast<const uint4 *>(ap + ((FULL || j < cur.nblk) ? 32 * j : 0));
-                a[j][0] = q[0]; a[j][1] = q[1];
+        for (int g = 0; g < 8; ++g) {
+            int d;
+            if (CLS == 4) {
+                d = __builtin_amdgcn_sdot8((int)T[t][0], (int)R[4 * g], 0, false);
+                d = __builtin_amdgcn_sdot8((int)T[t][1], (int)R[4 * g + 1], d, false);
+                d = __builtin_amdgcn_sdot8((int)T[t][2], (int)R[4 * g + 2], d, false);
+                d = __builtin_amdgcn_sdot8((int)T[t][3], (int)R[4 * g + 3], d, false);
+            } else if (CLS == 8) {
+                d = __builtin_amdgcn_sdot4((int)T[t][0], (int)R[4 * g], 0, false);
+                d = __builtin_amdgcn_sdot4((int)T[t][1], (int)R[4 * g + 1], d, false);
+                d = __builtin_amdgcn_sdot4((int)T[t][2], (int)R[4 * g + 2], d, false);
+                d = __builtin_amdgcn_sdot4((int)T[t][3], (int)R[4 * g + 3], d, false);
+                d += __builtin_amdgcn_mov_dpp(d, 0xB1, 0xF, 0xF, true);
+            } else {
+                uint32_t wb[4], ww[3];
+                piece6(&R[4 * g], e & 1, ww);
+                wide6x16(ww, wb);
+                d = __builtin_amdgcn_sdot4((int)ab[0], (int)wb[0], 0, false);
+                d = __builtin_amdgcn_sdot4((int)ab[1], (int)wb[1], d, false);
+                d = __builtin_amdgcn_sdot4((int)ab[2], (int)wb[2], d, false);
+                d = __builtin_amdgcn_sdot4((int)ab[3], (int)wb[3], d, false);
+                d += __builtin_amdgcn_mov_dpp(d, 0xB1, 0xF, 0xF, true);
             }
-            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!FULL && j >= cur.nblk) break;
-                int d = 0;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    d = __builtin_amdgcn_sdot4((int)a[j][h].x, (int)w[j][h].x, d, false);
-                    d = __builtin_amdgcn_sdot4((int)a[j][h].y, (int)w[j][h].y, d, false);
-                    d = __builtin_amdgcn_sdot4((int)a[j][h].z, (int)w[j][h].z, d, false);
-                    d = __builtin_amdgcn_sdot4((int)a[j][h].w, (int)w[j][h].w, d, false);
-                }
-                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
-                acc[t] = __builtin_fmaf((float)d, sa * sw[j], acc[t]);
-            }
+            acc[t][g] = __builtin_fmaf((float)d, on ? sa * sw[g] : 0.f, acc[t][g]);
         }
-    } else {
-        uint32_t wb[4][8];
+    }
+}
+
+// The body of k_gemv for one width class: every load of the slice is issued
+// first (scale bytes, then the chunks' codes), then the chunks are computed
+// in order as their loads land.
+template <int MT, int CLS>
+__device__ __forceinline__ void vec_body(const int8_t *__restrict__ a8, int64_t la8, const uint8_t *__restrict__ a6,
+                                         int64_t la6, const uint8_t *__restrict__ a4, int64_t la4,
+                                         const uint8_t *__restrict__ asc, int64_t las, const QView &W, int32_t M,
+                                         int64_t N, int32_t nb, const GemvChunk &sl, uint32_t *scw_s,
+                                         uint32_t *sca_s, float *__restrict__ out, int64_t ldo) {
+    const int lane = threadIdx.x;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const int32_t rows_left = N - row0 < 64 ? (int32_t)(N - row0) : 64;
+
+    // scale bytes of the slice: five dwords from the dword holding block gb
+    // (indices clamped to the row's last dword); lane r: W row r, lanes
+    // 5 t + k: dword k of token t
+    const int32_t d0 = sl.gb >> 2, dl = (nb - 1) >> 2;
+    uint32_t vw[5], va = 0;
+    {
+        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + (row0 + (lane < rows_left ? lane : 0)) * W.lds);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint8_t *wp = tile + lane * kGemvPitch6 + 24 * j;
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(wp);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(wp + 8);
-            const uint2 v2 = *reinterpret_cast<const uint2 *>(wp + 16);
-            const uint32_t wr[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
+        for (int k = 0; k < 5; ++k) vw[k] = sp[min(d0 + k, dl)];
+        const int t = lane / 5, k = lane - 5 * t;
+        if (t < MT && t < M) va = reinterpret_cast<const uint32_t *>(asc + t * las)[min(d0 + k, dl)];
+    }
+    GemvChunk ch[kVecChunks];
+    uint32_t R[kVecChunks][32], T[kVecChunks][MT][4];
 #pragma unroll
-            for (int g = 0; g < 8; ++g) wb[j][g] = wide6(group6(wr, g));
+    for (int j = 0; j < kVecChunks; ++j) {
+        ch[j] = vec_chunk(sl, j);
+        gemv_fetch(W, row0, rows_left, ch[j], lane, R[j]);
+        gemv_fetch_tok<MT>(a8, la8, a6, la6, a4, la4, M, ch[j], lane, T[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < 5; ++k) scw_s[lane * kVecScW + k] = vw[k];
+    if (lane < 5 * MT) sca_s[(lane / 5) * kVecScW + lane % 5] = va;
+    __syncthreads();
+
+    float acc[MT][8];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int g = 0; g < 8; ++g) acc[t][g] = 0.f;
+    const uint8_t *scw = reinterpret_cast<const uint8_t *>(scw_s);
+    const uint8_t *sca = reinterpret_cast<const uint8_t *>(sca_s);
+#pragma unroll
+    for (int j = 0; j < kVecChunks; ++j)
+        vec_dot<MT, CLS>(ch[j], (sl.gb & 3) + (ch[j].gb - sl.gb), M, lane, R[j], T[j], scw, sca, acc);
+
+    // sum each row over its eight lanes; lane (rs, e) then writes row rs + 8 e
+    const int rs = lane >> 3, e = lane & 7;
+    const int64_t n = row0 + rs + 8 * e;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t >= M) break;
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const float s = sum8(acc[t][g]);
+            v = e == g ? s : v;
         }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t >= M) break;
-            const uint8_t *ap = a6 + t * la6 + 24 * (int64_t)cur.pb;
-            uint32_t ar[4][6];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t *q = reinterpret_cast<const uint32_t *>(ap + ((FULL || j < cur.nblk) ? 24 * j : 0));
-#pragma unroll
-                for (int i = 0; i < 6; ++i) ar[j][i] = q[i];
-            }
-            const uint64_t sab = bytes8(reinterpret_cast<const uint32_t *>(asc + t * las), cur.gb, dl);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!FULL && j >= cur.nblk) break;
-                int d = 0;
-#pragma unroll
-                for (int g = 0; g < 8; ++g) d = __builtin_amdgcn_sdot4((int)wide6(group6(ar[j], g)), (int)wb[j][g], d, false);
-                const float sa = e8m0_to_f32((uint32_t)(sab >> (8 * j)) & 0xFFu);
-                acc[t] = __builtin_fmaf((float)d, sa * (sw[j] * 0.0625f), acc[t]);
-            }
-        }
+        if (n < N) out[t * ldo + n] = v;
     }
 }
 
@@ -1236,67 +1321,20 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
                                              const uint8_t *__restrict__ a6, int64_t la6,
                                              const uint8_t *__restrict__ a4, int64_t la4,
                                              const uint8_t *__restrict__ asc, int64_t las, QView W, int32_t M,
-                                             int64_t N, int32_t n8, int32_t n6, int32_t nb, int32_t bps,
+                                             int64_t N, int32_t n8, int32_t n6, int32_t n4,
                                              float *__restrict__ out, int64_t ldo, int64_t slice_stride) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kGemvTile];
-    __shared__ __attribute__((aligned(16))) uint32_t sct[64 * kGemvScPitch / 4];
-    const int lane = threadIdx.x;
-    const int64_t row0 = (int64_t)blockIdx.x * 64;
-    const int32_t rows_left = N - row0 < 64 ? (int32_t)(N - row0) : 64;
-    const int32_t b0 = (int32_t)blockIdx.y * bps;
-    const int32_t b1 = b0 + bps < nb ? b0 + bps : nb;
-    const int32_t h6 = n8 + n6;
-
-    uint32_t R[32];
-    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
-    gemv_fetch(W, row0, rows_left, c, lane, R);
-
-    // the slice's W scale bytes: dwords b0/4 .. (b1-1)/4 of each row (b0 is a
-    // multiple of 8; scale rows are 4-byte aligned), 16 lanes per row
-    {
-        const int32_t nd = (b1 - b0 + 3) >> 2;
-        const int d = lane & 15, rq = lane >> 4;
-        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + row0 * W.lds + b0);
-        const int64_t ldw = W.lds >> 2;
-        uint32_t v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = rq + 4 * i;
-            v[i] = sp[(d < nd && r < rows_left) ? r * ldw + d : 0];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sct[(rq + 4 * i) * (kGemvScPitch / 4) + d] = v[i];
-    }
-
-    float acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-    const uint32_t *my_sc = sct + lane * (kGemvScPitch / 4);
-    while (true) {
-        gemv_stage(tile, c.cls, lane, R);
-        __builtin_amdgcn_wave_barrier();
-        const GemvChunk cur = c;
-        const int32_t next = cur.gb + cur.nblk;
-        if (next < b1) {
-            c = gemv_chunk(next, b1, n8, h6, nb);
-            gemv_fetch(W, row0, rows_left, c, lane, R);
-        }
-        const uint64_t swb = bytes8(my_sc, cur.gb - b0, (next - 1 - b0) >> 2);
-        if (cur.nblk == (cur.cls == 4 ? 8 : 4))
-            gemv_chunk_dot<MT, true>(a8, la8, a6, la6, a4, la4, asc, las, M, cur, tile, swb, lane, acc);
-        else
-            gemv_chunk_dot<MT, false>(a8, la8, a6, la6, a4, la4, asc, las, M, cur, tile, swb, lane, acc);
-        if (next >= b1) break;
-        __builtin_amdgcn_wave_barrier();
-    }
-    const int64_t n = row0 + lane;
-    if (n >= N) return;
-    float *o = out + (int64_t)blockIdx.y * slice_stride + n;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t >= M) break;
-        o[t * ldo] = acc[t];
-    }
+    __shared__ uint32_t scw_s[64 * kVecScW];
+    __shared__ uint32_t sca_s[MT * kVecScW];
+    const VecSlices S = vec_slices(n8, n6, n4);
+    const GemvChunk sl = vec_slice((int32_t)blockIdx.y, n8, n6, n4, S);
+    const int32_t nb = n8 + n6 + n4;
+    float *o = out + (int64_t)blockIdx.y * slice_stride;
+    if (sl.cls == 4)
+        vec_body<MT, 4>(a8, la8, a6, la6, a4, la4, asc, las, W, M, N, nb, sl, scw_s, sca_s, o, ldo);
+    else if (sl.cls == 8)
+        vec_body<MT, 8>(a8, la8, a6, la6, a4, la4, asc, las, W, M, N, nb, sl, scw_s, sca_s, o, ldo);
+    else
+        vec_body<MT, 6>(a8, la8, a6, la6, a4, la4, asc, las, W, M, N, nb, sl, scw_s, sca_s, o, ldo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1559,18 +1597,6 @@ struct GemvPlan {
     int32_t nslices, bps;
 };
 
-GemvPlan gemv_plan(const mxs_qmat &A, const mxs_qmat &W) {
-    const int32_t nb = (int32_t)(A.K / 32);
-    const int64_t waves = ceil_div(W.rows, 64);
-    int64_t ns = ceil_div(8192, waves);            // a few rounds of waves over the machine
-    const int64_t max_ns = ceil_div(nb, 16);       // at least 16 blocks per slice
-    const int64_t min_ns = ceil_div(nb, kGemvMaxSlice);
-    ns = ns > max_ns ? max_ns : ns;
-    ns = ns < min_ns ? min_ns : ns;
-    const int32_t bps = (int32_t)(ceil_div(ceil_div(nb, ns), 8) * 8);
-    return GemvPlan{(int32_t)ceil_div(nb, bps), bps};
-}
-
 struct PrepLayout {
     int64_t Mp, Np, Kp;
     size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
@@ -1605,20 +1631,21 @@ bool use_gemv(const mxs_qmat &A, const mxs_qmat &W) {
 
 template <int MT>
 hipError_t launch_gemv_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
-    const GemvPlan P = gemv_plan(A, W);
+    const VecSlices S = vec_slices(A.n8, A.n6, A.n4);
+    const int32_t ns = S.s8 + S.s6 + S.s4;
     const int64_t M = A.rows, N = W.rows;
-    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)P.nslices);
-    if (P.nslices == 1) {
+    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ns);
+    if (ns == 1) {
         hipLaunchKernelGGL((k_gemv<MT>), grid, dim3(64), 0, st, A.q8, A.ld8, A.q6, A.ld6, A.q4, A.ld4, A.sc, A.lds,
-                           view_of(W), (int32_t)M, N, A.n8, A.n6, (int32_t)(A.K / 32), P.bps, Y, ldy, (int64_t)0);
+                           view_of(W), (int32_t)M, N, A.n8, A.n6, A.n4, Y, ldy, (int64_t)0);
         return hipGetLastError();
     }
     float *part = static_cast<float *>(ws);
     hipLaunchKernelGGL((k_gemv<MT>), grid, dim3(64), 0, st, A.q8, A.ld8, A.q6, A.ld6, A.q4, A.ld4, A.sc, A.lds,
-                       view_of(W), (int32_t)M, N, A.n8, A.n6, (int32_t)(A.K / 32), P.bps, part, N, M * N);
+                       view_of(W), (int32_t)M, N, A.n8, A.n6, A.n4, part, N, M * N);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, part, P.nslices,
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, part, ns,
                        (int32_t)M, N, Y, ldy);
     return hipGetLastError();
 }
@@ -1704,11 +1731,11 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
 // Decode (up to 32 tokens) and 33..63 tokens take the same kernels in both
 // entry points; they differ in the prefill kernels only.
 size_t decode_workspace(const mxs_qmat &A, const mxs_qmat &W) {
-    const GemvPlan P = decode_plan(A, W);
-    const GemvPlan Q = gemv_plan(A, W);
-    const size_t a = P.nslices > 1 ? (size_t)P.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
-    const size_t b = Q.nslices > 1 ? (size_t)Q.nslices * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
-    return a > b ? a : b;
+    const int64_t ns = A.rows > kGemvVecRows ? decode_plan(A, W).nslices : [&] {
+        const VecSlices S = vec_slices(A.n8, A.n6, A.n4);
+        return (int64_t)S.s8 + S.s6 + S.s4;
+    }();
+    return ns > 1 ? (size_t)ns * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0;
 }
 
 hipError_t launch_small(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
