@@ -8,9 +8,11 @@ resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
 (2 M N K per step over the step time) with mxs_mixed_gemm (int8 block sums);
-per-stage times, TOPS and GB/s are in `stages` (`ms` from back-to-back
-calls through the Python binding, `graph_ms` from the same calls replayed
-from one HIP graph, i.e. without the Python launch path); `roofline` is for the
+per-stage times, TOPS and GB/s are in `stages` (`ms`: median of single
+calls, each after a read pass over 512 MB that evicts the 256 MB Infinity Cache,
+so inputs come from HBM; `warm_ms`: back-to-back calls through the Python
+binding; `warm_graph_ms`: the same calls replayed from one HIP graph; both
+warm figures re-read inputs the cache holds); `roofline` is for the
 dominant kernel; `variant_mx` repeats the step with mxs_mixed_gemm_mx
 (prefill on the block-scaled fp6 matrix cores); `cpu_baseline` is the CPU
 oracle timed on a bounded sample of the same step.
@@ -23,11 +25,15 @@ profiles/ and is reported only while the GEMM source is unchanged since.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-probe   (a plain device copy of known size, to
                                        scale the HBM byte counters)
+       python bench.py --overhead     (mixed_gemm under the all-4-bit, 4.03-bit,
+                                       binary 4/8 and 5/15/80 % maps, prefill and
+                                       decode: one JSON line per map)
        python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
                                        and 32 tokens: one JSON line per case, GB/s
                                        of packed W + scale bytes against HBM peak,
-                                       from calls replayed from a HIP graph; `us`
-                                       is the same calls made eagerly)
+                                       median of single calls after an Infinity
+                                       Cache flush; `warm_graph_us` is the same
+                                       calls replayed back to back from a graph)
 """
 from __future__ import annotations
 
@@ -90,6 +96,7 @@ def decode_cases(mx, synth, torch, reps=20):
     """70B MLP decode GEMMs (up 28672 x 8192, down 8192 x 28672, 5/15/80 %)."""
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[4]
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     for li, lay in enumerate(cfg["layers"]):
         N, K = lay["N"], lay["K"]
         bp8, bp6 = lay["budget"]
@@ -107,12 +114,50 @@ def decode_cases(mx, synth, torch, reps=20):
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ws = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(Aq, Wq)), dtype=torch.uint8, device=dev)
             fn = lambda: mx.mxs_mixed_gemm(Aq, Wq, Y, ws=ws)
-            t = time_stage(torch, fn, reps)
+            tc = time_cold(torch, fn, reps, flush)
             tg = time_graph(torch, fn, reps)
-            print(json.dumps({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": t * 1e6,
-                              "graph_us": tg * 1e6, "w_bytes": wbytes, "GBps": wbytes / tg / 1e9,
-                              "hbm_frac": wbytes / tg / HBM_PEAK, "eager_hbm_frac": wbytes / t / HBM_PEAK}),
+            print(json.dumps({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": tc * 1e6,
+                              "warm_graph_us": tg * 1e6, "w_bytes": wbytes, "GBps": wbytes / tc / 1e9,
+                              "hbm_frac": wbytes / tc / HBM_PEAK, "warm_hbm_frac": wbytes / tg / HBM_PEAK}),
                   flush=True)
+
+
+def overhead_cases(mx, synth, torch, reps=20):
+    """Cost of the mixed map against uniform MXINT4: mixed_gemm on the same
+    layer under the all-4-bit map, the 4.03-bit map (one 8-bit block), the
+    binary 4/8 map of the same 8-bit share (5 %), and the 5/15/80 % map, for
+    the q_proj prefill (2048 x 4096 x 4096) and the 70B up-projection decode
+    (1 token, 28672 x 8192)."""
+    dev = torch.device("cuda:0")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    for case, M, N, K, seed in (("prefill q_proj", 2048, 4096, 4096, 5000), ("decode 70B up", 1, 28672, 8192, 5100)):
+        nb = K // 32
+        gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+        W = synth.weights(N, K, seed + synth.ROLE_W, device=dev)
+        X = synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev)
+        perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(dev)
+        base = None
+        for name, (bp8, bp6) in (("uniform 4-bit", (0, 0)), ("one 8-bit block", ((10000 + nb - 1) // nb, 0)),
+                                 ("binary 4/8 (5 % 8-bit)", (500, 0)), ("5/15/80 %", (500, 1500))):
+            n8, n6, n4 = mx.mxs_budget_blocks(K, bp8, bp6)
+            Wq = mx.mxs_quantize(W, perm, n8, n6, n4)
+            Aq = mx.mxs_quantize(X, perm, n8, n6, n4)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            out = {"case": case, "map": name, "blocks": [n8, n6, n4], "avg_bits": (8 * n8 + 6 * n6 + 4 * n4) / nb}
+            for entry in ("mxs_mixed_gemm", "mxs_mixed_gemm_mx"):
+                wsf = getattr(mx, entry + "_workspace")
+                ws = torch.empty(max(1, wsf(Aq, Wq)), dtype=torch.uint8, device=dev)
+                f = getattr(mx, entry)
+                fn = lambda: f(Aq, Wq, Y, ws=ws)
+                out[entry + "_us"] = time_graph(torch, fn, reps) * 1e6
+                out[entry + "_cold_us"] = time_cold(torch, fn, reps, flush) * 1e6
+            if base is None:
+                base = out
+            for k in ("mxs_mixed_gemm_us", "mxs_mixed_gemm_mx_us", "mxs_mixed_gemm_cold_us"):
+                out[k.replace("_us", "_vs_uniform")] = out[k] / base[k]
+            print(json.dumps(out), flush=True)
+            del Wq, Aq, Y
+        del W, X
 
 
 def build_workload(mx, synth, torch, dev):
@@ -197,6 +242,30 @@ def time_stage(torch, fn, reps):
     return s.elapsed_time(e) / reps * 1e-3
 
 
+FLUSH_BYTES = 512 << 20   # more than the 256 MB Infinity Cache in front of HBM
+
+
+def time_cold(torch, fn, reps, flush):
+    """Median time of single calls, each after a read pass over a buffer
+    larger than the Infinity Cache, so the call's inputs come from HBM rather
+    than from the cache that repeated calls would leave warm. The pass only
+    reads, so the cache holds no dirty lines that the call would have to
+    write back."""
+    fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        torch.amax(flush)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2] * 1e-3
+
+
 def time_graph(torch, fn, reps):
     """Mean time per call of reps back-to-back calls replayed from one HIP
     graph: the device time of the calls without the Python launch path."""
@@ -261,6 +330,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--overhead", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -276,6 +346,9 @@ def main():
     from bit_gemm_hdiag_amd import synth
     if args.decode:
         decode_cases(mx, synth, torch)
+        return
+    if args.overhead:
+        overhead_cases(mx, synth, torch)
         return
 
     dev = torch.device("cuda:0")
@@ -321,16 +394,17 @@ def main():
     log(f"step {step_x * 1e3:.3f} ms, mixed_gemm_mx call {gemm_x * 1e6:.1f} us")
 
     work = algorithmic_work(w)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     stage_out = {}
     for name, fn in stages + [("mixed_gemm_mx", stage_fns(mx, w, variant=True)[5][1])]:
-        t = time_stage(torch, fn, args.stage_reps)
+        t = time_cold(torch, fn, max(args.stage_reps, 9), flush)
+        tw = time_stage(torch, fn, args.stage_reps)
         tg = time_graph(torch, fn, args.stage_reps)
         wk = work["mixed_gemm" if name == "mixed_gemm_mx" else name]
-        d = dict(ms=t * 1e3, graph_ms=tg * 1e3)
+        d = dict(ms=t * 1e3, warm_ms=tw * 1e3, warm_graph_ms=tg * 1e3)
         if "bytes" in wk:
             d["GBps"] = wk["bytes"] / t / 1e9
             d["hbm_frac"] = wk["bytes"] / t / HBM_PEAK
-            d["graph_hbm_frac"] = wk["bytes"] / tg / HBM_PEAK
         if "ops" in wk:
             d["TOPS"] = wk["ops"] / t / 1e12
             d["int8_mfma_frac"] = wk["ops"] / t / INT8_PEAK

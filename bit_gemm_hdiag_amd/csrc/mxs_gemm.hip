@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(const int8_t *__restrict__ P
 // at the end. Slices write partial rows that a second kernel adds in slice
 // order, so the result does not depend on scheduling.
 constexpr int kGemvMaxRows = 32;   // decode path: up to 32 tokens
-constexpr int kGemvVecRows = 4;    // up to 4 tokens on the vector ALU, above on the matrix cores
+constexpr int kGemvVecRows = 8;    // up to 8 tokens on the vector ALU, above on the matrix cores
 constexpr int kGemvPitch = 144;     // 8-bit and 4-bit tiles: 128 bytes + 16 (conflict-free b128 reads)
 constexpr int kGemvPitch6 = 104;    // 6-bit tile: 96 bytes + 8 (conflict-free b64 reads)
 constexpr int kGemvTile = 64 * kGemvPitch;
@@ -1691,7 +1691,8 @@ hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t l
     if (M > kGemvVecRows) return launch_decode(A, W, Y, ldy, ws, st);
     if (M <= 1) return launch_gemv_t<1>(A, W, Y, ldy, ws, st);
     if (M <= 2) return launch_gemv_t<2>(A, W, Y, ldy, ws, st);
-    return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
+    if (M <= 4) return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
+    return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
 }
 
 // Prefill workspace: the two prepared operands, record-aligned.

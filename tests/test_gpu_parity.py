@@ -221,9 +221,11 @@ def test_mixed_gemm(mx, orc, M, N, K, budget, entry):
 
 @pytest.mark.parametrize("M,N,K,budget", [(1, 65, 32, (0, 0)), (2, 130, 512, (10000, 0)), (3, 64, 352, (0, 10000)),
                                           (4, 200, 480, (3100, 4000)), (4, 1000, 4096, (500, 1500)),
-                                          (2, 77, 1056, (300, 1000)), (1, 129, 800, (800, 2000))])
+                                          (2, 77, 1056, (300, 1000)), (1, 129, 800, (800, 2000)),
+                                          (6, 150, 2048, (500, 1500)), (8, 70, 544, (3100, 4000)),
+                                          (5, 64, 96, (0, 0))])
 def test_mixed_gemm_vector_decode(mx, orc, M, N, K, budget):
-    # the vector decode kernel (up to 4 tokens): one-slice and many-slice
+    # the vector decode kernel (up to 8 tokens): one-slice and many-slice
     # cases, single-width budgets, partial slices and ragged row tiles
     gemm_case(mx, orc, M, N, K, budget, seed=M * 11 + N)
 
