@@ -63,6 +63,9 @@ def _load():
                                       P, c_int64, P, c_int64, P, c_int64, P, c_int64,
                                       P, c_int64, P]
         lib.or_quantize_kv.argtypes = [P, c_int64, c_int64, c_int64, P, P]
+        lib.or_allocate_blocks.argtypes = [P, c_int64, c_int32, c_int32, P, P]
+        lib.or_output_error.argtypes = [P, c_int64, c_int64, c_int64, P, c_int64, c_int64, P, c_int64, P]
+        lib.or_layer_budget.argtypes = [c_int32, P, P, P, c_double, P, P]
         _lib = lib
     return _lib
 
@@ -138,6 +141,16 @@ def allocate(score_, bp8: int, bp6: int):
 
 
 # -- section 7: quantize + pack ------------------------------------------------
+def allocate_blocks(score_, n8: int, n6: int):
+    """allocate() with the block counts given instead of the budget."""
+    sc = np.ascontiguousarray(score_, dtype=np.float64)
+    K = sc.shape[0]
+    bits = np.zeros(K, np.uint8)
+    perm = np.zeros(K, np.int32)
+    _check(_load().or_allocate_blocks(_ptr(sc), K, n8, n6, _ptr(bits), _ptr(perm)), "allocate_blocks")
+    return bits, perm
+
+
 def quantize(X, perm, n8: int, n6: int, n4: int):
     """Planes dict(q8 int8[R,32 n8], q6 uint8[R,24 n6], q4 uint8[R,16 n4], sc uint8[R,nb])."""
     X = _f32(X)
@@ -201,3 +214,29 @@ def quantize_kv(kv):
     scales = np.zeros((T, H, D // BLOCK), np.uint8)
     _check(_load().or_quantize_kv(_ptr(kv), T, H, D, _ptr(codes), _ptr(scales)), "quantize_kv")
     return codes, scales
+
+
+# -- section 11: layer-wise allocation ----------------------------------------
+def output_error(X, W, Yq):
+    """sum over (t, n) of (X W^T - Yq)^2 in fp64 (X [M, K], W [N, K] float32,
+    Yq [M, N] any float)."""
+    X, W = _f32(X), _f32(W)
+    Yq = np.ascontiguousarray(Yq, dtype=np.float64)
+    M, K = X.shape
+    N = W.shape[0]
+    err = np.zeros(1, np.float64)
+    _check(_load().or_output_error(_ptr(X), M, K, K, _ptr(W), N, K, _ptr(Yq), N, _ptr(err)), "output_error")
+    return float(err[0])
+
+
+def layer_budget(S, rows, K, B: float):
+    """(blocks int32[L, 3] = (n8, n6, n4) per layer, R) for layer
+    sensitivities S, weight rows and columns per layer and average width B."""
+    S = np.ascontiguousarray(S, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    K = np.ascontiguousarray(K, dtype=np.int64)
+    L = S.shape[0]
+    out = np.zeros((L, 3), np.int32)
+    R = np.zeros(1, np.float64)
+    _check(_load().or_layer_budget(L, _ptr(S), _ptr(rows), _ptr(K), float(B), _ptr(out), _ptr(R)), "layer_budget")
+    return out, float(R[0])

@@ -280,12 +280,13 @@ static int or_rank_cmp(const void *a, const void *b)
     return i < j ? -1 : (i > j);           /* then smaller index */
 }
 
-int or_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6,
-                uint8_t *bits, int32_t *perm)
+/* the same with the block counts given (n8 blocks of 8 bits, n6 of 6) */
+int or_allocate_blocks(const double *score, int64_t K, int32_t n8, int32_t n6,
+                       uint8_t *bits, int32_t *perm)
 {
-    int32_t nb3[3];
-    if (!score || !bits || !perm) return -1;
-    if (or_budget_blocks(K, bp8, bp6, nb3)) return -1;
+    if (!score || !bits || !perm || K < OR_BLOCK || K % OR_BLOCK) return -1;
+    if (n8 < 0 || n6 < 0 || (int64_t)n8 + n6 > K / OR_BLOCK) return -1;
+    const int32_t nb3[2] = {n8, n6};
     int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
     if (!order) return -1;
     for (int64_t k = 0; k < K; ++k) order[k] = (int32_t)k;
@@ -301,6 +302,14 @@ int or_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6,
             if (bits[k] == cls[c]) perm[j++] = (int32_t)k;
     free(order);
     return 0;
+}
+
+int or_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6,
+                uint8_t *bits, int32_t *perm)
+{
+    int32_t nb3[3];
+    if (or_budget_blocks(K, bp8, bp6, nb3)) return -1;
+    return or_allocate_blocks(score, K, nb3[0], nb3[1], bits, perm);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -487,4 +496,117 @@ int or_quantize_kv(const float *kv, int64_t T, int64_t H, int64_t D,
     if (!kv || !codes || !scales || T < 0 || H < 1 || D < OR_BLOCK || D % OR_BLOCK) return -1;
     return or_quantize(kv, T * H, D, D, NULL, 0, 0, (int32_t)(D / OR_BLOCK), NULL, 0, NULL, 0,
                        codes, D / 2, scales, D / OR_BLOCK);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 11. Layer-wise allocation under a global control parameter R              */
+/* ------------------------------------------------------------------------ */
+/*
+ * [NL] §2.1 ("Laaggewijze sensitiviteit"): a layer's sensitivity is the L2
+ * error at the model output when that layer alone is quantized. [NL] §2.3:
+ * widths are assigned under a target average bitwidth B with one global
+ * parameter R; every layer keeps its 32 most sensitive columns at 8 bits,
+ * and its number of 6-bit columns is proportional to its sensitivity,
+ * scaled by R so that the global average meets B.
+ *
+ * Reading (the model output needs a trained model, which is not built):
+ *   S_l = || X W^T - Q4(X) Q4(W)^T ||_F^2 over calibration tokens X, with Q4
+ *         uniform MXINT4 on both operands (the layer quantized on its own);
+ *   n8_l = 1,  n6_l = min(nb_l - 1, floor(R S_l + 1/2))  (whole blocks),
+ *   R = the largest value whose average over all weights (each layer
+ *       weighted by rows_l * K_l, mantissa bits only) does not exceed B.
+ * The average is a step function of R that jumps where R S_l = j - 1/2; R
+ * is found by bisection over those breakpoints: in ascending order (ties
+ * taken together), a breakpoint is accepted while the extra bits it adds
+ * still fit; the first that does not fit ends the search. The budget in
+ * extra bits above 4 is floor((B - 4) * sum_l rows_l K_l).
+ */
+
+/* sum_{t,n} (sum_k X[t,k] W[n,k] - Yq[t,n])^2: fp64, t then n ascending */
+int or_output_error(const float *X, int64_t M, int64_t K, int64_t ldx,
+                    const float *W, int64_t N, int64_t ldw,
+                    const double *Yq, int64_t ldy, double *err)
+{
+    if (!X || !W || !Yq || !err || M < 0 || N < 0 || K < 1 || ldx < K || ldw < K || ldy < N) return -1;
+    double *row = (double *)malloc(sizeof(double) * (size_t)(N + 1));
+    if (!row) return -1;
+    double total = 0.0;
+    for (int64_t t = 0; t < M; ++t) {
+        #pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += (double)X[t * ldx + k] * (double)W[n * ldw + k];
+            row[n] = acc;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            const double d = row[n] - Yq[t * ldy + n];
+            total += d * d;
+        }
+    }
+    free(row);
+    *err = total;
+    return 0;
+}
+
+typedef struct {
+    double key;     /* (j - 1/2) / S_l */
+    int32_t layer;
+    int32_t j;
+} or_bp;
+
+static int or_bp_cmp(const void *a, const void *b)
+{
+    const or_bp *x = (const or_bp *)a, *y = (const or_bp *)b;
+    if (x->key != y->key) return x->key < y->key ? -1 : 1;
+    if (x->layer != y->layer) return x->layer < y->layer ? -1 : 1;
+    return x->j < y->j ? -1 : (x->j > y->j);
+}
+
+int or_layer_budget(int32_t L, const double *S, const int64_t *rows, const int64_t *K, double B,
+                    int32_t *nblk /* [L][3] */, double *R_out)
+{
+    if (L < 1 || !S || !rows || !K || !nblk || !(B >= 4.0) || !(B <= 8.0)) return -1;
+    double total = 0.0, need8 = 0.0;
+    int64_t nbp = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        if (rows[l] < 1 || K[l] < OR_BLOCK || K[l] % OR_BLOCK || !(S[l] >= 0.0) || isinf(S[l])) return -1;
+        total += (double)rows[l] * (double)K[l];
+        need8 += 4.0 * OR_BLOCK * (double)rows[l];      /* one 8-bit block: +4 bits on 32 columns */
+        if (S[l] > 0.0) nbp += K[l] / OR_BLOCK - 1;
+    }
+    const double allowed = floor((B - 4.0) * total);
+    if (need8 > allowed) return -1;
+    or_bp *bp = (or_bp *)malloc(sizeof(or_bp) * (size_t)(nbp + 1));
+    if (!bp) return -1;
+    int64_t c = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        nblk[3 * l] = 1;
+        nblk[3 * l + 1] = 0;
+        if (S[l] > 0.0)
+            for (int32_t j = 1; j < K[l] / OR_BLOCK; ++j) {
+                bp[c].key = ((double)j - 0.5) / S[l];
+                bp[c].layer = l;
+                bp[c].j = j;
+                ++c;
+            }
+    }
+    qsort(bp, (size_t)nbp, sizeof(or_bp), or_bp_cmp);
+    double used = need8, R = 0.0;
+    for (int64_t i = 0; i < nbp;) {
+        int64_t e = i;
+        double add = 0.0;
+        while (e < nbp && bp[e].key == bp[i].key) {       /* a group of equal breakpoints */
+            add += 2.0 * OR_BLOCK * (double)rows[bp[e].layer];   /* 6-bit block: +2 bits on 32 columns */
+            ++e;
+        }
+        if (used + add > allowed) break;
+        used += add;
+        R = bp[i].key;
+        for (int64_t q = i; q < e; ++q) nblk[3 * bp[q].layer + 1] = bp[q].j;
+        i = e;
+    }
+    for (int32_t l = 0; l < L; ++l) nblk[3 * l + 2] = (int32_t)(K[l] / OR_BLOCK) - 1 - nblk[3 * l + 1];
+    if (R_out) *R_out = R;
+    free(bp);
+    return 0;
 }
