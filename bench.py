@@ -28,6 +28,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --overhead     (mixed_gemm under the all-4-bit, 4.03-bit,
                                        binary 4/8 and 5/15/80 % maps, prefill and
                                        decode: one JSON line per map)
+       python bench.py --layerwise    (layer sensitivities and the layer-wise budget
+                                       for the seven linear layers of a 70B block)
        python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
                                        and 32 tokens: one JSON line per case, GB/s
                                        of packed W + scale bytes against HBM peak,
@@ -158,6 +160,59 @@ def overhead_cases(mx, synth, torch, reps=20):
             print(json.dumps(out), flush=True)
             del Wq, Aq, Y
         del W, X
+
+
+FP32_MFMA_PEAK = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
+
+
+def layerwise_cases(mx, synth, torch, T=256, B=4.5, reps=10):
+    """Layer-wise allocation for the seven linear layers of one 70B block:
+    each layer's sensitivity S (uniform-MXINT4 output error on T calibration
+    tokens: two quantize calls, the mixed GEMM and mxs_output_error), then
+    mxs_layer_budget at average width B. The output-error kernel is timed
+    against the fp32 matrix-core peak (2 T N K flops of the dense product)."""
+    dev = torch.device("cuda:0")
+    layers = [("q_proj", 8192, 8192), ("k_proj", 1024, 8192), ("v_proj", 1024, 8192), ("o_proj", 8192, 8192),
+              ("gate_proj", 28672, 8192), ("up_proj", 28672, 8192), ("down_proj", 8192, 28672)]
+    S, rows, Ks = [], [], []
+    for i, (name, N, K) in enumerate(layers):
+        seed = 6000 + 16 * i
+        inp = {"q_proj": 0, "k_proj": 0, "v_proj": 0, "o_proj": 1, "gate_proj": 2, "up_proj": 2, "down_proj": 3}[name]
+        gains = synth.outlier_gains(K, 6000 + 16 * inp + synth.ROLE_CHANNELS)
+        X = synth.activations(T, K, 6000 + 16 * inp + synth.ROLE_CALIB, gains, device=dev)
+        W = synth.weights(N, K, seed + synth.ROLE_W, device=dev)
+        nb = K // 32
+        A4 = mx.qmat_alloc(T, K, 0, 0, nb, dev)
+        W4 = mx.qmat_alloc(N, K, 0, 0, nb, dev)
+        Yq = torch.empty((T, N), dtype=torch.float32, device=dev)
+        ws_g = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(A4, W4)), dtype=torch.uint8, device=dev)
+        err = torch.empty(1, dtype=torch.float64, device=dev)
+        ws_e = torch.empty(mx.mxs_output_error_workspace(T, N), dtype=torch.uint8, device=dev)
+
+        def pipeline():
+            mx.mxs_quantize(X, None, 0, 0, nb, out=A4)
+            mx.mxs_quantize(W, None, 0, 0, nb, out=W4)
+            mx.mxs_mixed_gemm(A4, W4, Yq, ws=ws_g)
+            mx.mxs_output_error(X, W, Yq, err=err, ws=ws_e)
+
+        pipeline()
+        s_l = err.cpu().item()
+        t_err = time_graph(torch, lambda: mx.mxs_output_error(X, W, Yq, err=err, ws=ws_e), reps)
+        t_all = time_graph(torch, pipeline, reps)
+        flops = 2 * T * N * K
+        S.append(s_l); rows.append(N); Ks.append(K)
+        print(json.dumps({"case": "layerwise 70B block", "layer": name, "N": N, "K": K, "tokens": T, "S": s_l,
+                          "output_error_us": t_err * 1e6, "output_error_TFLOPs": flops / t_err / 1e12,
+                          "fp32_mfma_frac": flops / t_err / FP32_MFMA_PEAK, "sensitivity_us": t_all * 1e6}),
+              flush=True)
+        del X, W, A4, W4, Yq
+    t0 = time.perf_counter()
+    blocks, R = mx.mxs_layer_budget(S, rows, Ks, B)
+    t_budget = time.perf_counter() - t0
+    bits = sum(r * 32 * (8 * b[0] + 6 * b[1] + 4 * b[2]) for r, b in zip(rows, blocks))
+    print(json.dumps({"case": "layerwise 70B block budget", "B": B, "R": R, "blocks": blocks,
+                      "avg_bits": bits / sum(r * k for r, k in zip(rows, Ks)), "host_us": t_budget * 1e6}),
+          flush=True)
 
 
 def build_workload(mx, synth, torch, dev):
@@ -331,6 +386,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--overhead", action="store_true")
+    ap.add_argument("--layerwise", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -349,6 +405,9 @@ def main():
         return
     if args.overhead:
         overhead_cases(mx, synth, torch)
+        return
+    if args.layerwise:
+        layerwise_cases(mx, synth, torch)
         return
 
     dev = torch.device("cuda:0")

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
 from dataclasses import dataclass
 
 import torch
@@ -62,6 +62,11 @@ def _load():
         "mxs_mixed_gemm_mx_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
         "mxs_mixed_gemm_mx": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
         "mxs_quantize_kv": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, P]),
+        "mxs_allocate_blocks": (S, [P, c_int64, c_int32, c_int32, P, P, P]),
+        "mxs_output_error_workspace": (c_size_t, [c_int64, c_int64]),
+        "mxs_output_error": (S, [P, P, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64, P, c_int64, P, P,
+                                 c_size_t, P]),
+        "mxs_layer_budget": (S, [c_int32, P, P, P, c_double, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -73,7 +78,8 @@ _lib = _load()
 EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_blocks",
             "mxs_calibrate_workspace", "mxs_score_workspace", "mxs_calibrate", "mxs_score",
             "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
-            "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv")
+            "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv", "mxs_allocate_blocks",
+            "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget")
 
 
 def _check(status: int, where: str):
@@ -292,3 +298,57 @@ def mxs_quantize_kv(kv: torch.Tensor, codes=None, scales=None):
     _check(_lib.mxs_quantize_kv(kv.data_ptr(), _dtype(kv), T, H, D, _ptr(codes), _ptr(scales),
                                 _stream(kv.device)), "mxs_quantize_kv")
     return codes, scales
+
+
+# ------------------------------------------------------------ layer-wise budget
+def mxs_allocate_blocks(score: torch.Tensor, n8: int, n6: int, bits=None, perm=None):
+    """mxs_allocate with the block counts given: (bits, perm)."""
+    if not score.is_cuda or score.dtype != torch.float64 or not score.is_contiguous():
+        raise ValueError("score must be a contiguous fp64 GPU tensor")
+    K = score.numel()
+    if bits is None:
+        bits = torch.empty(K, dtype=torch.uint8, device=score.device)
+    if perm is None:
+        perm = torch.empty(K, dtype=torch.int32, device=score.device)
+    _check(_lib.mxs_allocate_blocks(score.data_ptr(), K, n8, n6, bits.data_ptr(), perm.data_ptr(),
+                                    _stream(score.device)), "mxs_allocate_blocks")
+    return bits, perm
+
+
+def mxs_output_error_workspace(M: int, N: int) -> int:
+    return int(_lib.mxs_output_error_workspace(M, N))
+
+
+def mxs_output_error(X: torch.Tensor, W: torch.Tensor, Yq: torch.Tensor, err=None, ws=None) -> torch.Tensor:
+    """err (fp64 [1] on the GPU) = sum over (t, n) of (X W^T - Yq)^2."""
+    px, ldx = _dev2d(X, "X")
+    pw, ldw = _dev2d(W, "W")
+    py, ldy = _dev2d(Yq, "Yq")
+    if X.dtype != W.dtype:
+        raise TypeError("X and W must have the same element type")
+    if Yq.dtype != torch.float32:
+        raise TypeError("Yq must be fp32")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(Yq.shape) != (M, N):
+        raise ValueError("shapes do not match: X [M, K], W [N, K], Yq [M, N]")
+    if err is None:
+        err = torch.empty(1, dtype=torch.float64, device=X.device)
+    p, n = _workspace(mxs_output_error_workspace(M, N), X.device, ws)
+    _check(_lib.mxs_output_error(px, pw, _dtype(X), M, N, K, ldx, ldw, py, ldy, err.data_ptr(), p, n,
+                                 _stream(X.device)), "mxs_output_error")
+    return err
+
+
+def mxs_layer_budget(S, rows, K, B: float):
+    """(blocks [L][3] as (n8, n6, n4) lists, R) for layer sensitivities S."""
+    L = len(S)
+    s_arr = (ctypes.c_double * L)(*[float(x) for x in S])
+    r_arr = (c_int64 * L)(*[int(x) for x in rows])
+    k_arr = (c_int64 * L)(*[int(x) for x in K])
+    out = (c_int32 * (3 * L))()
+    R = c_double(0.0)
+    _check(_lib.mxs_layer_budget(L, ctypes.cast(s_arr, c_void_p), ctypes.cast(r_arr, c_void_p),
+                                 ctypes.cast(k_arr, c_void_p), float(B), ctypes.cast(out, c_void_p),
+                                 ctypes.byref(R)), "mxs_layer_budget")
+    return [[out[3 * i], out[3 * i + 1], out[3 * i + 2]] for i in range(L)], R.value

@@ -2,6 +2,7 @@
 // workspace sizing and kernel launches on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <math.h>
 #include <string.h>
 
 #include "mxs_internal.h"
@@ -135,6 +136,51 @@ mxs_status mxs_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6
     if (!score || !bits || !perm) return fail(MXS_ERR_ARG, "allocate: NULL pointer");
     if (K > 131072) return fail(MXS_ERR_UNSUPPORTED, "allocate: K=%lld above 131072", (long long)K);
     return device_status(mxs::launch_allocate(score, K, 32 * nb3[0], 32 * nb3[1], bits, perm, stream), "allocate");
+}
+
+mxs_status mxs_allocate_blocks(const double *score, int64_t K, int32_t n8, int32_t n6, uint8_t *bits,
+                               int32_t *perm, hipStream_t stream) {
+    if (K <= 0 || K % 32) return fail(MXS_ERR_SHAPE, "allocate_blocks: K=%lld must be a positive multiple of 32", (long long)K);
+    if (n8 < 0 || n6 < 0 || (int64_t)n8 + n6 > K / 32)
+        return fail(MXS_ERR_BUDGET, "allocate_blocks: n8=%d n6=%d outside 0..K/32=%lld", n8, n6, (long long)(K / 32));
+    if (!score || !bits || !perm) return fail(MXS_ERR_ARG, "allocate_blocks: NULL pointer");
+    if (K > 131072) return fail(MXS_ERR_UNSUPPORTED, "allocate_blocks: K=%lld above 131072", (long long)K);
+    return device_status(mxs::launch_allocate(score, K, 32 * n8, 32 * n6, bits, perm, stream), "allocate_blocks");
+}
+
+mxs_status mxs_layer_budget(int32_t L, const double *S, const int64_t *rows, const int64_t *K, double B,
+                            int32_t *nblk, double *R) {
+    if (L < 1 || !S || !rows || !K || !nblk) return fail(MXS_ERR_ARG, "layer_budget: L < 1 or NULL pointer");
+    for (int32_t l = 0; l < L; ++l) {
+        if (!(S[l] >= 0.0) || S[l] == HUGE_VAL) return fail(MXS_ERR_ARG, "layer_budget: S[%d] is negative or not finite", l);
+        if (rows[l] < 1 || K[l] < 32 || K[l] % 32)
+            return fail(MXS_ERR_SHAPE, "layer_budget: layer %d has rows=%lld K=%lld", l, (long long)rows[l], (long long)K[l]);
+    }
+    if (!(B >= 4.0 && B <= 8.0)) return fail(MXS_ERR_BUDGET, "layer_budget: B=%g outside [4, 8]", B);
+    if (mxs::layer_budget(L, S, rows, K, B, nblk, R))
+        return fail(MXS_ERR_BUDGET, "layer_budget: B=%g cannot pay for one 8-bit block per layer", B);
+    return ok();
+}
+
+size_t mxs_output_error_workspace(int64_t M, int64_t N) {
+    return mxs::output_error_workspace(M > 0 ? M : 0, N > 0 ? N : 0);
+}
+
+mxs_status mxs_output_error(const void *X, const void *W, mxs_dtype dtype, int64_t M, int64_t N, int64_t K,
+                            int64_t ldx, int64_t ldw, const float *Yq, int64_t ldy, double *err, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "output_error: unknown dtype %d", (int)dtype);
+    if (M < 0 || N < 0 || K < 32 || K % 32 || ldx < K || ldw < K || ldy < N)
+        return fail(MXS_ERR_SHAPE, "output_error: M=%lld N=%lld K=%lld ldx=%lld ldw=%lld ldy=%lld", (long long)M,
+                    (long long)N, (long long)K, (long long)ldx, (long long)ldw, (long long)ldy);
+    if (!err || !ws || (M > 0 && !X) || (N > 0 && !W) || (M > 0 && N > 0 && !Yq))
+        return fail(MXS_ERR_ARG, "output_error: NULL pointer");
+    const size_t es = dtype == MXS_BF16 ? 2 : 4;
+    if ((M > 0 && (!aligned(X, 16) || (ldx * es) % 16)) || (N > 0 && (!aligned(W, 16) || (ldw * es) % 16)))
+        return fail(MXS_ERR_UNSUPPORTED, "output_error: X and W rows need 16-byte alignment");
+    if (ws_bytes < mxs::output_error_workspace(M, N)) return fail(MXS_ERR_WORKSPACE, "output_error: workspace too small");
+    return device_status(mxs::launch_output_error(X, W, dtype, M, N, K, ldx, ldw, Yq, ldy, err, ws, stream),
+                         "output_error");
 }
 
 mxs_status mxs_quantize(const void *X, mxs_dtype dtype, int64_t ldx, const int32_t *perm,

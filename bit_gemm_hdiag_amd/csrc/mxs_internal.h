@@ -39,4 +39,12 @@ size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W);
 hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
                                 void *ws, size_t ws_bytes, hipStream_t st);
 
+// layer sensitivity and layer-wise budget (mxs_layerwise.hip)
+size_t output_error_workspace(int64_t M, int64_t N);
+hipError_t launch_output_error(const void *X, const void *W, mxs_dtype dtype, int64_t M, int64_t N, int64_t K,
+                               int64_t ldx, int64_t ldw, const float *Yq, int64_t ldy, double *err, void *ws,
+                               hipStream_t st);
+int layer_budget(int32_t L, const double *S, const int64_t *rows, const int64_t *K, double B, int32_t *nblk,
+                 double *R_out);
+
 }  // namespace mxs

@@ -164,6 +164,62 @@ mxs_status mxs_allocate(const double *score, int64_t K, int32_t bp8, int32_t bp6
                         uint8_t *bits, int32_t *perm, hipStream_t stream);
 
 /*
+ * mxs_allocate with the block counts given instead of the budget: the first
+ * 32 n8 ranked columns get 8 bits, the next 32 n6 6 bits, the rest 4 bits
+ * (for a layer-wise budget from mxs_layer_budget). Same ranking, bit map,
+ * permutation, layout and stream semantics as mxs_allocate.
+ * Errors: MXS_ERR_ARG (NULL), MXS_ERR_SHAPE (K % 32), MXS_ERR_BUDGET
+ * (n8, n6 < 0 or n8 + n6 > K/32), MXS_ERR_UNSUPPORTED (K > 131072),
+ * MXS_ERR_DEVICE.
+ */
+mxs_status mxs_allocate_blocks(const double *score, int64_t K, int32_t n8, int32_t n6,
+                               uint8_t *bits, int32_t *perm, hipStream_t stream);
+
+/*
+ * Layer sensitivity ([NL] §2.1, layer-wise sensitivity: the output error
+ * when one layer alone is quantized). Reading: without a trained model the
+ * model-output error is replaced by the layer's own output error on
+ * calibration tokens,
+ *     err = sum_{t,n} (sum_k X[t,k] W[n,k] - Yq[t,n])^2,
+ * where Yq is the product of the quantized operands from mxs_mixed_gemm
+ * (uniform MXINT4 on both for the layer sensitivity S of mxs_layer_budget).
+ * The product is formed on the fp32 matrix cores (bf16 inputs widen
+ * exactly; each element carries at most the rounding of a K-term fp32 sum),
+ * the squared differences are summed in fp64 in a fixed order, so the
+ * result is deterministic. A calibration-time call.
+ * X: [M, ldx], W: [N, ldw], both of `dtype`, rows 16-byte aligned; Yq:
+ * [M, ldy] fp32; err: one fp64 on the device (written). ws >=
+ * mxs_output_error_workspace(M, N) bytes. All device pointers, owned by
+ * the caller; asynchronous on `stream`.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (M or N < 0, K % 32, ld too small),
+ * MXS_ERR_UNSUPPORTED (alignment), MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+size_t mxs_output_error_workspace(int64_t M, int64_t N);
+mxs_status mxs_output_error(const void *X, const void *W, mxs_dtype dtype, int64_t M, int64_t N,
+                            int64_t K, int64_t ldx, int64_t ldw, const float *Yq, int64_t ldy,
+                            double *err, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Layer-wise budget under one global control parameter R ([NL] §2.3: the
+ * 32 most sensitive columns of every layer get 8 bits; a layer's number of
+ * 6-bit columns is proportional to its sensitivity, scaled by R so that the
+ * average width meets the target B). Reading: layer l gets n8 = 1 and
+ * n6 = min(nb_l - 1, floor(R S_l + 1/2)) blocks (nb_l = K_l / 32), for the
+ * largest R whose average mantissa width over all weights (layer l weighted
+ * by rows_l K_l) does not exceed B; the budget in bits above 4 is
+ * floor((B - 4) sum_l rows_l K_l). R is found exactly, by bisection over
+ * the breakpoints R S_l = j - 1/2 (equal breakpoints taken together).
+ * Host call: S, rows, K: [L] host arrays (S_l >= 0 finite, e.g. from
+ * mxs_output_error); nblk: [L][3] host out (n8, n6, n4 per layer); R: host
+ * out, may be NULL.
+ * Errors: MXS_ERR_ARG (NULL, L < 1, S negative or not finite),
+ * MXS_ERR_SHAPE (rows < 1, K % 32), MXS_ERR_BUDGET (B outside [4, 8] or
+ * too small for one 8-bit block per layer).
+ */
+mxs_status mxs_layer_budget(int32_t L, const double *S, const int64_t *rows, const int64_t *K,
+                            double B, int32_t *nblk, double *R);
+
+/*
  * MXINT quantisation of weights or activations ([NL] §1: one shared
  * power-of-two scale per block of 32; §2.2: 4/6/8-bit mantissas; [RP]
  * "Triplet Quantization": weights and activations). Row r, permuted block b

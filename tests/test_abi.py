@@ -152,3 +152,77 @@ def test_quantize_and_gemm_errors(lib):
     kv.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
     assert kv(FAKE, 1, 4, 8, 100, FAKE, FAKE, None) == -2
     assert kv(None, 1, 4, 8, 128, FAKE, FAKE, None) == -1
+
+
+def test_layer_budget_matches_oracle(mx, orc):
+    # host code: the library's solution for R must equal the oracle's exactly
+    rng = np.random.default_rng(21)
+    for _ in range(400):
+        L = int(rng.integers(1, 9))
+        K = (32 * rng.integers(1, 300, L)).astype(np.int64)
+        rows = rng.integers(1, 30000, L).astype(np.int64)
+        S = rng.lognormal(0.0, 2.0, L) * rng.choice([1.0, 0.0], L, p=[0.9, 0.1])
+        if rng.random() < 0.2:
+            S[:] = S[0]                                   # equal sensitivities: grouped breakpoints
+        total = float(np.sum(rows * K))
+        lo = 4.0 + float(np.sum(128 * rows)) / total
+        B = float(rng.uniform(lo, 8.0))
+        want, R = orc.layer_budget(S, rows, K, B)
+        got, gR = mx.mxs_layer_budget(S, rows, K, B)
+        assert got == want.tolist() and gR == R
+
+
+def test_layer_budget_errors(mx, lib):
+    P = ctypes.c_void_p
+    S = (ctypes.c_double * 2)(1.0, 2.0)
+    rows = (ctypes.c_int64 * 2)(10, 10)
+    K = (ctypes.c_int64 * 2)(64, 96)
+    out = (ctypes.c_int32 * 6)()
+    f = lib.mxs_layer_budget
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_double, P, P]
+    c = lambda x: ctypes.cast(x, P)
+    assert f(2, c(S), c(rows), c(K), 6.0, c(out), None) == 0
+    assert f(0, c(S), c(rows), c(K), 6.0, c(out), None) == -1
+    assert f(2, None, c(rows), c(K), 6.0, c(out), None) == -1
+    assert f(2, c(S), c(rows), c(K), 3.9, c(out), None) == -3
+    assert f(2, c(S), c(rows), c(K), 4.1, c(out), None) == -3      # cannot pay the 8-bit blocks
+    K[1] = 100
+    assert f(2, c(S), c(rows), c(K), 6.0, c(out), None) == -2
+    K[1] = 96
+    S[0] = float("nan")
+    assert f(2, c(S), c(rows), c(K), 6.0, c(out), None) == -1
+    S[0] = float("inf")
+    assert f(2, c(S), c(rows), c(K), 6.0, c(out), None) == -1
+    with pytest.raises(mx.MxsError):
+        mx.mxs_layer_budget([1.0, -1.0], [1, 1], [64, 64], 6.0)
+
+
+def test_output_error_and_allocate_blocks_errors(lib):
+    P = ctypes.c_void_p
+    f = lib.mxs_output_error
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
+    lib.mxs_output_error_workspace.restype = ctypes.c_size_t
+    lib.mxs_output_error_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert lib.mxs_output_error_workspace(130, 70) == 3 * 2 * 8
+    fake = P(4096)          # never dereferenced: every call below fails validation
+    need = lib.mxs_output_error_workspace(64, 64)
+    assert f(fake, fake, 7, 64, 64, 64, 64, 64, fake, 64, fake, fake, need, None) == -1     # dtype
+    assert f(fake, fake, 0, 64, 64, 48, 64, 64, fake, 64, fake, fake, need, None) == -2     # K % 32
+    assert f(fake, fake, 0, 64, 64, 64, 32, 64, fake, 64, fake, fake, need, None) == -2     # ldx < K
+    assert f(fake, fake, 0, 64, 64, 64, 64, 64, fake, 63, fake, fake, need, None) == -2     # ldy < N
+    assert f(None, fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, fake, need, None) == -1     # X NULL
+    assert f(fake, fake, 0, 64, 64, 64, 64, 64, fake, 64, None, fake, need, None) == -1     # err NULL
+    assert f(P(4100), fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, fake, need, None) == -6  # alignment
+    assert f(fake, fake, 1, 64, 64, 64, 68, 64, fake, 64, fake, fake, need, None) == -6     # bf16 row pitch
+    assert f(fake, fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, fake, need - 1, None) == -4  # workspace
+    g = lib.mxs_allocate_blocks
+    g.restype = ctypes.c_int32
+    g.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    assert g(fake, 100, 1, 0, fake, fake, None) == -2
+    assert g(fake, 128, 3, 2, fake, fake, None) == -3
+    assert g(fake, 128, -1, 0, fake, fake, None) == -3
+    assert g(None, 128, 1, 0, fake, fake, None) == -1
+    assert g(fake, 262144, 1, 0, fake, fake, None) == -6
