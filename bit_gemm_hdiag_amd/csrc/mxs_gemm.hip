@@ -1338,7 +1338,7 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
 }
 
 // ---------------------------------------------------------------------------
-// Decode with the matrix cores.
+// Decode with the matrix cores (9 to 32 tokens).
 //
 // One v_mfma_i32_32x32x32_i8 yields a 32 token x 32 row tile of exact block
 // sums; the per-block epilogue (convert, scale, accumulate) then runs only
@@ -1347,15 +1347,21 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
 // 6-bit * 4, 4-bit * 16, the factor folded into the scales); W fragments and
 // token fragments are unpacked in registers in the same k order.
 //
-// A workgroup of four waves owns 64 W rows and one K range of 4 * bpw
-// blocks; wave w takes the w-th quarter of it, so the four partial sums of a
-// row meet in LDS (added in wave order) instead of in global memory. W
-// chunks are fetched and staged per wave as in k_gemv; the W scale bytes and
-// the tokens' scales (times the fold factor) of the whole range are staged
-// once per workgroup; the tokens' code fragments are loaded with the W
-// chunk, one chunk ahead. Ranges of different workgroups write partial rows
-// that k_gemv_reduce adds in range order.
-constexpr int kDecMaxBpw = 32;     // blocks per wave (a multiple of 8)
+// The work is cut into the slices of the vector kernel (one width class,
+// two chunks). A workgroup of four waves owns 64 W rows and four consecutive
+// slices, one per wave. A wave issues every load of its slice at once (the
+// W and token scale bytes, both chunks of W codes with the coalesced loads
+// of k_gemv, the tokens' fragments), then stages each W chunk through its
+// own LDS tile into the MFMA layout. The four waves' sums meet in LDS and are
+// added in wave order; slice groups write partial rows that k_gemv_reduce
+// adds in order.
+constexpr int kDecScW = 6;   // dwords of staged W scale bytes per row (20 used)
+
+struct DecWaveLds {          // one wave's LDS
+    uint8_t tile[kGemvTile];          // a staged W chunk
+    uint32_t wsc[64 * kDecScW];       // W scale bytes of the slice, row-major
+    float asc[16 * 32];               // tokens' scales times the fold, [block][token]
+};
 
 // 16 MFMA bytes (one k-half) of a 4-bit block half held as two dwords: the
 // low nibbles of each dword, then its high nibbles, each as code * 16
@@ -1374,42 +1380,30 @@ __device__ __forceinline__ v4i unpack6_half(const uint32_t w[3]) {
     return v4i{(int)wide6(g0), (int)wide6(g1), (int)wide6(g2), (int)wide6(g3)};
 }
 
-struct DecLds {                    // byte offsets into the dynamic LDS
-    int wsc, wsc_pitch, asc, total;
-};
-
-__host__ __device__ inline DecLds dec_lds(int bpw) {
-    DecLds L;
-    L.wsc = 4 * kGemvTile;                     // after the four W tiles
-    L.wsc_pitch = 4 * bpw + 4;                 // bytes per W row (pitch/4 odd: conflict-free dword reads)
-    L.asc = L.wsc + 64 * L.wsc_pitch;
-    L.total = L.asc + 4 * bpw * 32 * 4;        // [block][token] floats
-    return L;
-}
-
 // token fragment loads of one chunk (lane: token l % 32, k-half l / 32).
-// Branch-free: lanes of tokens past M read token 0 and blocks past the chunk
-// read its first block; those values meet zero token scales or are never
-// used.
+// Branch-free: lanes of tokens past M read token 0, blocks past the chunk
+// read its first block and an empty chunk reads the plane's first block;
+// those values meet zero token scales or are never used.
 __device__ __forceinline__ void dec_fetch_a(const QView &A, int32_t M, const GemvChunk &c, int t, int h,
                                             uint32_t RA[16]) {
     const int64_t tr = t < M ? t : 0;
+    const int64_t pb = c.nblk > 0 ? c.pb : 0;   // an empty chunk re-reads the plane's first block
     if (c.cls == 4) {
-        const uint8_t *base = A.q4 + tr * A.ld4 + 16 * (int64_t)c.pb + 8 * h;
+        const uint8_t *base = A.q4 + tr * A.ld4 + 16 * pb + 8 * h;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint2 v = *reinterpret_cast<const uint2 *>(base + 16 * (j < c.nblk ? j : 0));
             RA[2 * j] = v.x; RA[2 * j + 1] = v.y;
         }
     } else if (c.cls == 8) {
-        const int8_t *base = A.q8 + tr * A.ld8 + 32 * (int64_t)c.pb + 16 * h;
+        const int8_t *base = A.q8 + tr * A.ld8 + 32 * pb + 16 * h;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint4 v = *reinterpret_cast<const uint4 *>(base + 32 * (j < c.nblk ? j : 0));
             RA[4 * j] = v.x; RA[4 * j + 1] = v.y; RA[4 * j + 2] = v.z; RA[4 * j + 3] = v.w;
         }
     } else {
-        const uint8_t *base = A.q6 + tr * A.ld6 + 24 * (int64_t)c.pb + 12 * h;
+        const uint8_t *base = A.q6 + tr * A.ld6 + 24 * pb + 12 * h;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t *q = reinterpret_cast<const uint32_t *>(base + 24 * (j < c.nblk ? j : 0));
@@ -1418,106 +1412,79 @@ __device__ __forceinline__ void dec_fetch_a(const QView &A, int32_t M, const Gem
     }
 }
 
-__global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int64_t N, int32_t n8, int32_t n6,
-                                                int32_t nb, int32_t bpw, float *__restrict__ out, int64_t ldo,
-                                                int64_t slice_stride) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dlds[];
-    const DecLds L = dec_lds(bpw);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, h = lane >> 5;
+// One wave's slice (width CLS): loads, then per chunk stage, MFMA and the
+// per-block epilogue into acc (tile i = W rows 32 i .. 32 i + 31).
+template <int CLS>
+__device__ __forceinline__ void dec_body(const QView &A, const QView &W, int32_t M, int64_t N, int32_t nb,
+                                         const GemvChunk &sl, DecWaveLds &L, float acc[2][16]) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * 64;
     const int32_t rows_left = N - row0 < 64 ? (int32_t)(N - row0) : 64;
-    const int32_t g0 = (int32_t)blockIdx.y * 4 * bpw;                  // workgroup range [g0, g1)
-    const int32_t g1 = g0 + 4 * bpw < nb ? g0 + 4 * bpw : nb;
-    const int32_t b0 = g0 + wave * bpw < g1 ? g0 + wave * bpw : g1;     // this wave's quarter
-    const int32_t b1 = b0 + bpw < g1 ? b0 + bpw : g1;
-    const int32_t h6 = n8 + n6;
-    uint8_t *my_tile = dlds + wave * kGemvTile;
-    uint8_t *wsc = dlds + L.wsc;
-    float *asc = reinterpret_cast<float *>(dlds + L.asc);
+    constexpr int bpc = CLS == 4 ? 8 : 4;
+    constexpr float fold = CLS == 8 ? 1.f : (CLS == 6 ? 0.25f : 0.0625f);
 
-    // W scale bytes of the range (aligned dwords: g0 is a multiple of 32)
+    // scale bytes: five W dwords from the one holding block gb (clamped to
+    // the row's last dword), lane = row; token l32's bytes of blocks h + 2 i
+    const int32_t d0 = sl.gb >> 2, dl = (nb - 1) >> 2;
+    uint32_t vw[5], ab[8];
     {
-        const int32_t nd = (g1 - g0 + 3) >> 2;
-        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + row0 * W.lds + g0);
-        const int64_t ldw = W.lds >> 2;
-        for (int it = tid; it < 64 * nd; it += 256) {
-            const int r = it / nd, d = it - r * nd;
-            const uint32_t v = sp[r < rows_left ? r * ldw + d : 0];
-            *reinterpret_cast<uint32_t *>(wsc + r * L.wsc_pitch + 4 * d) = v;
+        const uint32_t *sp = reinterpret_cast<const uint32_t *>(W.sc + (row0 + (lane < rows_left ? lane : 0)) * W.lds);
+#pragma unroll
+        for (int k = 0; k < 5; ++k) vw[k] = sp[min(d0 + k, dl)];
+        const uint8_t *ap = A.sc + (int64_t)(l32 < M ? l32 : 0) * A.lds + sl.gb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = h + 2 * i;
+            ab[i] = ap[j < sl.nblk ? j : 0];
         }
     }
-    // tokens' scales of the range, times the MFMA byte factor's inverse; zero past M
-    for (int it = tid; it < 32 * 4 * bpw; it += 256) {
-        const int t = it & 31, j = it >> 5;
-        const int32_t b = g0 + j;
-        float v = 0.f;
-        if (t < M && b < g1) {
-            const float fold = b < n8 ? 1.f : (b < h6 ? 0.25f : 0.0625f);
-            v = e8m0_to_f32(A.sc[t * A.lds + b]) * fold;
-        }
-        asc[j * 32 + t] = v;
-    }
-
-    uint32_t R[32], RA[16];
-    GemvChunk c = gemv_chunk(b0, b1, n8, h6, nb);
-    const bool work = b0 < b1;
-    if (work) {
-        gemv_fetch(W, row0, rows_left, c, lane, R);
-        dec_fetch_a(A, M, c, l32, h, RA);
-    }
-    __syncthreads();   // scales staged
-
-    float acc[2][16];
+    GemvChunk ch[kVecChunks];
+    uint32_t R[kVecChunks][32], RA[kVecChunks][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < kVecChunks; ++j) {
+        ch[j] = vec_chunk(sl, j);
+        ch[j].cls = CLS;   // known at compile time: folds the width branches of the loads
+        gemv_fetch(W, row0, rows_left, ch[j], lane, R[j]);
+        dec_fetch_a(A, M, ch[j], l32, h, RA[j]);
+    }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < 5; ++k) L.wsc[lane * kDecScW + k] = vw[k];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int j = h + 2 * i;
+        L.asc[j * 32 + l32] = (l32 < M && j < sl.nblk) ? e8m0_to_f32(ab[i]) * fold : 0.f;
+    }
+    const uint8_t *wsb = reinterpret_cast<const uint8_t *>(L.wsc);
     const int qmax = (M + 7) >> 3;
-    const uint32_t *row_sc[2] = {reinterpret_cast<const uint32_t *>(wsc + l32 * L.wsc_pitch),
-                                 reinterpret_cast<const uint32_t *>(wsc + (32 + l32) * L.wsc_pitch)};
-    while (work) {
-        gemv_stage(my_tile, c.cls, lane, R);
-        uint32_t CA[16];
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) CA[i] = RA[i];
+    for (int c = 0; c < kVecChunks; ++c) {
+        if (ch[c].nblk == 0) break;
+        __builtin_amdgcn_wave_barrier();            // the previous chunk's tile reads are done
+        gemv_stage(L.tile, CLS, lane, R[c]);
         __builtin_amdgcn_wave_barrier();
-        const GemvChunk cur = c;
-        const int32_t next = cur.gb + cur.nblk;
-        if (next < b1) {
-            c = gemv_chunk(next, b1, n8, h6, nb);
-            gemv_fetch(W, row0, rows_left, c, lane, R);
-            dec_fetch_a(A, M, c, l32, h, RA);
-        }
-        uint64_t swb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) swb[i] = bytes8(row_sc[i], cur.gb - g0, (next - 1 - g0) >> 2);
-        const float wfold = cur.cls == 8 ? 1.f : (cur.cls == 6 ? 0.25f : 0.0625f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j >= cur.nblk) break;
-            if (cur.cls != 4 && j >= 4) break;
+        for (int j = 0; j < bpc; ++j) {
+            if (j >= ch[c].nblk) break;
             v4i fa, fw[2];
-            if (cur.cls == 4) {
-                fa = unpack4_half(CA[2 * j], CA[2 * j + 1]);
+            if (CLS == 4) {
+                fa = unpack4_half(RA[c][2 * j], RA[c][2 * j + 1]);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(my_tile + (i * 32 + l32) * kGemvPitch + 16 * j + 8 * h);
+                    const uint2 v = *reinterpret_cast<const uint2 *>(L.tile + (i * 32 + l32) * kGemvPitch + 16 * j + 8 * h);
                     fw[i] = unpack4_half(v.x, v.y);
                 }
-            } else if (cur.cls == 8) {
-                fa = v4i{(int)CA[(4 * j) & 15], (int)CA[(4 * j + 1) & 15], (int)CA[(4 * j + 2) & 15], (int)CA[(4 * j + 3) & 15]};
+            } else if (CLS == 8) {
+                fa = v4i{(int)RA[c][4 * j], (int)RA[c][4 * j + 1], (int)RA[c][4 * j + 2], (int)RA[c][4 * j + 3]};
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    fw[i] = *reinterpret_cast<const v4i *>(my_tile + (i * 32 + l32) * kGemvPitch + 32 * j + 16 * h);
+                    fw[i] = *reinterpret_cast<const v4i *>(L.tile + (i * 32 + l32) * kGemvPitch + 32 * j + 16 * h);
             } else {
-                const uint32_t wa[3] = {CA[(3 * j) & 15], CA[(3 * j + 1) & 15], CA[(3 * j + 2) & 15]};
+                const uint32_t wa[3] = {RA[c][3 * j], RA[c][3 * j + 1], RA[c][3 * j + 2]};
                 fa = unpack6_half(wa);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const uint32_t *q = reinterpret_cast<const uint32_t *>(my_tile + (i * 32 + l32) * kGemvPitch6 + 24 * j + 12 * h);
+                    const uint32_t *q = reinterpret_cast<const uint32_t *>(L.tile + (i * 32 + l32) * kGemvPitch6 + 24 * j + 12 * h);
                     const uint32_t w[3] = {q[0], q[1], q[2]};
                     fw[i] = unpack6_half(w);
                 }
@@ -1525,10 +1492,11 @@ __global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int
             v16i I[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) I[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fw[i], zero, 0, 0, 0);
+            const int col = (sl.gb & 3) + c * bpc + j;   // the block's staged scale byte
             float sw[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) sw[i] = e8m0_to_f32((uint32_t)(swb[i] >> (8 * j)) & 0xFFu) * wfold;
-            const float *sa_blk = asc + (cur.gb - g0 + j) * 32;
+            for (int i = 0; i < 2; ++i) sw[i] = e8m0_to_f32(wsb[(i * 32 + l32) * 4 * kDecScW + col]) * fold;
+            const float *sa_blk = L.asc + (c * bpc + j) * 32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (q >= qmax) break;
@@ -1540,13 +1508,40 @@ __global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int
                         acc[i][4 * q + r] = __builtin_fmaf((float)I[i][4 * q + r], sa[r] * sw[i], acc[i][4 * q + r]);
             }
         }
-        if (next >= b1) break;
-        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_decode(QView A, QView W, int32_t M, int64_t N, int32_t n8, int32_t n6,
+                                                int32_t n4, float *__restrict__ out, int64_t ldo,
+                                                int64_t slice_stride) {
+    __shared__ __attribute__((aligned(16))) DecWaveLds lds[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const VecSlices S = vec_slices(n8, n6, n4);
+    const int32_t ns = S.s8 + S.s6 + S.s4, nb = n8 + n6 + n4;
+    const int32_t s = (int32_t)blockIdx.y * 4 + wave;
+
+    float acc[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    if (s < ns) {
+        const GemvChunk sl = vec_slice(s, n8, n6, n4, S);
+        if (sl.cls == 4)
+            dec_body<4>(A, W, M, N, nb, sl, lds[wave], acc);
+        else if (sl.cls == 8)
+            dec_body<8>(A, W, M, N, nb, sl, lds[wave], acc);
+        else
+            dec_body<6>(A, W, M, N, nb, sl, lds[wave], acc);
     }
 
     // the four waves' sums of each output, added in wave order
+    const int qmax = (M + 7) >> 3;
     __syncthreads();
-    float *red = reinterpret_cast<float *>(dlds);   // [wave][q][i][r][lane], the W tiles are free now
+    float *red = reinterpret_cast<float *>(lds);   // [wave][q][i][r][lane], 32 KiB
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (q >= qmax) break;
@@ -1592,10 +1587,6 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ p
     for (; s < ns; ++s) v = v + part[(int64_t)s * stride + i];
     Y[t * ldy + n] = v;
 }
-
-struct GemvPlan {
-    int32_t nslices, bps;
-};
 
 struct PrepLayout {
     int64_t Mp, Np, Kp;
@@ -1650,38 +1641,21 @@ hipError_t launch_gemv_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t
     return hipGetLastError();
 }
 
-// Decode plan: blocks per wave (bpw) and the number of K ranges. Ranges of
-// 4 * bpw blocks; enough workgroups for ~3 per CU, but few enough ranges
-// that the partial rows (8 M N bytes per range, written and read back) stay
-// small next to W.
-GemvPlan decode_plan(const mxs_qmat &A, const mxs_qmat &W) {
-    const int32_t nb = (int32_t)(A.K / 32);
-    const int64_t tiles = ceil_div(W.rows, 64);
-    const int64_t row_bytes = 32 * (int64_t)A.n8 + 24 * (int64_t)A.n6 + 16 * (int64_t)A.n4 + nb;
-    int64_t ns = ceil_div(768, tiles);
-    const int64_t cap = (row_bytes / 8) / (8 * (A.rows > 0 ? A.rows : 1));   // partials <= ~1/8 of W
-    ns = ns > cap ? cap : ns;
-    ns = ns < 1 ? 1 : ns;
-    int32_t bpw = (int32_t)(ceil_div(ceil_div(nb, 4 * ns), 8) * 8);
-    bpw = bpw > kDecMaxBpw ? kDecMaxBpw : bpw;
-    return GemvPlan{(int32_t)ceil_div(nb, 4 * bpw), bpw};
+// slice groups of the matrix-core decode kernel (four slices per workgroup)
+int64_t decode_groups(const mxs_qmat &A) {
+    const VecSlices S = vec_slices(A.n8, A.n6, A.n4);
+    return ceil_div((int64_t)S.s8 + S.s6 + S.s4, 4);
 }
 
 hipError_t launch_decode(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
-    const GemvPlan P = decode_plan(A, W);
-    const int64_t M = A.rows, N = W.rows;
-    const DecLds L = dec_lds(P.bps);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_decode),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(kDecMaxBpw).total);
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)P.nslices);
-    float *dst = P.nslices == 1 ? Y : static_cast<float *>(ws);
-    hipLaunchKernelGGL(k_decode, grid, dim3(256), (size_t)L.total, st, view_of(A), view_of(W), (int32_t)M, N, A.n8,
-                       A.n6, (int32_t)(A.K / 32), P.bps, dst, P.nslices == 1 ? ldy : N,
-                       P.nslices == 1 ? (int64_t)0 : M * N);
-    e = hipGetLastError();
-    if (e != hipSuccess || P.nslices == 1) return e;
-    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, dst, P.nslices,
+    const int64_t M = A.rows, N = W.rows, ng = decode_groups(A);
+    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ng);
+    float *dst = ng == 1 ? Y : static_cast<float *>(ws);
+    hipLaunchKernelGGL(k_decode, grid, dim3(256), 0, st, view_of(A), view_of(W), (int32_t)M, N, A.n8, A.n6, A.n4,
+                       dst, ng == 1 ? ldy : N, ng == 1 ? (int64_t)0 : M * N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ng == 1) return e;
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, dst, (int32_t)ng,
                        (int32_t)M, N, Y, ldy);
     return hipGetLastError();
 }
@@ -1732,7 +1706,7 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
 // Decode (up to 32 tokens) and 33..63 tokens take the same kernels in both
 // entry points; they differ in the prefill kernels only.
 size_t decode_workspace(const mxs_qmat &A, const mxs_qmat &W) {
-    const int64_t ns = A.rows > kGemvVecRows ? decode_plan(A, W).nslices : [&] {
+    const int64_t ns = A.rows > kGemvVecRows ? decode_groups(A) : [&] {
         const VecSlices S = vec_slices(A.n8, A.n6, A.n4);
         return (int64_t)S.s8 + S.s6 + S.s4;
     }();

@@ -223,9 +223,12 @@ def test_mixed_gemm(mx, orc, M, N, K, budget, entry):
                                           (4, 200, 480, (3100, 4000)), (4, 1000, 4096, (500, 1500)),
                                           (2, 77, 1056, (300, 1000)), (1, 129, 800, (800, 2000)),
                                           (6, 150, 2048, (500, 1500)), (8, 70, 544, (3100, 4000)),
-                                          (5, 64, 96, (0, 0))])
+                                          (5, 64, 96, (0, 0)), (9, 70, 544, (3100, 4000)), (16, 130, 96, (0, 0)),
+                                          (31, 64, 2048, (10000, 0)), (24, 200, 352, (0, 10000)),
+                                          (12, 65, 8192, (500, 1500))])
 def test_mixed_gemm_vector_decode(mx, orc, M, N, K, budget):
-    # the vector decode kernel (up to 8 tokens): one-slice and many-slice
+    # the decode kernels (vector up to 8 tokens, matrix cores 9..32): one-slice
+    # and many-slice cases, slice groups with fewer than four slices,
     # cases, single-width budgets, partial slices and ragged row tiles
     gemm_case(mx, orc, M, N, K, budget, seed=M * 11 + N)
 
