@@ -468,8 +468,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
     float acc[2][2][16];
     v16i I[2][2];
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    // two zero B operands the compiler cannot see through, so the four
-    // restart MFMAs stay distinct and write the accumulators in place
+    // two zero B operands the compiler cannot see through, so the restart
+    // MFMAs stay distinct and write the accumulators in place
     v4i zb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -486,7 +486,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
         }
 
-    bool aligned = true;
+    // A block whose integer sums end (the last block of its window, or any
+    // block of a window whose rows are not all aligned) needs an epilogue.
+    // Inside a stage it is left pending: the next block runs it (by then the
+    // block's MFMAs have finished, so the vector ALU does not wait for them),
+    // tile by tile, each tile followed by a restart MFMA that zeroes its
+    // integer sums in place (the matrix core has slack, the vector ALU has
+    // none), then the new block's MFMAs accumulate as usual. The last block of
+    // a stage runs its epilogue at once: the next step's DMA refills the slot
+    // of the stage before the one it computes, so scales cannot be read across
+    // that step. After the loop no DMA follows, so a pending epilogue of the
+    // final stage runs there. pCA / pCW: the pending block's code scales.
+    bool aligned = true, pend = false;
+    const float *pCA = nullptr, *pCW = nullptr;
+    auto load_sa = [&](int i, f32x4_t sa[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sa[q] = *reinterpret_cast<const f32x4_t *>(pCA + i * 32 + 8 * q + 4 * h);
+    };
+    auto epi = [&](int i, int j, const f32x4_t sa[4]) {
+        const float cw = __builtin_fabsf(pCW[j * 32 + l32]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i][j][4 * q + e] =
+                    __builtin_fmaf((float)I[i][j][4 * q + e], __builtin_fabsf(sa[q][e]) * cw, acc[i][j][4 * q + e]);
+    };
     auto compute = [&](int st, const int8_t *sbase) {
         const float *sCA = reinterpret_cast<const float *>(sbase + kDStA + kDStW);
         const float *sCW = sCA + kDSB * kGBM;
@@ -519,35 +544,40 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
                 const float vw = sCW[blk * kGBN + wn * 64 + lane];
                 aligned = __all(va > 0.f && vw > 0.f);
             }
+            if (pend) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    f32x4_t sa[4];
+                    load_sa(i, sa);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        epi(i, j, sa);
+                        I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fw[j], I[i][j], 0, 0, 0);
-            if (last || !aligned) {
-                float cw[2];
+            pend = last || !aligned;
+            if (pend) {
+                pCA = sCA + blk * kGBM + wm * 64;
+                pCW = sCW + blk * kGBN + wn * 64;
+                if (blk == kDSB - 1) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) cw[j] = __builtin_fabsf(sCW[blk * kGBN + wn * 64 + j * 32 + l32]);
+                    for (int i = 0; i < 2; ++i) {
+                        f32x4_t sa[4];
+                        load_sa(i, sa);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sCA + blk * kGBM + wm * 64 + i * 32 + 8 * q + 4 * h);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float sa = __builtin_fabsf(v[e]);
-#pragma unroll
-                            for (int j = 0; j < 2; ++j)
-                                acc[i][j][4 * q + e] = __builtin_fmaf((float)I[i][j][4 * q + e], sa * cw[j], acc[i][j][4 * q + e]);
+                        for (int j = 0; j < 2; ++j) {
+                            epi(i, j, sa);
+                            I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
                         }
                     }
-                // restart the integer sums with a zero-product MFMA (C = 0):
-                // the matrix core has slack here, the vector ALU has none
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
+                    pend = false;
+                }
             }
         }
     };
@@ -576,6 +606,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
     }
 done:
 #undef MXS_DSTEP
+    if (pend) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f32x4_t sa[4];
+            load_sa(i, sa);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) epi(i, j, sa);
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
 #pragma unroll
     for (int i = 0; i < 2; ++i)
