@@ -109,16 +109,22 @@ __global__ __launch_bounds__(256) void k_outerr(const T *__restrict__ X, int64_t
         __syncthreads();
     }
 
-    // result register 4 q + r of lane l: row 8 q + 4 h + r, column l % 32
+    // result register 4 q + r of lane l: row 8 q + 4 h + r, column l % 32.
+    // All 16 Yq values are requested before any is used (rows and columns
+    // past the matrix read its last row / column and are left out of the sum).
     double s = 0.0;
-    const int64_t col = tn + 32 * wn + l32;
+    const int64_t col = tn + 32 * wn + l32, cc = col < N ? col : N - 1;
+    float yq[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int64_t row = tm + 32 * wm + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (row < M && col < N) {
-            const double d = (double)acc[i] - (double)Yq[row * ldy + col];
-            s += d * d;
-        }
+        yq[i] = Yq[(row < M ? row : M - 1) * ldy + cc];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t row = tm + 32 * wm + 8 * (i >> 2) + 4 * h + (i & 3);
+        const double d = (double)acc[i] - (double)yq[i];
+        s += (row < M && col < N) ? d * d : 0.0;
     }
     red[tid] = s;
     __syncthreads();
