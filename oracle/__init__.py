@@ -66,6 +66,7 @@ def _load():
         lib.or_allocate_blocks.argtypes = [P, c_int64, c_int32, c_int32, P, P]
         lib.or_output_error.argtypes = [P, c_int64, c_int64, c_int64, P, c_int64, c_int64, P, c_int64, P]
         lib.or_layer_budget.argtypes = [c_int32, P, P, P, c_double, P, P]
+        lib.or_attend_kv4.argtypes = [P, P, P, P, P, c_int64, c_int64, c_int64, c_int64, c_double, P]
         _lib = lib
     return _lib
 
@@ -240,3 +241,17 @@ def layer_budget(S, rows, K, B: float):
     R = np.zeros(1, np.float64)
     _check(_load().or_layer_budget(L, _ptr(S), _ptr(rows), _ptr(K), float(B), _ptr(out), _ptr(R)), "layer_budget")
     return out, float(R[0])
+
+
+# -- section 12: attention over the 4-bit K/V cache ----------------------------
+def attend_kv4(q, kc, ks, vc, vs, scale: float):
+    """out float64[Hq, D] for one query token q float32[Hq, D] over K/V codes
+    uint8[T, Hkv, D/2] and scales uint8[T, Hkv, D/32] (section 10 layout)."""
+    q = _f32(q)
+    kc, ks, vc, vs = (np.ascontiguousarray(a, np.uint8) for a in (kc, ks, vc, vs))
+    Hq, D = q.shape
+    T, Hkv = kc.shape[0], kc.shape[1]
+    out = np.zeros((Hq, D), np.float64)
+    _check(_load().or_attend_kv4(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), T, Hq, Hkv, D, float(scale),
+                                 _ptr(out)), "attend_kv4")
+    return out

@@ -610,3 +610,53 @@ int or_layer_budget(int32_t L, const double *S, const int64_t *rows, const int64
     free(bp);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 12. Attention over the 4-bit K/V cache (one query token)                  */
+/* ------------------------------------------------------------------------ */
+/*
+ * [NL] §4 (W4A4KV4) and [KR] abstract: keys and values are kept as 4-bit
+ * MXINT (section 10). Reading: they are consumed by plain scaled dot-product
+ * attention of one query token per head, heads grouped onto the KV heads
+ * (query head h reads KV head h / (Hq / Hkv)); K and V enter dequantized
+ * exactly (code * 2^(byte - 127), a 0x00 byte gives 0, a 0xFF byte NaN):
+ *   s_t   = scale * sum_d q[h,d] K[t,g,d]
+ *   p_t   = exp(s_t - max_t s) / sum_t exp(s_t - max_t s)
+ *   o[h,d] = sum_t p_t V[t,g,d]
+ * in fp64, t ascending.
+ */
+static double or_kv_value(const uint8_t *codes, const uint8_t *scales, int64_t t, int64_t g, int64_t Hkv,
+                          int64_t D, int64_t d)
+{
+    const uint8_t byte = codes[(t * Hkv + g) * (D / 2) + d / 2];
+    const int c = or_sext((d & 1) ? (uint32_t)(byte >> 4) : (uint32_t)(byte & 15u), 4);
+    return or_dequant(c, scales[(t * Hkv + g) * (D / OR_BLOCK) + d / OR_BLOCK]);
+}
+
+int or_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc, const uint8_t *vs,
+                  int64_t T, int64_t Hq, int64_t Hkv, int64_t D, double scale, double *out)
+{
+    if (!q || !kc || !ks || !vc || !vs || !out || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv ||
+        D < OR_BLOCK || D % OR_BLOCK) return -1;
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    if (!s) return -1;
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t g = h / (Hq / Hkv);
+        double m = -INFINITY;
+        for (int64_t t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += (double)q[h * D + d] * or_kv_value(kc, ks, t, g, Hkv, D, d);
+            s[t] = scale * acc;
+            if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < T; ++t) { s[t] = exp(s[t] - m); l += s[t]; }
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t) acc += s[t] * or_kv_value(vc, vs, t, g, Hkv, D, d);
+            out[h * D + d] = acc / l;
+        }
+    }
+    free(s);
+    return 0;
+}
