@@ -30,6 +30,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                                        decode: one JSON line per map)
        python bench.py --layerwise    (layer sensitivities and the layer-wise budget
                                        for the seven linear layers of a 70B block)
+       python bench.py --attention    (one query token over the MXINT4 K/V cache,
+                                       70B heads, 2048 / 8192 / 32768 tokens)
        python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
                                        and 32 tokens: one JSON line per case, GB/s
                                        of packed W + scale bytes against HBM peak,
@@ -215,6 +217,30 @@ def layerwise_cases(mx, synth, torch, T=256, B=4.5, reps=10):
           flush=True)
 
 
+def attention_cases(mx, synth, torch, reps=20):
+    """Attention of one query token over the MXINT4 K/V cache, Llama-2-70B
+    heads (64 query heads on 8 KV heads, head dimension 128), at 2048, 8192
+    and 32768 cached tokens: bytes = the K and V codes and scales, read once."""
+    dev = torch.device("cuda:0")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    Hq, Hkv, D = 64, 8, 128
+    for T in (2048, 8192, 32768):
+        seed = 9000 + T
+        kc, ks = mx.mxs_quantize_kv(synth.kv(T, Hkv, D, seed, device=dev))
+        vc, vs = mx.mxs_quantize_kv(synth.kv(T, Hkv, D, seed + 1, device=dev))
+        q = torch.randn(Hq, D, generator=torch.Generator().manual_seed(seed)).to(dev)
+        out = torch.empty(Hq, D, dtype=torch.float32, device=dev)
+        ws = torch.empty(mx.mxs_attend_kv4_workspace(T, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+        fn = lambda: mx.mxs_attend_kv4(q, (kc, ks), (vc, vs), D ** -0.5, out=out, ws=ws)
+        tc = time_cold(torch, fn, reps, flush)
+        tg = time_graph(torch, fn, reps)
+        nbytes = 2 * T * Hkv * (D // 2 + D // 32)
+        print(json.dumps({"case": "attention over MXINT4 K/V, 70B heads 64/8 x 128", "tokens": T,
+                          "kv_bytes": nbytes, "us": tc * 1e6, "warm_graph_us": tg * 1e6,
+                          "GBps": nbytes / tc / 1e9, "hbm_frac": nbytes / tc / HBM_PEAK,
+                          "warm_hbm_frac": nbytes / tg / HBM_PEAK}), flush=True)
+
+
 def build_workload(mx, synth, torch, dev):
     cfg = synth.CONFIGS[2]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
@@ -387,6 +413,7 @@ def main():
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--overhead", action="store_true")
     ap.add_argument("--layerwise", action="store_true")
+    ap.add_argument("--attention", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -408,6 +435,9 @@ def main():
         return
     if args.layerwise:
         layerwise_cases(mx, synth, torch)
+        return
+    if args.attention:
+        attention_cases(mx, synth, torch)
         return
 
     dev = torch.device("cuda:0")

@@ -67,6 +67,8 @@ def _load():
         "mxs_output_error": (S, [P, P, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64, P, c_int64, P, P,
                                  c_size_t, P]),
         "mxs_layer_budget": (S, [c_int32, P, P, P, c_double, P, P]),
+        "mxs_attend_kv4_workspace": (c_size_t, [c_int64, c_int64, c_int64, c_int64]),
+        "mxs_attend_kv4": (S, [P, P, P, P, P, c_int64, c_int64, c_int64, c_int64, ctypes.c_float, P, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -79,7 +81,8 @@ EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_bl
             "mxs_calibrate_workspace", "mxs_score_workspace", "mxs_calibrate", "mxs_score",
             "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
             "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv", "mxs_allocate_blocks",
-            "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget")
+            "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget", "mxs_attend_kv4_workspace",
+            "mxs_attend_kv4")
 
 
 def _check(status: int, where: str):
@@ -352,3 +355,32 @@ def mxs_layer_budget(S, rows, K, B: float):
                                  ctypes.cast(k_arr, c_void_p), float(B), ctypes.cast(out, c_void_p),
                                  ctypes.byref(R)), "mxs_layer_budget")
     return [[out[3 * i], out[3 * i + 1], out[3 * i + 2]] for i in range(L)], R.value
+
+
+# ------------------------------------------------------- attention over KV4
+def mxs_attend_kv4_workspace(T: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(_lib.mxs_attend_kv4_workspace(T, Hq, Hkv, D))
+
+
+def mxs_attend_kv4(q: torch.Tensor, k_cache, v_cache, scale: float, out=None, ws=None) -> torch.Tensor:
+    """out [Hq, D] fp32: attention of one query token q [Hq, D] (fp32) over K/V
+    caches given as (codes [T, Hkv, D/2], scales [T, Hkv, D/32]) from
+    mxs_quantize_kv."""
+    kc, ks = k_cache
+    vc, vs = v_cache
+    if not q.is_cuda or q.dtype != torch.float32 or q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous fp32 [Hq, D] GPU tensor")
+    for t in (kc, ks, vc, vs):
+        if not t.is_cuda or t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("caches must be contiguous uint8 [T, Hkv, ...] GPU tensors")
+    Hq, D = q.shape
+    T, Hkv = kc.shape[0], kc.shape[1]
+    if tuple(kc.shape) != (T, Hkv, D // 2) or tuple(vc.shape) != (T, Hkv, D // 2) \
+            or tuple(ks.shape) != (T, Hkv, D // 32) or tuple(vs.shape) != (T, Hkv, D // 32):
+        raise ValueError("cache shapes do not match q")
+    if out is None:
+        out = torch.empty((Hq, D), dtype=torch.float32, device=q.device)
+    p, n = _workspace(mxs_attend_kv4_workspace(T, Hq, Hkv, D), q.device, ws)
+    _check(_lib.mxs_attend_kv4(q.data_ptr(), kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vs.data_ptr(), T, Hq,
+                               Hkv, D, float(scale), out.data_ptr(), p, n, _stream(q.device)), "mxs_attend_kv4")
+    return out

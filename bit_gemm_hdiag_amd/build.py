@@ -15,7 +15,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libmxsens.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["mxs_colsum.hip", "mxs_allocate.hip", "mxs_quantize.hip", "mxs_gemm.hip", "mxs_layerwise.hip", "mxs_api.hip"]
+SOURCES = ["mxs_colsum.hip", "mxs_allocate.hip", "mxs_quantize.hip", "mxs_gemm.hip", "mxs_layerwise.hip", "mxs_attention.hip", "mxs_api.hip"]
 # packed fp32 instructions are disabled for all device code; common-code
 # sinking is off because merging the tails of per-width branches turned
 # register arrays of the decode kernels into scratch memory

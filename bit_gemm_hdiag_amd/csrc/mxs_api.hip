@@ -183,6 +183,26 @@ mxs_status mxs_output_error(const void *X, const void *W, mxs_dtype dtype, int64
                          "output_error");
 }
 
+size_t mxs_attend_kv4_workspace(int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+    return mxs::attend_kv4_workspace(T, Hq, Hkv, D);
+}
+
+mxs_status mxs_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc,
+                          const uint8_t *vs, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                          float *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !kc || !ks || !vc || !vs || !out || !ws) return fail(MXS_ERR_ARG, "attend_kv4: NULL pointer");
+    if (T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || D < 32 || D % 32)
+        return fail(MXS_ERR_SHAPE, "attend_kv4: T=%lld Hq=%lld Hkv=%lld D=%lld", (long long)T, (long long)Hq,
+                    (long long)Hkv, (long long)D);
+    if (!mxs::attend_kv4_supported(Hq, Hkv, D) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(q, 4))
+        return fail(MXS_ERR_UNSUPPORTED, "attend_kv4: needs Hq/Hkv <= 16, D <= 256 and 16-byte aligned codes");
+    if (T > (int64_t)65535 * 64) return fail(MXS_ERR_UNSUPPORTED, "attend_kv4: T=%lld too long", (long long)T);
+    if (ws_bytes < mxs::attend_kv4_workspace(T, Hq, Hkv, D)) return fail(MXS_ERR_WORKSPACE, "attend_kv4: workspace too small");
+    return device_status(mxs::launch_attend_kv4(q, kc, ks, vc, vs, T, Hq, Hkv, D, scale, out, ws, stream),
+                         "attend_kv4");
+}
+
 mxs_status mxs_quantize(const void *X, mxs_dtype dtype, int64_t ldx, const int32_t *perm,
                         const mxs_qmat *out, hipStream_t stream) {
     if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "unknown dtype %d", (int)dtype);

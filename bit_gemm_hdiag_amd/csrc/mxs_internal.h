@@ -47,4 +47,11 @@ hipError_t launch_output_error(const void *X, const void *W, mxs_dtype dtype, in
 int layer_budget(int32_t L, const double *S, const int64_t *rows, const int64_t *K, double B, int32_t *nblk,
                  double *R_out);
 
+// attention over the 4-bit K/V cache (mxs_attention.hip)
+size_t attend_kv4_workspace(int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
+bool attend_kv4_supported(int64_t Hq, int64_t Hkv, int64_t D);
+hipError_t launch_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc,
+                             const uint8_t *vs, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                             float *out, void *ws, hipStream_t st);
+
 }  // namespace mxs

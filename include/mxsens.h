@@ -288,6 +288,30 @@ mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int
 mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H, int64_t D,
                            uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
+/*
+ * Attention of one query token over the 4-bit K/V cache ([NL] §4,
+ * W4A4KV4: keys and values kept as 4-bit MXINT, as written by
+ * mxs_quantize_kv). Reading: plain scaled dot-product attention, query head
+ * h reading KV head h / (Hq / Hkv):
+ *     s_t = scale * sum_d q[h,d] K[t,g,d],  p = softmax_t(s),
+ *     out[h,d] = sum_t p_t V[t,g,d],
+ * with K, V dequantized exactly (code * 2^(byte - 127)). fp32 arithmetic,
+ * every sum in a fixed order (deterministic); the result matches the fp64
+ * definition within the rounding of the score dot products, the
+ * exponentials and the T-term sums.
+ * q: [Hq, D] fp32; kc, vc: [T, Hkv, D/2] uint8 codes (16-byte aligned);
+ * ks, vs: [T, Hkv, D/32] uint8 E8M0 scales; out: [Hq, D] fp32. All device
+ * pointers owned by the caller; ws >= mxs_attend_kv4_workspace(T, Hq, Hkv, D)
+ * bytes; asynchronous on `stream`. Hq / Hkv <= 16, D <= 256, D % 32 == 0,
+ * T <= 65535 * 64.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_UNSUPPORTED, MXS_ERR_WORKSPACE,
+ * MXS_ERR_DEVICE.
+ */
+size_t mxs_attend_kv4_workspace(int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
+mxs_status mxs_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *ks, const uint8_t *vc,
+                          const uint8_t *vs, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                          float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -226,3 +226,27 @@ def test_output_error_and_allocate_blocks_errors(lib):
     assert g(fake, 128, -1, 0, fake, fake, None) == -3
     assert g(None, 128, 1, 0, fake, fake, None) == -1
     assert g(fake, 262144, 1, 0, fake, fake, None) == -6
+
+
+def test_attend_kv4_errors(lib):
+    P = ctypes.c_void_p
+    f = lib.mxs_attend_kv4
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                  P, P, ctypes.c_size_t, P]
+    lib.mxs_attend_kv4_workspace.restype = ctypes.c_size_t
+    lib.mxs_attend_kv4_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    need = lib.mxs_attend_kv4_workspace(300, 8, 2, 64)
+    assert need == 5 * 8 * (2 + 64) * 4               # 64 tokens per workgroup: 5 splits
+    a = P(4096)            # never dereferenced: every call below fails validation
+    args = lambda **kw: [kw.get(k, v) for k, v in (("q", a), ("kc", a), ("ks", a), ("vc", a), ("vs", a), ("T", 300),
+                                                 ("Hq", 8), ("Hkv", 2), ("D", 64), ("s", 0.1), ("o", a), ("ws", a),
+                                                 ("n", need), ("st", None))]
+    assert f(*args(q=None)) == -1
+    assert f(*args(T=0)) == -2
+    assert f(*args(Hq=7)) == -2
+    assert f(*args(D=48)) == -2
+    assert f(*args(Hq=34, Hkv=2)) == -6            # group of 17 heads
+    assert f(*args(D=288)) == -6
+    assert f(*args(kc=P(4100))) == -6              # codes not 16-byte aligned
+    assert f(*args(n=need - 1)) == -4
