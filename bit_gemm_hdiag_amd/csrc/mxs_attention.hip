@@ -337,18 +337,17 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
         __builtin_amdgcn_sched_barrier(0);
 
         // software pipeline: the next sub-chunk's K loads fly while this
-        // one's values are summed, its V loads while its scores are formed
-        float sv[4][4];
-        attn_scores<ND>(kch, qv, 0, nt, scale2, c, kb0, sv);
-        // (scheduling barriers keep the loads ahead of the work they overlap)
-        for (int lt = 0;; lt += kASub) {
+        // one's values are summed, its V loads while the next scores are
+        // formed; one copy of each phase keeps the code small (scheduling
+        // barriers keep the loads ahead of the work they overlap)
+        for (int lt = 0; lt < nt; lt += kASub) {
+            float sv[4][4];
+            attn_scores<ND>(kch, qv, lt, nt, scale2, c, kb0, sv);
             load_k<ND>(kch, a, lt + kASub, i);
             __builtin_amdgcn_sched_barrier(0);
             attn_values<ND>(st, vch, sv, i, vb0);
-            if (lt + kASub >= nt) break;
             load_v<ND>(vch, a, lt + kASub, c);
             __builtin_amdgcn_sched_barrier(0);
-            attn_scores<ND>(kch, qv, lt + kASub, nt, scale2, c, kb0, sv);
         }
     }
 
