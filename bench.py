@@ -14,8 +14,9 @@ so inputs come from HBM; `warm_ms`: back-to-back calls through the Python
 binding; `warm_graph_ms`: the same calls replayed from one HIP graph; both
 warm figures re-read inputs the cache holds); `roofline` is for the
 dominant kernel; `variant_mx` repeats the step with mxs_mixed_gemm_mx
-(prefill on the block-scaled fp6 matrix cores); `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same step.
+(prefill on the block-scaled fp6 matrix cores) and `variant_fused` with
+mxs_mixed_gemm_fused (X quantized inside the product, no quantize_x stage);
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same step.
 
 The dominant kernel's roofline uses the mixed_gemm call's own duration,
 timed with HIP events on its stream inside every timed step; its HBM
@@ -269,18 +270,24 @@ def build_workload(mx, synth, torch, dev):
     w["Y"] = torch.empty((M, N), dtype=torch.float32, device=dev)
     w["ws_g"] = torch.empty(max(1, mx.mxs_mixed_gemm_workspace(w["Aq"], w["Wq"])), **u8)
     w["ws_gx"] = torch.empty(max(1, mx.mxs_mixed_gemm_mx_workspace(w["Aq"], w["Wq"])), **u8)
+    w["ws_gf"] = torch.empty(max(1, mx.mxs_mixed_gemm_fused_workspace(M, w["X"].dtype, w["Wq"])), **u8)
     T, H, D = cfg["kv"]["T"], cfg["kv"]["H"], cfg["kv"]["D"]
     w["kc"] = [torch.empty((T, H, D // 2), **u8) for _ in range(2)]
     w["ks"] = [torch.empty((T, H, D // 32), **u8) for _ in range(2)]
     return w
 
 
-def stage_fns(mx, w, variant=False):
-    """The step's stages; with variant=True the GEMM stage is mixed_gemm_mx."""
+def stage_fns(mx, w, variant=None):
+    """The step's stages; variant "mx": the GEMM stage is mixed_gemm_mx;
+    variant "fused": quantize_x and the GEMM are one mixed_gemm_fused call."""
     n8, n6, n4 = w["blocks"]
-    gemm = ((lambda: mx.mxs_mixed_gemm_mx(w["Aq"], w["Wq"], w["Y"], ws=w["ws_gx"])) if variant
-            else (lambda: mx.mxs_mixed_gemm(w["Aq"], w["Wq"], w["Y"], ws=w["ws_g"])))
-    return [
+    if variant == "mx":
+        gemm = lambda: mx.mxs_mixed_gemm_mx(w["Aq"], w["Wq"], w["Y"], ws=w["ws_gx"])
+    elif variant == "fused":
+        gemm = lambda: mx.mxs_mixed_gemm_fused(w["X"], w["perm"], w["Wq"], w["Y"], ws=w["ws_gf"])
+    else:
+        gemm = lambda: mx.mxs_mixed_gemm(w["Aq"], w["Wq"], w["Y"], ws=w["ws_g"])
+    stages = [
         ("calibrate", lambda: (w["hdiag"].zero_(), mx.mxs_calibrate(w["Xc"], w["hdiag"], ws=w["ws_cal"]))),
         ("score", lambda: mx.mxs_score(w["W"], w["hdiag"], w["score"], ws=w["ws_sc"])),
         ("allocate", lambda: mx.mxs_allocate(w["score"], w["bp8"], w["bp6"], w["bits"], w["perm"])),
@@ -290,6 +297,7 @@ def stage_fns(mx, w, variant=False):
         ("quantize_kv", lambda: (mx.mxs_quantize_kv(w["Kc"], w["kc"][0], w["ks"][0]),
                                  mx.mxs_quantize_kv(w["Vc"], w["kc"][1], w["ks"][1]))),
     ]
+    return [st for st in stages if not (variant == "fused" and st[0] == "quantize_x")]
 
 
 def algorithmic_work(w):
@@ -479,17 +487,22 @@ def main():
     step_s, gemm_call_s = run_steps(stages)
     log(f"step {step_s * 1e3:.3f} ms, mixed_gemm call {gemm_call_s * 1e6:.1f} us")
     log("the same step with mixed_gemm_mx")
-    step_x, gemm_x = run_steps(stage_fns(mx, w, variant=True))
+    step_x, gemm_x = run_steps(stage_fns(mx, w, variant="mx"))
     log(f"step {step_x * 1e3:.3f} ms, mixed_gemm_mx call {gemm_x * 1e6:.1f} us")
+    log("the same step with mixed_gemm_fused (no quantize_x stage)")
+    step_f, gemm_f = run_steps(stage_fns(mx, w, variant="fused"))
+    log(f"step {step_f * 1e3:.3f} ms, mixed_gemm_fused call {gemm_f * 1e6:.1f} us")
 
     work = algorithmic_work(w)
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     stage_out = {}
-    for name, fn in stages + [("mixed_gemm_mx", stage_fns(mx, w, variant=True)[5][1])]:
+    extra = [("mixed_gemm_mx", dict(stage_fns(mx, w, variant="mx"))["mixed_gemm"]),
+             ("mixed_gemm_fused", dict(stage_fns(mx, w, variant="fused"))["mixed_gemm"])]
+    for name, fn in stages + extra:
         t = time_cold(torch, fn, max(args.stage_reps, 9), flush)
         tw = time_stage(torch, fn, args.stage_reps)
         tg = time_graph(torch, fn, args.stage_reps)
-        wk = work["mixed_gemm" if name == "mixed_gemm_mx" else name]
+        wk = work["mixed_gemm" if name in ("mixed_gemm_mx", "mixed_gemm_fused") else name]
         d = dict(ms=t * 1e3, warm_ms=tw * 1e3, warm_graph_ms=tg * 1e3)
         if "bytes" in wk:
             d["GBps"] = wk["bytes"] / t / 1e9
@@ -518,6 +531,13 @@ def main():
                "frac": ach_x * 1e12 / FP6_PEAK, "int8_peak_frac": ach_x * 1e12 / INT8_PEAK,
                "traffic": measured_traffic("traffic_bytes_per_call_mx")}
     qx = stage_out["quantize_x"]
+    ach_f = ops / gemm_f / 1e12
+    fused = {"entry": "mxs_mixed_gemm_fused (X quantized into the prefill operand: k_quant_prep + "
+                      "k_gemm_prep of W + k_gemm_dma; the step drops its quantize_x stage)",
+             "value": ops / step_f / 1e12, "ms_per_step": step_f * 1e3, "launch_us": gemm_f * 1e6,
+             "achieved": ach_f, "unit": "TOP/s", "peak": INT8_PEAK / 1e12, "frac": ach_f * 1e12 / INT8_PEAK,
+             "cold_us": stage_out["mixed_gemm_fused"]["ms"] * 1e3,
+             "unfused_cold_us": (qx["ms"] + stage_out["mixed_gemm"]["ms"]) * 1e3}
     out = {
         "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": ops / step_s / 1e12,
@@ -541,6 +561,7 @@ def main():
         "stages": stage_out,
         "roofline": roofline,
         "variant_mx": variant,
+        "variant_fused": fused,
     }
     if not args.no_cpu:
         log("cpu baseline (oracle)")

@@ -69,6 +69,8 @@ def _load():
         "mxs_layer_budget": (S, [c_int32, P, P, P, c_double, P, P]),
         "mxs_attend_kv4_workspace": (c_size_t, [c_int64, c_int64, c_int64, c_int64]),
         "mxs_attend_kv4": (S, [P, P, P, P, P, c_int64, c_int64, c_int64, c_int64, ctypes.c_float, P, P, c_size_t, P]),
+        "mxs_mixed_gemm_fused_workspace": (c_size_t, [c_int64, c_int32, POINTER(_QMat)]),
+        "mxs_mixed_gemm_fused": (S, [P, c_int32, c_int64, c_int64, P, POINTER(_QMat), P, c_int64, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -82,7 +84,7 @@ EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_bl
             "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
             "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv", "mxs_allocate_blocks",
             "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget", "mxs_attend_kv4_workspace",
-            "mxs_attend_kv4")
+            "mxs_attend_kv4", "mxs_mixed_gemm_fused_workspace", "mxs_mixed_gemm_fused")
 
 
 def _check(status: int, where: str):
@@ -277,6 +279,37 @@ def _gemm(fn, wsfn, name, A: QMat, W: QMat, Y, ws) -> torch.Tensor:
 def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
     """Y [M, N] fp32 = Qa(X) Qw(W)^T with per-block MX scales."""
     return _gemm(_lib.mxs_mixed_gemm, _lib.mxs_mixed_gemm_workspace, "mxs_mixed_gemm", A, W, Y, ws)
+
+
+def mxs_mixed_gemm_fused_workspace(M: int, dtype: torch.dtype, W: QMat) -> int:
+    dt = MXS_BF16 if dtype == torch.bfloat16 else MXS_F32
+    return int(_lib.mxs_mixed_gemm_fused_workspace(M, dt, ctypes.byref(W.c_struct())))
+
+
+def mxs_mixed_gemm_fused(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, Y: torch.Tensor | None = None,
+                         ws=None) -> torch.Tensor:
+    """Y [M, N] fp32 = mixed_gemm(quantize(X[:, perm] at W's block counts), W), X quantized inside the call."""
+    px, ldx = _dev2d(X, "X")
+    M, K = X.shape
+    if K != W.K:
+        raise ValueError("X and W differ in K")
+    if perm is not None and (perm.dtype != torch.int32 or not perm.is_contiguous() or perm.numel() != K
+                             or not perm.is_cuda):
+        raise ValueError("perm must be a contiguous int32 [K] GPU tensor")
+    if Y is None:
+        Y = torch.empty((M, W.rows), dtype=torch.float32, device=X.device)
+    if Y.dtype != torch.float32:
+        raise TypeError("Y must be fp32")
+    py, ldy = _dev2d(Y, "Y")
+    w = W.c_struct()
+    dt = _dtype(X)
+    if ws is None:
+        p, n = _workspace(int(_lib.mxs_mixed_gemm_fused_workspace(M, dt, ctypes.byref(w))), X.device, None)
+    else:
+        p, n = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check(_lib.mxs_mixed_gemm_fused(px, dt, M, ldx, _ptr(perm), ctypes.byref(w), py, ldy, p, n,
+                                     _stream(X.device)), "mxs_mixed_gemm_fused")
+    return Y
 
 
 def mxs_mixed_gemm_mx_workspace(A: QMat, W: QMat) -> int:

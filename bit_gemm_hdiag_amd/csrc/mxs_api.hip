@@ -218,6 +218,14 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W) {
     return mxs::gemm_workspace(*A, *W);
 }
 
+// Operand loads are 16/4/8-byte vector loads per row.
+static mxs_status check_planes_aligned(const mxs_qmat *m, const char *name) {
+    if ((m->n8 && (!aligned(m->q8, 16) || m->ld8 % 16)) || (m->n6 && (!aligned(m->q6, 4) || m->ld6 % 4)) ||
+        (m->n4 && (!aligned(m->q4, 8) || m->ld4 % 8)))
+        return fail(MXS_ERR_UNSUPPORTED, "%s: planes need q8/ld8 16-byte, q6/ld6 4-byte and q4/ld4 8-byte alignment", name);
+    return MXS_OK;
+}
+
 // Argument checks shared by both GEMM entry points.
 static mxs_status check_gemm(const mxs_qmat *A, const mxs_qmat *W, const float *Y, int64_t ldy, const void *ws,
                              size_t ws_bytes, size_t need, const char *name) {
@@ -227,13 +235,7 @@ static mxs_status check_gemm(const mxs_qmat *A, const mxs_qmat *W, const float *
     if (A->K != W->K || A->n8 != W->n8 || A->n6 != W->n6 || A->n4 != W->n4)
         return fail(MXS_ERR_SHAPE, "%s: A and W differ in K or block counts", name);
     if (ldy < W->rows || (!Y && A->rows > 0 && W->rows > 0)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: Y NULL or ldy < N", name);
-    // operand loads are 16/4/8-byte vector loads per row
-    const mxs_qmat *q[2] = {A, W};
-    for (const mxs_qmat *m : q) {
-        if ((m->n8 && (!aligned(m->q8, 16) || m->ld8 % 16)) || (m->n6 && (!aligned(m->q6, 4) || m->ld6 % 4)) ||
-            (m->n4 && (!aligned(m->q4, 8) || m->ld4 % 8)))
-            return fail(MXS_ERR_UNSUPPORTED, "%s: planes need q8/ld8 16-byte, q6/ld6 4-byte and q4/ld4 8-byte alignment", name);
-    }
+    if ((s = check_planes_aligned(A, name)) != MXS_OK || (s = check_planes_aligned(W, name)) != MXS_OK) return s;
     if (A->rows > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "%s: more than 4194304 rows in A", name);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
         return fail(MXS_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", name, need, ws ? ws_bytes : 0);
@@ -246,6 +248,30 @@ mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_
     const mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm");
     if (s != MXS_OK) return s;
     return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm");
+}
+
+size_t mxs_mixed_gemm_fused_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W) {
+    if (!W || !dtype_ok(dtype) || M < 0 || W->K <= 0 || W->K % 32) return 0;
+    return mxs::gemm_fused_workspace(M, dtype, *W);
+}
+
+mxs_status mxs_mixed_gemm_fused(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx, const int32_t *perm,
+                                const mxs_qmat *W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "mixed_gemm_fused: unknown dtype %d", (int)dtype);
+    mxs_status s = check_qmat(W, "W");
+    if (s != MXS_OK) return s;
+    if (M < 0 || ldx < W->K) return fail(MXS_ERR_SHAPE, "mixed_gemm_fused: M=%lld ldx=%lld K=%lld", (long long)M, (long long)ldx, (long long)W->K);
+    if (M > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm_fused: more than 4194304 rows in X");
+    const bool work = M > 0 && W->rows > 0;
+    if (work && !X) return fail(MXS_ERR_ARG, "mixed_gemm_fused: X is NULL");
+    if (ldy < W->rows || (!Y && work)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "mixed_gemm_fused: Y NULL or ldy < N");
+    if ((s = check_planes_aligned(W, "mixed_gemm_fused")) != MXS_OK) return s;
+    const size_t need = mxs::gemm_fused_workspace(M, dtype, *W);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return fail(MXS_ERR_WORKSPACE, "mixed_gemm_fused: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+    return device_status(mxs::launch_mixed_gemm_fused(X, dtype, M, ldx, perm, *W, Y, ldy, ws, ws_bytes, stream),
+                         "mixed_gemm_fused");
 }
 
 size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W) {

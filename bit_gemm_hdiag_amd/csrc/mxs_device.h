@@ -201,6 +201,46 @@ __device__ __forceinline__ void store_bytes(uint8_t *p, uint64_t w, int n) {
     }
 }
 
+// ---------------------------------------------------------------- gathers
+// LDS budget of the row-staged gathers (the permutation as 16-bit indices
+// plus one source row).
+constexpr int64_t kStageLds = 96 * 1024;
+
+// sperm[j] = perm[j] as 16 bits (an index outside [0, K) is clamped). With a
+// 16-byte aligned permutation each thread takes 8 consecutive indices per
+// pass (two 16-byte loads, one 16-byte LDS write) and issues the loads of up
+// to 8 passes before writing, so the workgroup waits for one round trip
+// instead of one per pass. K is a multiple of 32.
+__device__ __forceinline__ void stage_perm(const int32_t *__restrict__ perm, int64_t K, uint16_t *sperm, int tid) {
+    const uint32_t k = (uint32_t)K;
+    auto clamp = [k](uint32_t v) { return v < k ? v : k - 1u; };
+    if (reinterpret_cast<uintptr_t>(perm) % 16 == 0) {
+        constexpr int kPasses = 8;
+        for (int64_t j0 = 8 * (int64_t)tid; j0 < K; j0 += 2048 * kPasses) {
+            uint4 v[kPasses][2];
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int64_t j = j0 + 2048 * p;
+                if (j < K) {
+                    v[p][0] = reinterpret_cast<const uint4 *>(perm + j)[0];
+                    v[p][1] = reinterpret_cast<const uint4 *>(perm + j)[1];
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int64_t j = j0 + 2048 * p;
+                if (j < K)
+                    *reinterpret_cast<uint4 *>(sperm + j) =
+                        make_uint4(clamp(v[p][0].x) | (clamp(v[p][0].y) << 16), clamp(v[p][0].z) | (clamp(v[p][0].w) << 16),
+                                   clamp(v[p][1].x) | (clamp(v[p][1].y) << 16), clamp(v[p][1].z) | (clamp(v[p][1].w) << 16));
+            }
+        }
+    } else {
+        for (int64_t j = tid; j < K; j += 256) sperm[j] = (uint16_t)clamp((uint32_t)perm[j]);
+    }
+}
+
+
 // fp32 value 2^(byte - 127) of an E8M0 scale byte (0xFF -> +Inf, which turns
 // the all-zero codes of a non-finite block into NaN in any product).
 // Workgroup barrier for LDS hand-offs: waits only for this wave's LDS (and

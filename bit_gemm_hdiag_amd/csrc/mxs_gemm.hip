@@ -27,6 +27,8 @@
 // l mod 32. A and B use the same byte-to-k assignment, so any fixed
 // reordering of the k positions inside a block (as the 4-bit unpack does)
 // leaves the block sum unchanged.
+#include <cstring>
+
 #include "mxs_device.h"
 #include "mxs_internal.h"
 
@@ -332,6 +334,125 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
         if (ok) {
             const float4 v = *reinterpret_cast<const float4 *>(&s_cs[bb][4 * part]);
             *reinterpret_cast<float4 *>(J.cs + ob * J.Rp + rt * 64 + 4 * part) = v;
+        }
+    }
+}
+
+// Activation operand straight from X (the fused entry point): the same
+// prepared layout as k_gemm_prep writes from planes, computed from the
+// unquantized rows. A workgroup walks rows; each row and the permutation
+// (16-bit) are staged in LDS; wave w takes windows w, w + 4, ... of the row:
+// lane (block t / 4 of the window, quarter t % 4) gathers its 8 values,
+// quantizes them at the block's width (the quantizer of mxs_quantize: scale
+// from the quad's largest magnitude, codes rounded half to even and clamped
+// symmetrically), and the window's alignment (16-lane-group reduction of the
+// blocks' scale exponents) shifts the codes exactly as k_gemm_prep does.
+// Rows R .. Rp - 1 and padding blocks get zero codes and scale 1.
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int64_t R, int64_t ldx,
+                                                    const int32_t *__restrict__ perm, int64_t K, int64_t Rp,
+                                                    int64_t Kp, Segs S, int8_t *__restrict__ codes,
+                                                    float *__restrict__ cs) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint16_t *sperm = reinterpret_cast<uint16_t *>(lds);
+    T *srow = reinterpret_cast<T *>(lds + ((2 * K + 15) / 16) * 16);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = lane >> 2, q = lane & 3;
+    if (perm) {
+        stage_perm(perm, K, sperm, tid);
+    } else {
+        for (int64_t j = tid; j < K; j += 256) sperm[j] = (uint16_t)j;
+    }
+    const int64_t nb = K / 32, nbp = Kp / 32;
+    const int64_t nwin = S.win_base[3] + (nbp - nb + kG - 1) / kG;
+    const int64_t nvec = K * (int64_t)sizeof(T) / 16;
+    const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
+    for (int64_t row = blockIdx.x; row < Rp; row += gridDim.x) {
+        const bool real_row = row < R;
+        __syncthreads();                       // the previous row's gathers are done (and sperm is staged)
+        if (real_row) {
+            const T *x = X + row * ldx;
+            if (vec) {
+                for (int64_t v = tid; v < nvec; v += 256)
+                    reinterpret_cast<uint4 *>(srow)[v] = reinterpret_cast<const uint4 *>(x)[v];
+            } else {
+                for (int64_t j = tid; j < K; j += 256) srow[j] = x[j];
+            }
+        }
+        __syncthreads();
+        for (int64_t win = wave; win < nwin; win += 4) {
+            int sg = 0;
+            int64_t b;
+            bool real_blk;
+            if (win < S.win_base[3]) {
+                sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : 2);
+                b = S.lo[sg] + (win - S.win_base[sg]) * kG + blk;
+                real_blk = b < S.hi[sg];
+            } else {   // padding blocks nb .. nbp - 1
+                b = nb + (win - S.win_base[3]) * kG + blk;
+                real_blk = false;
+            }
+            const int cls = S.cls[sg], F = S.F[sg];
+            const bool real = real_blk && real_row;
+            float v[8];
+            if (real) {
+                const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + 32 * b + 8 * q);
+                const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = load1<T>(srow + (w[i] & 0xFFFFu));
+                    v[2 * i + 1] = load1<T>(srow + (w[i] >> 16));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            }
+            // codes of the quarter as bytes (the quantizer of mxs_quantize)
+            uint32_t a = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t m = __float_as_uint(v[i]) & 0x7fffffffu;
+                a = a > m ? a : m;
+            }
+            a = quad_max_u32(a);
+            const BlockScale bs = block_scale(a, cls);
+            const float magic = 12582912.0f, cm = cmax_of(cls);
+            uint32_t cb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                cb[i] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], bs.inv, magic), magic - cm, magic + cm));
+            uint32_t lo = __builtin_amdgcn_perm(cb[1], cb[0], 0x0C0C0400u) | __builtin_amdgcn_perm(cb[3], cb[2], 0x04000C0Cu);
+            uint32_t hi = __builtin_amdgcn_perm(cb[5], cb[4], 0x0C0C0400u) | __builtin_amdgcn_perm(cb[7], cb[6], 0x04000C0Cu);
+            const bool bad = real && bs.bad;
+            if (bad) lo = hi = 0;
+            const int s = (int)bs.byte - 127;
+            const uint32_t anynz = quad_max_u32((lo | hi) != 0 ? 1u : 0u);   // whole quad, unconditionally
+            const bool nz = real && !bad && anynz != 0;
+            // window reduction over the 16 blocks (lanes 4 apart)
+            int smax = nz ? s : -100000, smin = nz ? s : 100000, anybad = bad;
+#pragma unroll
+            for (int off = 4; off < 64; off <<= 1) {
+                smax = max(smax, __shfl_xor(smax, off));
+                smin = min(smin, __shfl_xor(smin, off));
+                anybad |= __shfl_xor(anybad, off);
+            }
+            const bool allzero = smax == -100000;
+            const bool aligned = !anybad && (allzero || smax - smin <= F);
+            const int base = allzero ? 0 : smax - F;
+            const int shift = aligned ? (nz ? s - base : 0) : F;
+            float scale;
+            if (!real) scale = 1.0f;
+            else if (bad) scale = -__builtin_inff();
+            else scale = aligned ? __builtin_ldexpf(1.0f, base) : -__builtin_ldexpf(1.0f, s - F);
+            // per-byte left shift (bits pushed into the next byte are masked off)
+            const uint32_t keep = 0x01010101u * ((0xFFu << shift) & 0xFFu);
+            lo = (lo << shift) & keep;
+            hi = (hi << shift) & keep;
+            if (b < nbp && (real_blk || b >= nb)) {
+                *reinterpret_cast<uint2 *>(codes + row * Kp + 32 * b + 8 * q) = make_uint2(lo, hi);
+                if (q == 0) cs[b * Rp + row] = scale;
+            }
         }
     }
 }
@@ -1803,6 +1924,121 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
     return hipGetLastError();
 }
 
+
+// Fused entry point: Y = mixed_gemm(quantize(X[:, perm] at W's block counts), W).
+// Prefill rows whose row and permutation fit the LDS stage take
+// k_quant_prep (no activation planes); other shapes quantize into planes
+// held in the workspace and take the unfused kernels.
+namespace {
+
+mxs_qmat act_shape(int64_t M, const mxs_qmat &W) {
+    mxs_qmat A;
+    memset(&A, 0, sizeof A);
+    A.rows = M;
+    A.K = W.K;
+    A.n8 = W.n8;
+    A.n6 = W.n6;
+    A.n4 = W.n4;
+    return A;
+}
+
+int64_t quant_prep_lds(int64_t K, mxs_dtype dt) {
+    return ((2 * K + 15) / 16) * 16 + K * (dt == MXS_BF16 ? 2 : 4);
+}
+
+bool fused_prefill(int64_t M, int64_t K, mxs_dtype dt) {
+    return M >= kPrefillMinRows && K <= 65536 && quant_prep_lds(K, dt) <= kStageLds;
+}
+
+// activation planes inside the workspace (rows 16-byte aligned)
+struct ActPlanes {
+    size_t q8, q6, q4, sc, total;
+    int64_t ld8, ld6, ld4, lds;
+};
+
+ActPlanes act_planes(const mxs_qmat &A) {
+    ActPlanes P;
+    P.ld8 = ceil_div(32 * (int64_t)A.n8, 16) * 16;
+    P.ld6 = ceil_div(24 * (int64_t)A.n6, 16) * 16;
+    P.ld4 = ceil_div(16 * (int64_t)A.n4, 16) * 16;
+    P.lds = ceil_div(A.K / 32, 16) * 16;
+    size_t off = 0;
+    P.q8 = off; off = align256(off + (size_t)(A.rows * P.ld8));
+    P.q6 = off; off = align256(off + (size_t)(A.rows * P.ld6));
+    P.q4 = off; off = align256(off + (size_t)(A.rows * P.ld4));
+    P.sc = off; off = align256(off + (size_t)(A.rows * P.lds));
+    P.total = off;
+    return P;
+}
+
+}  // namespace
+
+size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W) {
+    if (M == 0 || W.rows == 0) return 0;
+    const mxs_qmat A = act_shape(M, W);
+    if (fused_prefill(M, W.K, dt) && !use_gemv(A, W)) return prep_layout(A, W).total;
+    return act_planes(A).total + gemm_workspace(A, W);
+}
+
+hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64_t ldx, const int32_t *perm,
+                                   const mxs_qmat &W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                   hipStream_t st) {
+    const int64_t N = W.rows;
+    if (M == 0 || N == 0) return hipSuccess;
+    mxs_qmat A = act_shape(M, W);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    if (!fused_prefill(M, W.K, dt) || use_gemv(A, W)) {
+        const ActPlanes P = act_planes(A);
+        A.q8 = reinterpret_cast<int8_t *>(base + P.q8);
+        A.ld8 = P.ld8;
+        A.q6 = base + P.q6;
+        A.ld6 = P.ld6;
+        A.q4 = base + P.q4;
+        A.ld4 = P.ld4;
+        A.sc = base + P.sc;
+        A.lds = P.lds;
+        hipError_t e = launch_quantize(X, dt, ldx, perm, A, st);
+        if (e != hipSuccess) return e;
+        return launch_mixed_gemm(A, W, Y, ldy, base + P.total, ws_bytes - P.total, st);
+    }
+    const PrepLayout L = prep_layout(A, W);
+    int8_t *ac = reinterpret_cast<int8_t *>(base + L.a_codes);
+    int8_t *wc = reinterpret_cast<int8_t *>(base + L.w_codes);
+    float *acs = reinterpret_cast<float *>(base + L.a_cs);
+    float *wcs = reinterpret_cast<float *>(base + L.w_cs);
+    const Segs S = make_segs(A.n8, A.n6, A.n4);
+    const int64_t nb = A.K / 32, nbp = L.Kp / 32;
+    const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
+    const int64_t lds = quant_prep_lds(A.K, dt);
+    const int64_t per_cu = (160 * 1024) / lds;
+    int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
+    blocks = blocks < L.Mp ? blocks : L.Mp;
+    hipError_t e;
+    if (dt == MXS_BF16) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_prep<uint16_t>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_quant_prep<uint16_t>, dim3((unsigned)blocks), dim3(256), (size_t)lds, st,
+                           static_cast<const uint16_t *>(X), M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs);
+    } else {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_prep<float>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_quant_prep<float>, dim3((unsigned)blocks), dim3(256), (size_t)lds, st,
+                           static_cast<const float *>(X), M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
+    const int64_t tw = jw.tiles_r * windows;
+    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, A.K, L.Kp, S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
+    hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
+    return hipGetLastError();
+}
 
 hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
                                 void *ws, size_t, hipStream_t st) {

@@ -33,6 +33,10 @@ hipError_t launch_quantize(const void *X, mxs_dtype dt, int64_t ldx, const int32
 // mixed GEMM (mxs_gemm.hip): int8 block sums with fp32 scale epilogues, and
 // the variant on the block-scaled fp6 matrix cores (prefill kernels only)
 size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W);
+size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W);
+hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64_t ldx, const int32_t *perm,
+                                   const mxs_qmat &W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                   hipStream_t st);
 hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
                              void *ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W);

@@ -84,45 +84,10 @@ __global__ __launch_bounds__(256) void k_quant_gather(const T *__restrict__ X, i
     }
 }
 
-// LDS-staged gather: the permutation (as 16-bit indices) is staged once per
-// workgroup, then each row is read with coalesced 16-byte loads into LDS and
-// gathered from there. Used when the permutation and one row fit in LDS.
-constexpr int64_t kStageLds = 96 * 1024;
-
-// sperm[j] = perm[j] as 16 bits (an index outside [0, K) is clamped). With a
-// 16-byte aligned permutation each thread takes 8 consecutive indices per
-// pass (two 16-byte loads, one 16-byte LDS write) and issues the loads of up
-// to 8 passes before writing, so the workgroup waits for one round trip
-// instead of one per pass. K is a multiple of 32.
-__device__ __forceinline__ void stage_perm(const int32_t *__restrict__ perm, int64_t K, uint16_t *sperm, int tid) {
-    const uint32_t k = (uint32_t)K;
-    auto clamp = [k](uint32_t v) { return v < k ? v : k - 1u; };
-    if (reinterpret_cast<uintptr_t>(perm) % 16 == 0) {
-        constexpr int kPasses = 8;
-        for (int64_t j0 = 8 * (int64_t)tid; j0 < K; j0 += 2048 * kPasses) {
-            uint4 v[kPasses][2];
-#pragma unroll
-            for (int p = 0; p < kPasses; ++p) {
-                const int64_t j = j0 + 2048 * p;
-                if (j < K) {
-                    v[p][0] = reinterpret_cast<const uint4 *>(perm + j)[0];
-                    v[p][1] = reinterpret_cast<const uint4 *>(perm + j)[1];
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < kPasses; ++p) {
-                const int64_t j = j0 + 2048 * p;
-                if (j < K)
-                    *reinterpret_cast<uint4 *>(sperm + j) =
-                        make_uint4(clamp(v[p][0].x) | (clamp(v[p][0].y) << 16), clamp(v[p][0].z) | (clamp(v[p][0].w) << 16),
-                                   clamp(v[p][1].x) | (clamp(v[p][1].y) << 16), clamp(v[p][1].z) | (clamp(v[p][1].w) << 16));
-            }
-        }
-    } else {
-        for (int64_t j = tid; j < K; j += 256) sperm[j] = (uint16_t)clamp((uint32_t)perm[j]);
-    }
-}
-
+// LDS-staged gather: the permutation (as 16-bit indices, stage_perm) is
+// staged once per workgroup, then each row is read with coalesced 16-byte
+// loads into LDS and gathered from there. Used when the permutation and one
+// row fit in kStageLds.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant_gather_lds(const T *__restrict__ X, int64_t R, int64_t ldx,
                                                           const int32_t *__restrict__ perm, Planes P) {

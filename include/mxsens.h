@@ -278,6 +278,30 @@ mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Activation quantisation fused into the product ([NL] §1 and §2.3, [RP]
+ * "Triplet Quantization": activations quantised with the weight's channel
+ * map): Y = mixed_gemm(quantize(X, perm at W's block counts), W), the same
+ * result bit for bit as mxs_quantize into planes followed by mxs_mixed_gemm.
+ * With 64 or more rows (and, for the row staging, K <= 65536 with
+ * K * (2 + element size) <= 96 KiB) the activation rows are quantised
+ * straight into the prefill kernel's exponent-aligned int8 operand, so no
+ * activation planes are written or read; other shapes quantise into planes
+ * kept in the workspace and run the mxs_mixed_gemm kernels.
+ * X: [M, ldx >= K] row-major of `dtype` (device); perm: [K] int32 gather
+ * form (X column perm[j] becomes position j) or NULL for the identity;
+ * W: prepared weights (device planes, the plane alignment mxs_mixed_gemm
+ * asks for); Y: [M, ldy >= N] fp32 (device). ws >=
+ * mxs_mixed_gemm_fused_workspace(M, dtype, W) bytes, 256-byte aligned, owned
+ * by the caller; asynchronous on `stream`.
+ * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_UNSUPPORTED (more than 2^22
+ * rows, misaligned planes), MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+size_t mxs_mixed_gemm_fused_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W);
+mxs_status mxs_mixed_gemm_fused(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx, const int32_t *perm,
+                                const mxs_qmat *W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
  * KV-cache quantisation (W4A4KV4, [NL] §4 and [REV] "Validation": keys and
  * values stored as 4-bit MXINT). Reading: uniform 4-bit, blocks of 32
  * consecutive elements along the head dimension, no permutation.

@@ -250,3 +250,30 @@ def test_attend_kv4_errors(lib):
     assert f(*args(D=288)) == -6
     assert f(*args(kc=P(4100))) == -6              # codes not 16-byte aligned
     assert f(*args(n=need - 1)) == -4
+
+
+def test_gemm_fused_errors(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.mxs_mixed_gemm_fused
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, ctypes.c_int32, I64, I64, P, P, P, I64, P, ctypes.c_size_t, P]
+    wsf = lib.mxs_mixed_gemm_fused_workspace
+    wsf.restype = ctypes.c_size_t
+    wsf.argtypes = [I64, ctypes.c_int32, P]
+    W = qm(rows=16)
+    w = ctypes.byref(W)
+    assert f(FAKE, 7, 8, 64, None, w, FAKE, 16, None, 0, None) == -1         # unknown dtype
+    assert f(FAKE, 1, 8, 32, None, w, FAKE, 16, None, 0, None) == -2         # ldx < K
+    assert f(FAKE, 1, -1, 64, None, w, FAKE, 16, None, 0, None) == -2        # M < 0
+    assert f(None, 1, 8, 64, None, w, FAKE, 16, None, 0, None) == -1         # X NULL
+    assert f(FAKE, 1, 8, 64, None, w, FAKE, 8, None, 0, None) == -2          # ldy < N
+    assert f(FAKE, 1, 8, 64, None, None, FAKE, 16, None, 0, None) == -1      # W NULL
+    assert f(FAKE, 1, 8, 64, None, ctypes.byref(qm(rows=16, q4=0x20004)), FAKE, 16, None, 0, None) == -6
+    assert f(FAKE, 1, 1 << 23, 64, None, w, FAKE, 16, None, 0, None) == -6   # too many rows
+    for M in (8, 128):                                                       # planes path, fused path
+        need = wsf(M, 1, w)
+        assert need > 0
+        assert f(FAKE, 1, M, 64, None, w, FAKE, 16, FAKE, need - 1, None) == -4
+    assert wsf(0, 1, w) == 0
+    assert wsf(128, 9, w) == 0
+
