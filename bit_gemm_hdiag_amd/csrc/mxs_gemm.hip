@@ -348,7 +348,10 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
 // symmetrically), and the window's alignment (16-lane-group reduction of the
 // blocks' scale exponents) shifts the codes exactly as k_gemm_prep does.
 // Rows R .. Rp - 1 and padding blocks get zero codes and scale 1.
-template <typename T>
+// Rows are streamed one ahead: each thread holds its PPT 16-byte pieces of
+// the workgroup's next row in registers while the current row is quantized
+// (16-byte aligned rows; others are staged element by element).
+template <typename T, int PPT>
 __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int64_t R, int64_t ldx,
                                                     const int32_t *__restrict__ perm, int64_t K, int64_t Rp,
                                                     int64_t Kp, Segs S, int8_t *__restrict__ codes,
@@ -368,19 +371,32 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
     const int64_t nwin = S.win_base[3] + (nbp - nb + kG - 1) / kG;
     const int64_t nvec = K * (int64_t)sizeof(T) / 16;
     const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
-    for (int64_t row = blockIdx.x; row < Rp; row += gridDim.x) {
+    const int64_t G = gridDim.x;
+    u32x4 ring[PPT];
+    auto fetch = [&](int64_t row) {
+        if (vec && row < R) {
+            const u32x4 *x = reinterpret_cast<const u32x4 *>(X + row * ldx);
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                if (tid + 256 * i < nvec) ring[i] = __builtin_nontemporal_load(x + tid + 256 * i);
+        }
+    };
+    fetch(blockIdx.x);
+    for (int64_t row = blockIdx.x; row < Rp; row += G) {
         const bool real_row = row < R;
         __syncthreads();                       // the previous row's gathers are done (and sperm is staged)
         if (real_row) {
-            const T *x = X + row * ldx;
             if (vec) {
-                for (int64_t v = tid; v < nvec; v += 256)
-                    reinterpret_cast<uint4 *>(srow)[v] = reinterpret_cast<const uint4 *>(x)[v];
+#pragma unroll
+                for (int i = 0; i < PPT; ++i)
+                    if (tid + 256 * i < nvec) reinterpret_cast<u32x4 *>(srow)[tid + 256 * i] = ring[i];
             } else {
+                const T *x = X + row * ldx;
                 for (int64_t j = tid; j < K; j += 256) srow[j] = x[j];
             }
         }
         __syncthreads();
+        fetch(row + G);                        // in flight while this row is quantized
         for (int64_t win = wave; win < nwin; win += 4) {
             int sg = 0;
             int64_t b;
@@ -429,16 +445,23 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
             const int s = (int)bs.byte - 127;
             const uint32_t anynz = quad_max_u32((lo | hi) != 0 ? 1u : 0u);   // whole quad, unconditionally
             const bool nz = real && !bad && anynz != 0;
-            // window reduction over the 16 blocks (lanes 4 apart)
-            int smax = nz ? s : -100000, smin = nz ? s : 100000, anybad = bad;
+            // window reduction over the 16 blocks (lanes 4 apart), one packed
+            // word per step: high half max(s), low half max(-s) = -min(s); a
+            // non-finite block enters as +32767 in both halves, which makes
+            // the window unaligned; blocks without nonzero codes as -32768
+            const int hi16 = nz ? s : (bad ? 32767 : -32768);
+            const int lo16 = nz ? -s : (bad ? 32767 : -32768);
+            uint32_t red = ((uint32_t)hi16 << 16) | ((uint32_t)lo16 & 0xFFFFu);
 #pragma unroll
             for (int off = 4; off < 64; off <<= 1) {
-                smax = max(smax, __shfl_xor(smax, off));
-                smin = min(smin, __shfl_xor(smin, off));
-                anybad |= __shfl_xor(anybad, off);
+                const uint32_t o = (uint32_t)__shfl_xor((int)red, off);
+                typedef short v2s __attribute__((ext_vector_type(2)));
+                const v2s m = __builtin_elementwise_max(__builtin_bit_cast(v2s, red), __builtin_bit_cast(v2s, o));
+                red = __builtin_bit_cast(uint32_t, m);
             }
-            const bool allzero = smax == -100000;
-            const bool aligned = !anybad && (allzero || smax - smin <= F);
+            const int smax = (int)(int16_t)(red >> 16), smin = -(int)(int16_t)(red & 0xFFFFu);
+            const bool allzero = smax == -32768;
+            const bool aligned = allzero || smax - smin <= F;
             const int base = allzero ? 0 : smax - F;
             const int shift = aligned ? (nz ? s - base : 0) : F;
             float scale;
@@ -1973,6 +1996,42 @@ ActPlanes act_planes(const mxs_qmat &A) {
 
 }  // namespace
 
+template <typename T, int PPT>
+hipError_t launch_quant_prep_t(const T *X, int64_t M, int64_t ldx, const int32_t *perm, int64_t K, int64_t Mp,
+                               int64_t Kp, const Segs &S, int8_t *ac, float *acs, int64_t lds, hipStream_t st) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_prep<T, PPT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+    if (e != hipSuccess) return e;
+    // as many workgroups as LDS allows (up to 8 per CU), each streaming its
+    // rows one ahead
+    const int64_t per_cu = (160 * 1024) / lds;
+    int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
+    blocks = blocks < Mp ? blocks : Mp;
+    hipLaunchKernelGGL((k_quant_prep<T, PPT>), dim3((unsigned)blocks), dim3(256), (size_t)lds, st, X, M, ldx, perm,
+                       K, Mp, Kp, S, ac, acs);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_quant_prep_d(const T *X, int64_t M, int64_t ldx, const int32_t *perm, int64_t K, int64_t Mp,
+                               int64_t Kp, const Segs &S, int8_t *ac, float *acs, int64_t lds, hipStream_t st) {
+    const int64_t ppt = ceil_div(ceil_div(K * (int64_t)sizeof(T), (int64_t)16), (int64_t)256);
+    if (ppt <= 1) return launch_quant_prep_t<T, 1>(X, M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    if (ppt <= 2) return launch_quant_prep_t<T, 2>(X, M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    if (ppt <= 4) return launch_quant_prep_t<T, 4>(X, M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    if (ppt <= 8) return launch_quant_prep_t<T, 8>(X, M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    if (ppt <= 16) return launch_quant_prep_t<T, 16>(X, M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_prep(const void *X, mxs_dtype dt, int64_t M, int64_t ldx, const int32_t *perm, int64_t K,
+                             int64_t Mp, int64_t Kp, const Segs &S, int8_t *ac, float *acs, hipStream_t st) {
+    const int64_t lds = quant_prep_lds(K, dt);
+    if (dt == MXS_BF16)
+        return launch_quant_prep_d(static_cast<const uint16_t *>(X), M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+    return launch_quant_prep_d(static_cast<const float *>(X), M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
+}
+
 size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W) {
     if (M == 0 || W.rows == 0) return 0;
     const mxs_qmat A = act_shape(M, W);
@@ -2009,25 +2068,7 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
     const Segs S = make_segs(A.n8, A.n6, A.n4);
     const int64_t nb = A.K / 32, nbp = L.Kp / 32;
     const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
-    const int64_t lds = quant_prep_lds(A.K, dt);
-    const int64_t per_cu = (160 * 1024) / lds;
-    int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
-    blocks = blocks < L.Mp ? blocks : L.Mp;
-    hipError_t e;
-    if (dt == MXS_BF16) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_prep<uint16_t>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_quant_prep<uint16_t>, dim3((unsigned)blocks), dim3(256), (size_t)lds, st,
-                           static_cast<const uint16_t *>(X), M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs);
-    } else {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_prep<float>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_quant_prep<float>, dim3((unsigned)blocks), dim3(256), (size_t)lds, st,
-                           static_cast<const float *>(X), M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs);
-    }
-    e = hipGetLastError();
+    hipError_t e = launch_quant_prep(X, dt, M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs, st);
     if (e != hipSuccess) return e;
     PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
     const int64_t tw = jw.tiles_r * windows;
