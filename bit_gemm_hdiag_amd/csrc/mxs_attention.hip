@@ -47,6 +47,29 @@ constexpr int kAMaxD = 256;     // head dimension
 constexpr int kAWaves = 2048;   // waves the split aims at
 
 typedef float v4f_a __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf_a __attribute__((ext_vector_type(8)));
+
+// x = h + m + l exactly: three bf16 parts, each the nearest bf16 to what is
+// left (every remainder is exact in fp32; the last one has at most 8
+// significant bits)
+// bf16 pair (lo, hi) of two fp32 values whose low 16 bits are zero (codes
+// times a power of two), so taking the high halves is exact
+__device__ __forceinline__ uint32_t bf16x2_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+typedef uint32_t v4u_a __attribute__((ext_vector_type(4)));
+
+struct Bf3 {
+    __bf16 h, m, l;
+};
+__device__ __forceinline__ Bf3 split3(float x) {
+    Bf3 t;
+    t.h = (__bf16)x;
+    const float r = x - (float)t.h;
+    t.m = (__bf16)r;
+    t.l = (__bf16)(r - (float)t.m);
+    return t;
+}
 
 // sign-extended 4-bit field k of w (k compile-time)
 __device__ __forceinline__ float nib(uint32_t w, int k) {
@@ -185,9 +208,11 @@ __device__ __forceinline__ void load_v(VChunk<ND> &ch, const AttnSrc &a, int lt0
 }
 
 // Scores (log2 units) of the sub-chunk: lane (i, c) gets head i's scores of
-// tokens lt0 + 16 u + 4 c + r, -inf past the wave's last token.
+// tokens lt0 + 16 u + 4 c + r, -inf past the wave's last token. Step b of
+// a tile takes the lane group's dword b of K (8 dims; code x scale is exact
+// in bf16) against the three bf16 parts of the query.
 template <int ND>
-__device__ __forceinline__ void attn_scores(const KChunk<ND> &ch, const float qv[8 * ND], int lt0, int nt,
+__device__ __forceinline__ void attn_scores(const KChunk<ND> &ch, const v8bf_a qp[ND][3], int lt0, int nt,
                                             float scale2, int c, int kb0, float sv[4][4]) {
     constexpr int DK = KGeom<ND>::DK, KNB = KGeom<ND>::NB;
     float ksc[4][KNB];
@@ -199,11 +224,18 @@ __device__ __forceinline__ void attn_scores(const KChunk<ND> &ch, const float qv
 #pragma unroll
     for (int u = 0; u < 4; ++u) sc4[u] = v4f_a{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < DK; ++s)
+    for (int b = 0; b < ND; ++b)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float kv = nib(ch.w[u][s >> 3], s & 7) * pick_scale<KNB, ND % 4 == 0>(ksc[u], c * DK, kb0, s);
-            sc4[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, qv[s], sc4[u], 0, 0, 0);
+            float kf[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                kf[n] = nib(ch.w[u][b], n) * pick_scale<KNB, ND % 4 == 0>(ksc[u], c * DK, kb0, 8 * b + n);
+            const v4u_a kw2 = {bf16x2_exact(kf[0], kf[1]), bf16x2_exact(kf[2], kf[3]), bf16x2_exact(kf[4], kf[5]),
+                               bf16x2_exact(kf[6], kf[7])};
+            const v8bf_a kv = __builtin_bit_cast(v8bf_a, kw2);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) sc4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qp[b][p], sc4[u], 0, 0, 0);
         }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -254,20 +286,37 @@ __device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND> 
     st.l += lsum;
     st.m = m_new;
 
-    // tokens in order of tile and step, dims i DL + n of tile n
+    // 32 tokens per step: lane group c contributes tokens 4 c + r of tiles
+    // u0 and u0 + 1 (the ones whose p it holds), V as exact bf16 values of
+    // dims i DL + n (tile n), p as three bf16 parts
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u0 = 0; u0 < 4; u0 += 2) {
+        v8bf_a pb[3];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float vsc[VNB];
-#pragma unroll
-            for (int b = 0; b < VNB; ++b) vsc[b] = e8m0_to_f32(ch.sb[u][r][b]);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float vv = nib(ch.w[u][r][n >> 3], n & 7) * pick_scale<VNB, false>(vsc, i * DL, vb0, n);
-                st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sv[u][r], st.acc[n], 0, 0, 0);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const Bf3 t = split3(sv[u0 + (j >> 2)][j & 3]);
+            pb[0][j] = t.h;
+            pb[1][j] = t.m;
+            pb[2][j] = t.l;
         }
+        float vsc[8][VNB];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int b = 0; b < VNB; ++b) vsc[j][b] = e8m0_to_f32(ch.sb[u0 + (j >> 2)][j & 3][b]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            float vf[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                vf[j] = nib(ch.w[u0 + (j >> 2)][j & 3][n >> 3], n & 7) * pick_scale<VNB, false>(vsc[j], i * DL, vb0, n);
+            const v4u_a vw2 = {bf16x2_exact(vf[0], vf[1]), bf16x2_exact(vf[2], vf[3]), bf16x2_exact(vf[4], vf[5]),
+                               bf16x2_exact(vf[6], vf[7])};
+            const v8bf_a vv = __builtin_bit_cast(v8bf_a, vw2);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[p], st.acc[n], 0, 0, 0);
+        }
+    }
 }
 
 // Waves per workgroup: eight where a wave fits in 256 VGPRs (D = 32, 64,
@@ -321,14 +370,21 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
         a.voff = i * ND;
         a.vso = vb0;
 
-        // query column of head i (zero for the padding heads), dims c DK + s
-        float qv[DK];
+        // query column of head i (zero for the padding heads), dims c DK + s,
+        // as three bf16 parts per step of 8 dims
+        v8bf_a qp[ND][3];
         {
-            const float *qp = q + ((int64_t)g * G + (i < G ? i : 0)) * D + c * DK;
+            const float *qs = q + ((int64_t)g * G + (i < G ? i : 0)) * D + c * DK;
+            float qv[DK];
 #pragma unroll
-            for (int s = 0; s < DK; ++s) qv[s] = qp[s];
+            for (int s = 0; s < DK; ++s) qv[s] = qs[s];
 #pragma unroll
-            for (int s = 0; s < DK; ++s) qv[s] = i < G ? qv[s] : 0.f;
+            for (int s = 0; s < DK; ++s) {
+                const Bf3 t = split3(i < G ? qv[s] : 0.f);
+                qp[s >> 3][0][s & 7] = t.h;
+                qp[s >> 3][1][s & 7] = t.m;
+                qp[s >> 3][2][s & 7] = t.l;
+            }
         }
         KChunk<ND> kch;
         VChunk<ND> vch;
@@ -342,7 +398,7 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
         // barriers keep the loads ahead of the work they overlap)
         for (int lt = 0; lt < nt; lt += kASub) {
             float sv[4][4];
-            attn_scores<ND>(kch, qv, lt, nt, scale2, c, kb0, sv);
+            attn_scores<ND>(kch, qp, lt, nt, scale2, c, kb0, sv);
             load_k<ND>(kch, a, lt + kASub, i);
             __builtin_amdgcn_sched_barrier(0);
             attn_values<ND>(st, vch, sv, i, vb0);
