@@ -195,10 +195,12 @@ mxs_status mxs_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *ks, 
     if (T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || D < 32 || D % 32)
         return fail(MXS_ERR_SHAPE, "attend_kv4: T=%lld Hq=%lld Hkv=%lld D=%lld", (long long)T, (long long)Hq,
                     (long long)Hkv, (long long)D);
-    if (!mxs::attend_kv4_supported(Hq, Hkv, D) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(q, 4))
-        return fail(MXS_ERR_UNSUPPORTED, "attend_kv4: needs Hq/Hkv <= 16, D <= 256 and 16-byte aligned codes");
+    if (!mxs::attend_kv4_supported(Hq, Hkv, D) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(q, 4) ||
+        !aligned(out, 16))
+        return fail(MXS_ERR_UNSUPPORTED, "attend_kv4: needs Hq/Hkv <= 16, D <= 256, 16-byte aligned codes and output");
     if (T > (int64_t)65535 * 64) return fail(MXS_ERR_UNSUPPORTED, "attend_kv4: T=%lld too long", (long long)T);
-    if (ws_bytes < mxs::attend_kv4_workspace(T, Hq, Hkv, D)) return fail(MXS_ERR_WORKSPACE, "attend_kv4: workspace too small");
+    if (ws_bytes < mxs::attend_kv4_workspace(T, Hq, Hkv, D) || !aligned(ws, 16))
+        return fail(MXS_ERR_WORKSPACE, "attend_kv4: workspace too small or not 16-byte aligned");
     return device_status(mxs::launch_attend_kv4(q, kc, ks, vc, vs, T, Hq, Hkv, D, scale, out, ws, stream),
                          "attend_kv4");
 }

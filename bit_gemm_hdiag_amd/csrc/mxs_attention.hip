@@ -41,7 +41,7 @@ namespace mxs {
 
 namespace {
 
-constexpr int kASub = 64;       // tokens per sub-chunk (four 16-token tiles)
+constexpr int kATile = 16;      // tokens per matrix tile; a sub-chunk is NTL = 2 or 4 tiles
 constexpr int kAMaxG = 16;      // query heads per KV head (MFMA rows)
 constexpr int kAMaxD = 256;     // head dimension
 constexpr int kAWaves = 2048;   // waves the split aims at
@@ -74,6 +74,34 @@ __device__ __forceinline__ Bf3 split3(float x) {
 // sign-extended 4-bit field k of w (k compile-time)
 __device__ __forceinline__ float nib(uint32_t w, int k) {
     return (float)((int32_t)(w << (28 - 4 * k)) >> 28);
+}
+
+// the 8 fields of w divided by 16 (v_cvt_off_f32_i4 reads bits 3:0 of the
+// selected byte: even fields straight from w, odd ones from w >> 4; exact);
+// the factor 16 goes into the other operand of the product
+template <int SEL>
+__device__ __forceinline__ float cvt_off_byte(uint32_t w) {
+    float r;
+    if constexpr (SEL == 0)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (SEL == 1)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (SEL == 2)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+__device__ __forceinline__ void nib16x8(uint32_t w, float f[8]) {
+    const uint32_t o = w >> 4;
+    f[0] = cvt_off_byte<0>(w);
+    f[1] = cvt_off_byte<0>(o);
+    f[2] = cvt_off_byte<1>(w);
+    f[3] = cvt_off_byte<1>(o);
+    f[4] = cvt_off_byte<2>(w);
+    f[5] = cvt_off_byte<2>(o);
+    f[6] = cvt_off_byte<3>(w);
+    f[7] = cvt_off_byte<3>(o);
 }
 
 // Buffer resource over n bytes at p (reads at offsets >= n return zero)
@@ -151,15 +179,15 @@ __device__ __forceinline__ float pick_scale(const float sc[NB], int base, int b0
 // Raw codes and scale bytes of one sub-chunk as one lane loads them: K rows
 // lt0 + 16 u + i (lane group c's dims), V rows lt0 + 16 u + 4 c + r (lane
 // i's dims).
-template <int ND>
+template <int ND, int NTL>
 struct KChunk {
-    uint32_t w[4][ND];
-    uint32_t sb[4][KGeom<ND>::NB];
+    uint32_t w[NTL][ND];
+    uint32_t sb[NTL][KGeom<ND>::NB];
 };
-template <int ND>
+template <int ND, int NTL>
 struct VChunk {
-    uint32_t w[4][4][(ND + 3) / 4];
-    uint32_t sb[4][4][VGeom<ND>::NB];
+    uint32_t w[NTL][4][(ND + 3) / 4];
+    uint32_t sb[NTL][4][VGeom<ND>::NB];
 };
 
 // Where one wave reads: the cache rows of its KV head from its first token
@@ -173,14 +201,14 @@ struct AttnSrc {
 
 // Rows past the wave's last token read as zero (the buffer ends there), so
 // the tail needs no clamping: zero codes, and the scale byte 0 gives value 0.
-template <int ND>
-__device__ __forceinline__ void load_k(KChunk<ND> &ch, const AttnSrc &a, int lt0, int i) {
+template <int ND, int NTL>
+__device__ __forceinline__ void load_k(KChunk<ND, NTL> &ch, const AttnSrc &a, int lt0, int i) {
     constexpr int D = 32 * ND, KNB = KGeom<ND>::NB;
     const int64_t left = a.nt - 1 - lt0;       // rows still valid after lt0
     const auto rc = attn_rsrc(a.kc + (int64_t)lt0 * a.rowb, left * a.rowb + D / 2);
     const auto rs = attn_rsrc(a.ks + (int64_t)lt0 * a.srow, left * a.srow + ND);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NTL; ++u) {
         load_words<ND>(rc, __umul24(16 * u + i, a.rowb) + a.koff, ch.w[u]);
 #pragma unroll
         for (int b = 0; b < KNB; ++b) {
@@ -189,14 +217,14 @@ __device__ __forceinline__ void load_k(KChunk<ND> &ch, const AttnSrc &a, int lt0
     }
 }
 
-template <int ND>
-__device__ __forceinline__ void load_v(VChunk<ND> &ch, const AttnSrc &a, int lt0, int c) {
+template <int ND, int NTL>
+__device__ __forceinline__ void load_v(VChunk<ND, NTL> &ch, const AttnSrc &a, int lt0, int c) {
     constexpr int D = 32 * ND, VNB = VGeom<ND>::NB;
     const int64_t left = a.nt - 1 - lt0;
     const auto rc = attn_rsrc(a.vc + (int64_t)lt0 * a.rowb, left * a.rowb + D / 2);
     const auto rs = attn_rsrc(a.vs + (int64_t)lt0 * a.srow, left * a.srow + ND);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             load_bytes<ND>(rc, __umul24(16 * u + 4 * c + r, a.rowb) + a.voff, ch.w[u][r]);
@@ -211,26 +239,26 @@ __device__ __forceinline__ void load_v(VChunk<ND> &ch, const AttnSrc &a, int lt0
 // tokens lt0 + 16 u + 4 c + r, -inf past the wave's last token. Step b of
 // a tile takes the lane group's dword b of K (8 dims; code x scale is exact
 // in bf16) against the three bf16 parts of the query.
-template <int ND>
-__device__ __forceinline__ void attn_scores(const KChunk<ND> &ch, const v8bf_a qp[ND][3], int lt0, int nt,
-                                            float scale2, int c, int kb0, float sv[4][4]) {
+template <int ND, int NTL>
+__device__ __forceinline__ void attn_scores(const KChunk<ND, NTL> &ch, const v8bf_a qp[ND][3], int lt0, int nt,
+                                            float scale2, int c, int kb0, float sv[NTL][4]) {
     constexpr int DK = KGeom<ND>::DK, KNB = KGeom<ND>::NB;
-    float ksc[4][KNB];
+    float ksc[NTL][KNB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
         for (int b = 0; b < KNB; ++b) ksc[u][b] = e8m0_to_f32(ch.sb[u][b]);
-    v4f_a sc4[4];
+    v4f_a sc4[NTL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sc4[u] = v4f_a{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NTL; ++u) sc4[u] = v4f_a{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < ND; ++b)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NTL; ++u) {
             float kf[8];
+            nib16x8(ch.w[u][b], kf);
 #pragma unroll
-            for (int n = 0; n < 8; ++n)
-                kf[n] = nib(ch.w[u][b], n) * pick_scale<KNB, ND % 4 == 0>(ksc[u], c * DK, kb0, 8 * b + n);
+            for (int n = 0; n < 8; ++n) kf[n] *= pick_scale<KNB, ND % 4 == 0>(ksc[u], c * DK, kb0, 8 * b + n);
             const v4u_a kw2 = {bf16x2_exact(kf[0], kf[1]), bf16x2_exact(kf[2], kf[3]), bf16x2_exact(kf[4], kf[5]),
                                bf16x2_exact(kf[6], kf[7])};
             const v8bf_a kv = __builtin_bit_cast(v8bf_a, kw2);
@@ -238,7 +266,7 @@ __device__ __forceinline__ void attn_scores(const KChunk<ND> &ch, const v8bf_a q
             for (int p = 0; p < 3; ++p) sc4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qp[b][p], sc4[u], 0, 0, 0);
         }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[u][r] = lt0 + 16 * u + 4 * c + r < nt ? sc4[u][r] * scale2 : -INFINITY;
 }
@@ -254,13 +282,13 @@ struct AttnState {
 
 // Folds the sub-chunk's scores into the running maximum and sum (sv becomes
 // p = 2^(s - m)), then adds p V to the accumulators.
-template <int ND>
-__device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND> &ch, float sv[4][4], int i,
+template <int ND, int NTL>
+__device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND, NTL> &ch, float sv[NTL][4], int i,
                                             int vb0) {
     constexpr int DL = VGeom<ND>::DL, VNB = VGeom<ND>::NB, NT = 2 * ND;
     float mloc = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sv[u][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
@@ -268,7 +296,7 @@ __device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND> 
     const float m_new = fmaxf(st.m, mloc);
     float lsum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             sv[u][r] = sv[u][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[u][r] - m_new);
@@ -290,11 +318,11 @@ __device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND> 
     // u0 and u0 + 1 (the ones whose p it holds), V as exact bf16 values of
     // dims i DL + n (tile n), p as three bf16 parts
 #pragma unroll
-    for (int u0 = 0; u0 < 4; u0 += 2) {
+    for (int u0 = 0; u0 < NTL; u0 += 2) {
         v8bf_a pb[3];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const Bf3 t = split3(sv[u0 + (j >> 2)][j & 3]);
+            const Bf3 t = split3(16.f * sv[u0 + (j >> 2)][j & 3]);   // V enters as code / 16
             pb[0][j] = t.h;
             pb[1][j] = t.m;
             pb[2][j] = t.l;
@@ -304,12 +332,25 @@ __device__ __forceinline__ void attn_values(AttnState<ND> &st, const VChunk<ND> 
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int b = 0; b < VNB; ++b) vsc[j][b] = e8m0_to_f32(ch.sb[u0 + (j >> 2)][j & 3][b]);
+        // the lane's 2 ND values of each of its 8 rows (code / 16)
+        float vr[8][NT];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float f[8];
+            nib16x8(ch.w[u0 + (j >> 2)][j & 3][0], f);
+#pragma unroll
+            for (int n = 0; n < NT && n < 8; ++n) vr[j][n] = f[n];
+            if constexpr (NT > 8) {
+                nib16x8(ch.w[u0 + (j >> 2)][j & 3][1], f);
+#pragma unroll
+                for (int n = 8; n < NT; ++n) vr[j][n] = f[n - 8];
+            }
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             float vf[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vf[j] = nib(ch.w[u0 + (j >> 2)][j & 3][n >> 3], n & 7) * pick_scale<VNB, false>(vsc[j], i * DL, vb0, n);
+            for (int j = 0; j < 8; ++j) vf[j] = vr[j][n] * pick_scale<VNB, false>(vsc[j], i * DL, vb0, n);
             const v4u_a vw2 = {bf16x2_exact(vf[0], vf[1]), bf16x2_exact(vf[2], vf[3]), bf16x2_exact(vf[4], vf[5]),
                                bf16x2_exact(vf[6], vf[7])};
             const v8bf_a vv = __builtin_bit_cast(v8bf_a, vw2);
@@ -330,7 +371,7 @@ struct AttnWg {
 // LDS of one workgroup: per wave, (m, l) and O of every query head of its group
 __host__ __device__ constexpr int attn_lds_bytes(int NW, int G, int D) { return NW * G * (D + 2) * 4; }
 
-template <int ND>
+template <int ND, int NTL>
 __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
     const float *__restrict__ q, const uint8_t *__restrict__ kc, const uint8_t *__restrict__ ks,
     const uint8_t *__restrict__ vc, const uint8_t *__restrict__ vs, int64_t T, int Hkv, int G, int HW, int NQ,
@@ -380,29 +421,30 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
             for (int s = 0; s < DK; ++s) qv[s] = qs[s];
 #pragma unroll
             for (int s = 0; s < DK; ++s) {
-                const Bf3 t = split3(i < G ? qv[s] : 0.f);
+                const Bf3 t = split3(i < G ? 16.f * qv[s] : 0.f);   // K enters as code / 16
                 qp[s >> 3][0][s & 7] = t.h;
                 qp[s >> 3][1][s & 7] = t.m;
                 qp[s >> 3][2][s & 7] = t.l;
             }
         }
-        KChunk<ND> kch;
-        VChunk<ND> vch;
-        load_k<ND>(kch, a, 0, i);
-        load_v<ND>(vch, a, 0, c);
+        constexpr int SUB = kATile * NTL;                        // tokens per sub-chunk
+        KChunk<ND, NTL> kch;
+        VChunk<ND, NTL> vch;
+        load_k<ND, NTL>(kch, a, 0, i);
+        load_v<ND, NTL>(vch, a, 0, c);
         __builtin_amdgcn_sched_barrier(0);
 
         // software pipeline: the next sub-chunk's K loads fly while this
         // one's values are summed, its V loads while the next scores are
         // formed; one copy of each phase keeps the code small (scheduling
         // barriers keep the loads ahead of the work they overlap)
-        for (int lt = 0; lt < nt; lt += kASub) {
-            float sv[4][4];
-            attn_scores<ND>(kch, qp, lt, nt, scale2, c, kb0, sv);
-            load_k<ND>(kch, a, lt + kASub, i);
+        for (int lt = 0; lt < nt; lt += SUB) {
+            float sv[NTL][4];
+            attn_scores<ND, NTL>(kch, qp, lt, nt, scale2, c, kb0, sv);
+            load_k<ND, NTL>(kch, a, lt + SUB, i);
             __builtin_amdgcn_sched_barrier(0);
-            attn_values<ND>(st, vch, sv, i, vb0);
-            load_v<ND>(vch, a, lt + kASub, c);
+            attn_values<ND, NTL>(st, vch, sv, i, vb0);
+            load_v<ND, NTL>(vch, a, lt + SUB, c);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -448,17 +490,20 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
 }
 
 // o[h, d] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) (maxima in log2
-// units, which the split kernel works in). One workgroup
-// per head: thread (d, ph) sums the splits ph, ph + P, ... in order (P =
-// 256 / D phases), then the phases are added in order.
+// units, which the split kernel works in). One workgroup per head: thread
+// (d4, ph) takes four dims d4 and the splits ph, ph + P, ... in order
+// (P = 256 / (D / 4) phases, loads issued several splits ahead), then the
+// phases are added in order.
 __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ pm, const float *__restrict__ pl,
                                                       const float *__restrict__ po, int64_t nsplit, int D,
                                                       float *__restrict__ out) {
     __shared__ float red[256];
-    __shared__ float sa[256], sl[256];
+    __shared__ float4 sa[256];
+    __shared__ float sl[256];
     const int64_t h = blockIdx.x;
     const int tid = threadIdx.x;
-    const float *hm = pm + h * nsplit, *hl = pl + h * nsplit, *ho = po + h * nsplit * D;
+    const float *hm = pm + h * nsplit, *hl = pl + h * nsplit;
+    const float4 *ho = reinterpret_cast<const float4 *>(po + h * nsplit * D);
     float m = -INFINITY;
     for (int64_t s = tid; s < nsplit; s += 256) m = fmaxf(m, hm[s]);
     red[tid] = m;
@@ -468,44 +513,58 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
         __syncthreads();
     }
     const float M = red[0];
-    const int P = 256 / D, d = tid % D, ph = tid / D;
-    float acc = 0.f, l = 0.f;
+    const int D4 = D / 4, P = 256 / D4, d4 = tid % D4, ph = tid / D4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
     if (ph < P) {
 #pragma unroll 4
         for (int64_t s = ph; s < nsplit; s += P) {
             const float f = __builtin_amdgcn_exp2f(hm[s] - M);
+            const float4 v = ho[s * D4 + d4];
             l = __builtin_fmaf(hl[s], f, l);
-            acc = __builtin_fmaf(ho[s * D + d], f, acc);
+            acc.x = __builtin_fmaf(v.x, f, acc.x);
+            acc.y = __builtin_fmaf(v.y, f, acc.y);
+            acc.z = __builtin_fmaf(v.z, f, acc.z);
+            acc.w = __builtin_fmaf(v.w, f, acc.w);
         }
     }
     sa[tid] = acc;
     sl[tid] = l;
     __syncthreads();
-    if (tid < D) {
-        float a = 0.f, L = 0.f;
-        for (int p = 0; p < P; ++p) {
-            a += sa[p * D + tid];
-            L += sl[p * D + tid];
+    if (tid < D4) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        float L = 0.f;
+        for (int q = 0; q < P; ++q) {
+            const float4 v = sa[q * D4 + tid];
+            a.x += v.x;
+            a.y += v.y;
+            a.z += v.z;
+            a.w += v.w;
+            L += sl[q * D4 + tid];
         }
-        out[h * D + tid] = a / L;
+        reinterpret_cast<float4 *>(out + h * D)[tid] = make_float4(a.x / L, a.y / L, a.z / L, a.w / L);
     }
 }
 
-// Split of the cache: TSw tokens per wave (a multiple of 64 chosen so that
-// about 2048 waves run); a workgroup takes HW KV heads (two when there are
+// Split of the cache: sub-chunks of 64 tokens (32 when there are fewer than
+// 4096 sub-chunks of 64, so that short caches still fill the chip); TSw
+// tokens per wave, a multiple of the sub-chunk chosen so that about 2048
+// waves run; a workgroup takes HW KV heads (two when there are
 // enough waves: two heads fill a 128-byte line of every cache row) and NQ
 // consecutive token parts of TSw tokens, as many as keep 256 or more
 // workgroups busy, at most the waves one workgroup may hold.
 struct AttnSplit {
-    int HW, NQ, TSw;
+    int NTL, HW, NQ, TSw;
     int64_t ns;
 };
 
 AttnSplit attn_split(int64_t T, int64_t Hkv, int64_t D) {
     AttnSplit s;
-    int64_t sub = ceil_div(ceil_div(T, (int64_t)kASub) * Hkv, (int64_t)kAWaves);
+    s.NTL = ceil_div(T, (int64_t)4 * kATile) * Hkv >= 2 * kAWaves ? 4 : 2;
+    const int64_t SUB = (int64_t)kATile * s.NTL;
+    int64_t sub = ceil_div(ceil_div(T, SUB) * Hkv, (int64_t)kAWaves);
     if (sub < 1) sub = 1;
-    s.TSw = (int)(sub * kASub);
+    s.TSw = (int)(sub * SUB);
     const int64_t waves = ceil_div(T, (int64_t)s.TSw) * Hkv;
     s.HW = Hkv >= 2 && waves >= 512 ? 2 : 1;
     const int nwmax = attn_waves((int)(D / 32));
@@ -522,8 +581,13 @@ hipError_t launch_part(const AttnSplit &sp, int64_t Hkv, int G, hipStream_t st, 
     const int nw = sp.HW * sp.NQ;
     if (nw > AttnWg<ND>::NW) return hipErrorInvalidValue;
     const dim3 grid((unsigned)sp.ns, (unsigned)ceil_div(Hkv, (int64_t)sp.HW));
-    hipLaunchKernelGGL(k_attn_part<ND>, grid, dim3(64 * nw), (size_t)attn_lds_bytes(nw, G, 32 * ND), st, q, kc, ks,
-                       vc, vs, T, (int)Hkv, G, sp.HW, sp.NQ, sp.TSw, scale2, pm, pl, po);
+    const size_t lds = (size_t)attn_lds_bytes(nw, G, 32 * ND);
+    if (sp.NTL == 4)
+        hipLaunchKernelGGL((k_attn_part<ND, 4>), grid, dim3(64 * nw), lds, st, q, kc, ks, vc, vs, T, (int)Hkv, G,
+                           sp.HW, sp.NQ, sp.TSw, scale2, pm, pl, po);
+    else
+        hipLaunchKernelGGL((k_attn_part<ND, 2>), grid, dim3(64 * nw), lds, st, q, kc, ks, vc, vs, T, (int)Hkv, G,
+                           sp.HW, sp.NQ, sp.TSw, scale2, pm, pl, po);
     return hipGetLastError();
 }
 
@@ -542,7 +606,8 @@ hipError_t launch_attend_kv4(const float *q, const uint8_t *kc, const uint8_t *k
                              float *out, void *ws, hipStream_t st) {
     const AttnSplit sp = attn_split(T, Hkv, D);
     const int G = (int)(Hq / Hkv);
-    float *pm = static_cast<float *>(ws), *pl = pm + sp.ns * Hq, *po = pl + sp.ns * Hq;
+    // partial outputs first (16-byte aligned with the workspace), then maxima and sums
+    float *po = static_cast<float *>(ws), *pm = po + sp.ns * Hq * D, *pl = pm + sp.ns * Hq;
     const float scale2 = scale * 1.44269504088896341f;   // scores in log2 units: 2^(s log2 e) = e^s
     hipError_t e;
     switch (D / 32) {

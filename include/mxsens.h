@@ -324,9 +324,10 @@ mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H
  * definition within the rounding of the score dot products, the
  * exponentials and the T-term sums.
  * q: [Hq, D] fp32; kc, vc: [T, Hkv, D/2] uint8 codes (16-byte aligned);
- * ks, vs: [T, Hkv, D/32] uint8 E8M0 scales; out: [Hq, D] fp32. All device
- * pointers owned by the caller; ws >= mxs_attend_kv4_workspace(T, Hq, Hkv, D)
- * bytes; asynchronous on `stream`. Hq / Hkv <= 16, D <= 256, D % 32 == 0,
+ * ks, vs: [T, Hkv, D/32] uint8 E8M0 scales; out: [Hq, D] fp32 (16-byte
+ * aligned). All device pointers owned by the caller; ws >=
+ * mxs_attend_kv4_workspace(T, Hq, Hkv, D) bytes, 16-byte aligned;
+ * asynchronous on `stream`. Hq / Hkv <= 16, D <= 256, D % 32 == 0,
  * T <= 65535 * 64.
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE, MXS_ERR_UNSUPPORTED, MXS_ERR_WORKSPACE,
  * MXS_ERR_DEVICE.

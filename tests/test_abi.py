@@ -237,7 +237,7 @@ def test_attend_kv4_errors(lib):
     lib.mxs_attend_kv4_workspace.restype = ctypes.c_size_t
     lib.mxs_attend_kv4_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     need = lib.mxs_attend_kv4_workspace(300, 8, 2, 64)
-    assert need == 5 * 8 * (2 + 64) * 4               # 64 tokens per workgroup: 5 splits
+    assert need == 10 * 8 * (2 + 64) * 4              # 32 tokens per workgroup: 10 splits
     a = P(4096)            # never dereferenced: every call below fails validation
     args = lambda **kw: [kw.get(k, v) for k, v in (("q", a), ("kc", a), ("ks", a), ("vc", a), ("vs", a), ("T", 300),
                                                  ("Hq", 8), ("Hkv", 2), ("D", 64), ("s", 0.1), ("o", a), ("ws", a),
