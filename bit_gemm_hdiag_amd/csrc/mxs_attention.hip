@@ -411,28 +411,30 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
         a.voff = i * ND;
         a.vso = vb0;
 
-        // query column of head i (zero for the padding heads), dims c DK + s,
-        // as three bf16 parts per step of 8 dims
-        v8bf_a qp[ND][3];
+        // query column of head i (zero for the padding heads), dims c DK + s;
+        // its loads go out first, then the first sub-chunk's, and the query
+        // is split into three bf16 parts per step of 8 dims while those fly
+        float qv[DK];
         {
             const float *qs = q + ((int64_t)g * G + (i < G ? i : 0)) * D + c * DK;
-            float qv[DK];
 #pragma unroll
             for (int s = 0; s < DK; ++s) qv[s] = qs[s];
-#pragma unroll
-            for (int s = 0; s < DK; ++s) {
-                const Bf3 t = split3(i < G ? 16.f * qv[s] : 0.f);   // K enters as code / 16
-                qp[s >> 3][0][s & 7] = t.h;
-                qp[s >> 3][1][s & 7] = t.m;
-                qp[s >> 3][2][s & 7] = t.l;
-            }
         }
+        __builtin_amdgcn_sched_barrier(0);
         constexpr int SUB = kATile * NTL;                        // tokens per sub-chunk
         KChunk<ND, NTL> kch;
         VChunk<ND, NTL> vch;
         load_k<ND, NTL>(kch, a, 0, i);
         load_v<ND, NTL>(vch, a, 0, c);
         __builtin_amdgcn_sched_barrier(0);
+        v8bf_a qp[ND][3];
+#pragma unroll
+        for (int s = 0; s < DK; ++s) {
+            const Bf3 t = split3(i < G ? 16.f * qv[s] : 0.f);   // K enters as code / 16
+            qp[s >> 3][0][s & 7] = t.h;
+            qp[s >> 3][1][s & 7] = t.m;
+            qp[s >> 3][2][s & 7] = t.l;
+        }
 
         // software pipeline: the next sub-chunk's K loads fly while this
         // one's values are summed, its V loads while the next scores are
@@ -449,7 +451,22 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
         }
     }
 
-    // to LDS: lane (i, c), tile n, register rr holds O[head i][dim (4 c + rr) DL + n]
+    // lane (i, c), tile n, register rr holds O[head i][dim (4 c + rr) DL + n]
+    if (NQ == 1) {   // one token part per workgroup: straight to the split outputs
+        if (i < G && g < Hkv) {
+            const int64_t hs = ((int64_t)g * G + i) * nsplit + split;
+            if (c == 0) {
+                pm[hs] = st.m;
+                pl[hs] = st.l;
+            }
+            float *op = po + hs * D;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) op[(4 * c + rr) * DL + n] = st.acc[n][rr];
+        }
+        return;
+    }
     if (i < G) {
         if (c == 0) {
             sml[(w * G + i) * 2] = st.m;
@@ -465,26 +482,37 @@ __global__ __launch_bounds__(64 * AttnWg<ND>::NW) void k_attn_part(
 
     // merge the token parts of each head in part order: M = max m_p,
     // O = sum_p O_p 2^(m_p - M), l = sum_p l_p 2^(m_p - M); part 0 always
-    // has tokens, so M is finite
-    for (int e = threadIdx.x; e < HW * G * D; e += 64 * NW) {
-        const int gl = e / (G * D), h = (e / D) % G, d = e % D;
+    // has tokens, so M is finite. Thread t takes elements t, t + B, ... of
+    // the (head row gh, dim d) grid, (gh, d) stepped without division
+    // (HW <= 2, so the KV head of row gh is gh >= G)
+    const int B = 64 * NW, Bq = B / D, Bd = B - Bq * D;
+    int gh = threadIdx.x / D, d = threadIdx.x - gh * D;
+    while (gh < HW * G) {
+        const int gl = gh >= G ? 1 : 0, h = gh - gl * G;
         const int gg = blockIdx.y * HW + gl;
-        if (gg >= Hkv) continue;
-        float M = -INFINITY;
-        for (int p = 0; p < NQ; ++p) M = fmaxf(M, sml[((p * HW + gl) * G + h) * 2]);
-        float o = 0.f, l = 0.f;
-        for (int p = 0; p < NQ; ++p) {
-            const int wp = p * HW + gl;
-            const float mp = sml[(wp * G + h) * 2];
-            const float f = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
-            o = __builtin_fmaf(so[(wp * G + h) * D + d], f, o);
-            l = __builtin_fmaf(sml[(wp * G + h) * 2 + 1], f, l);
+        if (gg < Hkv) {
+            float M = -INFINITY;
+            for (int p = 0; p < NQ; ++p) M = fmaxf(M, sml[((p * HW + gl) * G + h) * 2]);
+            float o = 0.f, l = 0.f;
+            for (int p = 0; p < NQ; ++p) {
+                const int wp = p * HW + gl;
+                const float mp = sml[(wp * G + h) * 2];
+                const float f = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+                o = __builtin_fmaf(so[(wp * G + h) * D + d], f, o);
+                l = __builtin_fmaf(sml[(wp * G + h) * 2 + 1], f, l);
+            }
+            const int64_t hs = ((int64_t)gg * G + h) * nsplit + split;
+            po[hs * D + d] = o;
+            if (d == 0) {
+                pm[hs] = M;
+                pl[hs] = l;
+            }
         }
-        const int64_t hs = ((int64_t)gg * G + h) * nsplit + split;
-        po[hs * D + d] = o;
-        if (d == 0) {
-            pm[hs] = M;
-            pl[hs] = l;
+        d += Bd;
+        gh += Bq;
+        if (d >= D) {
+            d -= D;
+            ++gh;
         }
     }
 }
