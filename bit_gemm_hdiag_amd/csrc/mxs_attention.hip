@@ -9,29 +9,31 @@
 // Codes are dequantized exactly (code * 2^(byte - 127) is exact in fp32).
 //
 // Layout of the work: a workgroup takes two KV heads (one when there is
-// only one), so it reads whole 128-byte lines of every cache row, and a run
-// of consecutive tokens split into token parts, one wave per (head, part).
-// A wave keeps the query rows of its group in registers and walks its part
-// in 64-token sub-chunks with an online softmax in log2 units (running
+// only one, or too little work), so it reads whole 128-byte lines of every
+// cache row, and a run of consecutive tokens split into token parts, one
+// wave per (head, part). A wave walks its part in sub-chunks of 64 tokens
+// (32 for short caches) with an online softmax in log2 units (running
 // maximum m and sum l per head; the output and l are rescaled by
-// 2^(m_old - m_new) when some maximum grows). The next sub-chunk's loads are
-// issued before the current one is computed. Both contractions run on the
-// fp32 matrix cores (v_mfma_f32_16x16x4_f32: inputs and products in fp32,
-// heads padded to 16 columns):
-//   scores  S^T[t, h] = sum_d K[t, d] q[h, d]: A = K (16 tokens x 4 dims per
-//           step, lane (t, c) walks dims c D/4 .. c D/4 + D/4 - 1),
-//           B = q (held in registers);
-//   output  O^T[d, h] += sum_t V[t, d] p[t, h]: A = V (16 dims x 4 tokens,
-//           lane (i, c) holds dims i D/16 .. i D/16 + D/16 - 1 of the
-//           tokens 4c + r), B = p, which the score step leaves in exactly the
-//           lane layout B needs.
-// Codes are dequantized in registers (code * 2^(byte - 127), exact). Cache
-// reads go through buffer descriptors that end at the part's last row, so
-// rows past it read as zero (value 0; their scores are set to -inf). The
-// parts of a workgroup are merged in LDS in part order, giving one (m, l, O)
-// per head and workgroup; a second kernel combines the workgroups of a head
-// in order, o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M). Every sum
-// has a fixed order, so the result is deterministic.
+// 2^(m_old - m_new) when some maximum grows). The next sub-chunk's loads
+// are issued before the current one is computed. Both contractions run on
+// the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, heads padded to 16
+// columns) with exact products: a code times its power-of-two scale is
+// exact in bf16, and the fp32 query and softmax weights enter as the exact
+// sum of three bf16 parts (one instruction per part); only the fp32
+// accumulation rounds.
+//   scores  S^T[t, h] = sum_d K[t, d] q[h, d]: A = K (16 tokens x 32 dims
+//           per step, lane (t, c) takes 8 of its dims c D/4 .. c D/4 +
+//           D/4 - 1 per step), B = the query parts (held in registers);
+//   output  O^T[d, h] += sum_t V[t, d] p[t, h]: A = V (16 dims x 32 tokens,
+//           lane (i, c) holds dims i D/16 .. i D/16 + D/16 - 1 of tokens
+//           4c + r of two tiles), B = the parts of p, which the score step
+//           leaves in exactly the lane layout B needs.
+// Cache reads go through buffer descriptors that end at the part's last
+// row, so rows past it read as zero (value 0; their scores are set to
+// -inf). The parts of a workgroup are merged in LDS in part order, giving
+// one (m, l, O) per head and workgroup; a second kernel combines the
+// workgroups of a head in order, o = sum_s O_s 2^(m_s - M) / sum_s l_s
+// 2^(m_s - M). Every sum has a fixed order, so the result is deterministic.
 #include <cmath>
 
 #include "mxs_device.h"

@@ -319,10 +319,12 @@ mxs_status mxs_quantize_kv(const void *kv, mxs_dtype dtype, int64_t T, int64_t H
  * h reading KV head h / (Hq / Hkv):
  *     s_t = scale * sum_d q[h,d] K[t,g,d],  p = softmax_t(s),
  *     out[h,d] = sum_t p_t V[t,g,d],
- * with K, V dequantized exactly (code * 2^(byte - 127)). fp32 arithmetic,
- * every sum in a fixed order (deterministic); the result matches the fp64
- * definition within the rounding of the score dot products, the
- * exponentials and the T-term sums.
+ * with K, V dequantized exactly (code * 2^(byte - 127)). Exact products
+ * (the fp32 query and softmax weights enter the bf16 matrix cores as exact
+ * three-part sums) with fp32 sums, every sum in a fixed order
+ * (deterministic); the result matches the fp64 definition within the
+ * rounding of the score dot products, the exponentials and the T-term
+ * sums.
  * q: [Hq, D] fp32; kc, vc: [T, Hkv, D/2] uint8 codes (16-byte aligned);
  * ks, vs: [T, Hkv, D/32] uint8 E8M0 scales; out: [Hq, D] fp32 (16-byte
  * aligned). All device pointers owned by the caller; ws >=
