@@ -54,11 +54,14 @@ def bound(q, K, V, scale):
 
 # the long cases run the workgroups that hold two KV heads and several token
 # parts: 32740 ends in a ragged part, 30000 in an empty part, 12000 (three KV
-# heads) in a workgroup with one head missing
+# heads) in a workgroup with one head missing; then plain multi-head (32 KV
+# heads), the largest group (16 query heads per KV head) and one KV head with
+# D = 160
 @pytest.mark.parametrize("T,Hq,Hkv,D", [(1, 8, 8, 32), (5, 4, 2, 64), (300, 64, 8, 128), (2048, 64, 8, 128),
                                         (257, 16, 1, 256), (1000, 32, 4, 96), (513, 12, 3, 64),
                                         (32740, 32, 8, 128), (30000, 16, 8, 64), (12000, 12, 3, 64),
-                                        (20000, 8, 4, 96), (40000, 4, 2, 256)])
+                                        (20000, 8, 4, 96), (40000, 4, 2, 256),
+                                        (1000, 32, 32, 128), (4000, 64, 4, 64), (9000, 16, 1, 160)])
 def test_attend_kv4_matches_oracle(mx, orc, T, Hq, Hkv, D):
     seed = T * 7 + Hq + D
     Kf = synth.kv(T, Hkv, D, seed, device=DEV)
