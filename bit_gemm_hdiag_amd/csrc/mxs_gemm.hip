@@ -558,19 +558,19 @@ __device__ __forceinline__ void dma_issue(const DmaLanes &D, int st, int nstage,
 __global__ __launch_bounds__(512, 1) void k_gemm_dma(
     const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
     const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
-    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy) {
+    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy, int32_t gm) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
 
     // tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
-    // takes a contiguous run of tiles; runs sweep groups of 8 row-tiles
+    // takes a contiguous run of tiles; runs sweep groups of gm row-tiles
     const int64_t tilesM = Mp / kGBM, tilesN = Np / kGBN, ntiles = tilesM * tilesN;
     int64_t t = blockIdx.x;
     if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
-    const int64_t per_group = 8 * tilesN;
-    const int64_t gid = t / per_group, first_m = gid * 8;
-    const int64_t gsz = tilesM - first_m < 8 ? tilesM - first_m : 8;
+    const int64_t per_group = gm * tilesN;
+    const int64_t gid = t / per_group, first_m = gid * gm;
+    const int64_t gsz = tilesM - first_m < gm ? tilesM - first_m : gm;
     const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
     const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
     const int nstage = (nb + kDSB - 1) / kDSB;
@@ -1771,6 +1771,13 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ p
     Y[t * ldy + n] = v;
 }
 
+// Row-tiles per group of k_gemm_dma's tile order. When every tile runs in
+// the first wave of workgroups, each XCD's run of 32 tiles then spans 4 row-
+// by 8 column-tiles (8 MB of int8 operands at K = 4096 rather than 10 MB with
+// 8 by 4), which measured 2-3 % faster at 2048 x 4096 x 4096; shapes with
+// more tiles than CUs keep groups of 8 (4 measured 1-2 % slower there).
+int32_t tile_group(int64_t ntiles) { return ntiles <= 256 ? 4 : 8; }
+
 struct PrepLayout {
     int64_t Mp, Np, Kp;
     size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
@@ -1943,7 +1950,7 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
     hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
-                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
     return hipGetLastError();
 }
 
@@ -2077,7 +2084,7 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
     hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
-                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy);
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
     return hipGetLastError();
 }
 
