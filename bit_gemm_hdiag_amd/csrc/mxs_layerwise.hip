@@ -65,53 +65,15 @@ __device__ __forceinline__ void load8f<uint16_t>(const uint16_t *p, float v[8]) 
 // Lane l of a wave supplies row l % 32 of each operand; in MFMA step s it
 // contributes k = s (lanes 0..31) and k = 16 + s (lanes 32..63) of the stage.
 // Rows past M or N load zeros and are left out of the sum.
-template <typename T>
-__global__ __launch_bounds__(256) void k_outerr(const T *__restrict__ X, int64_t M, int64_t ldx,
-                                                const T *__restrict__ W, int64_t N, int64_t ldw, int64_t K,
-                                                const float *__restrict__ Yq, int64_t ldy,
-                                                double *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) float sx[kET * kEP];
-    __shared__ __attribute__((aligned(16))) float sw[kET * kEP];
-    __shared__ double red[256];
+// The tile's sum of squared differences from its 16 products per lane
+// (result register 4 q + r of lane l: row 8 q + 4 h + r, column l % 32).
+// All 16 Yq values are requested before any is used (rows and columns past
+// the matrix read its last row / column and are left out of the sum).
+__device__ __forceinline__ void tile_err(const float (&acc)[16], int64_t M, int64_t N, const float *__restrict__ Yq,
+                                         int64_t ldy, double *red, double *__restrict__ part) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
     const int64_t tm = (int64_t)blockIdx.y * kET, tn = (int64_t)blockIdx.x * kET;
-    const int lr = tid >> 2, lc = (tid & 3) * 8;          // load role: row, first column
-    const bool xin = tm + lr < M, win = tn + lr < N;
-    const T *xp = X + (xin ? tm + lr : 0) * ldx + lc;
-    const T *wp = W + (win ? tn + lr : 0) * ldw + lc;
-
-    float xr[8], wr[8];
-    load8f<T>(xp, xr);
-    load8f<T>(wp, wr);
-    v16f_e acc = {};
-    for (int64_t k0 = 0; k0 < K; k0 += kEK) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sx[lr * kEP + lc + i] = xin ? xr[i] : 0.f;
-            sw[lr * kEP + lc + i] = win ? wr[i] : 0.f;
-        }
-        __syncthreads();
-        if (k0 + kEK < K) {
-            load8f<T>(xp + k0 + kEK, xr);
-            load8f<T>(wp + k0 + kEK, wr);
-        }
-        const float *ap = sx + (32 * wm + l32) * kEP + 16 * h;
-        const float *bp = sw + (32 * wn + l32) * kEP + 16 * h;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 a = reinterpret_cast<const float4 *>(ap)[q], b = reinterpret_cast<const float4 *>(bp)[q];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
-        }
-        __syncthreads();
-    }
-
-    // result register 4 q + r of lane l: row 8 q + 4 h + r, column l % 32.
-    // All 16 Yq values are requested before any is used (rows and columns
-    // past the matrix read its last row / column and are left out of the sum).
     double s = 0.0;
     const int64_t col = tn + 32 * wn + l32, cc = col < N ? col : N - 1;
     float yq[16];
@@ -135,6 +97,98 @@ __global__ __launch_bounds__(256) void k_outerr(const T *__restrict__ X, int64_t
     }
 }
 
+// Grid (tiles of W rows, tiles of X rows, K splits). Split z forms the
+// products over k in [z kper, min(K, (z + 1) kper)) (kper a multiple of
+// kEK). With one split the workgroup finishes the tile (tile_err); with
+// several it stores its 16 partial products per lane to py, tile-major
+// ([split][tile][thread][16]), and k_outerr_fin adds the splits in order.
+template <typename T>
+__global__ __launch_bounds__(256) void k_outerr(const T *__restrict__ X, int64_t M, int64_t ldx,
+                                                const T *__restrict__ W, int64_t N, int64_t ldw, int64_t K,
+                                                int64_t kper, const float *__restrict__ Yq, int64_t ldy,
+                                                float *__restrict__ py, double *__restrict__ part) {
+    __shared__ __attribute__((aligned(16))) float sx[kET * kEP];
+    __shared__ __attribute__((aligned(16))) float sw[kET * kEP];
+    __shared__ double red[256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+    const int64_t tm = (int64_t)blockIdx.y * kET, tn = (int64_t)blockIdx.x * kET;
+    const int lr = tid >> 2, lc = (tid & 3) * 8;          // load role: row, first column
+    const bool xin = tm + lr < M, win = tn + lr < N;
+    const int64_t klo = (int64_t)blockIdx.z * kper;
+    const int64_t kn = K - klo < kper ? K - klo : kper;   // may be <= 0 for a trailing split
+    const T *xp = X + (xin ? tm + lr : 0) * ldx + klo + lc;
+    const T *wp = W + (win ? tn + lr : 0) * ldw + klo + lc;
+
+    float xr[8], wr[8];
+    if (kn > 0) {
+        load8f<T>(xp, xr);
+        load8f<T>(wp, wr);
+    }
+    v16f_e acc = {};
+    for (int64_t k0 = 0; k0 < kn; k0 += kEK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sx[lr * kEP + lc + i] = xin ? xr[i] : 0.f;
+            sw[lr * kEP + lc + i] = win ? wr[i] : 0.f;
+        }
+        __syncthreads();
+        if (k0 + kEK < kn) {
+            load8f<T>(xp + k0 + kEK, xr);
+            load8f<T>(wp + k0 + kEK, wr);
+        }
+        const float *ap = sx + (32 * wm + l32) * kEP + 16 * h;
+        const float *bp = sw + (32 * wn + l32) * kEP + 16 * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 a = reinterpret_cast<const float4 *>(ap)[q], b = reinterpret_cast<const float4 *>(bp)[q];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = acc[i];
+    if (py) {
+        const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        float4 *dst = reinterpret_cast<float4 *>(
+            py + (((int64_t)blockIdx.z * gridDim.y * gridDim.x + tile) * 256 + tid) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        return;
+    }
+    tile_err(a, M, N, Yq, ldy, red, part);
+}
+
+// Adds the ns splits' partial products of each tile in split order, then
+// finishes the tile as a single-split k_outerr does. Grid (tiles of W rows,
+// tiles of X rows).
+__global__ __launch_bounds__(256) void k_outerr_fin(const float *__restrict__ py, int64_t ns, int64_t M, int64_t N,
+                                                    const float *__restrict__ Yq, int64_t ldy,
+                                                    double *__restrict__ part) {
+    __shared__ double red[256];
+    const int64_t tiles = (int64_t)gridDim.y * gridDim.x, tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = 0.f;
+    for (int64_t z = 0; z < ns; ++z) {
+        const float4 *src = reinterpret_cast<const float4 *>(py + ((z * tiles + tile) * 256 + threadIdx.x) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = src[q];
+            a[4 * q] += v.x;
+            a[4 * q + 1] += v.y;
+            a[4 * q + 2] += v.z;
+            a[4 * q + 3] += v.w;
+        }
+    }
+    tile_err(a, M, N, Yq, ldy, red, part);
+}
+
 // err = sum of part[0 .. n) in a fixed order: thread i adds part[i + 256 j]
 // for increasing j, then thread 0 adds the 256 thread sums in order.
 __global__ __launch_bounds__(256) void k_outerr_sum(const double *__restrict__ part, int64_t n,
@@ -153,9 +207,21 @@ __global__ __launch_bounds__(256) void k_outerr_sum(const double *__restrict__ p
 
 }  // namespace
 
+// K splits of the output-error product: with fewer 64 x 64 tiles than
+// compute units, up to 4 splits per tile fill the chip (the 1024-row k and
+// v projections have 64 tiles at 256 tokens).
+int64_t outerr_splits(int64_t tiles) {
+    if (tiles <= 0 || tiles >= 256) return 1;
+    const int64_t s = ceil_div((int64_t)256, tiles);
+    return s < 4 ? s : 4;
+}
+
 size_t output_error_workspace(int64_t M, int64_t N) {
     const int64_t tiles = ceil_div(M, kET) * ceil_div(N, kET);
-    return (size_t)(tiles > 0 ? tiles : 1) * sizeof(double);
+    const int64_t ns = outerr_splits(tiles);
+    const size_t parts = (size_t)(tiles > 0 ? tiles : 1) * sizeof(double);
+    // partial products start at the first 16-byte boundary after the tile sums
+    return ns > 1 ? parts + 16 + (size_t)(ns * tiles) * kET * kET * sizeof(float) : parts;
 }
 
 hipError_t launch_output_error(const void *X, const void *W, mxs_dtype dtype, int64_t M, int64_t N, int64_t K,
@@ -164,15 +230,27 @@ hipError_t launch_output_error(const void *X, const void *W, mxs_dtype dtype, in
     double *part = static_cast<double *>(ws);
     const int64_t tx = ceil_div(N, kET), ty = ceil_div(M, kET);
     if (tx > 0 && ty > 0) {
-        const dim3 grid((unsigned)tx, (unsigned)ty);
+        const int64_t ns = outerr_splits(tx * ty);
+        // partial products at the first 16-byte boundary after the tile sums
+        float *py = ns > 1 ? reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(part + tx * ty) + 15) &
+                                                      ~(uintptr_t)15)
+                           : nullptr;
+        const int64_t kper = ceil_div(ceil_div(K, (int64_t)kEK), ns) * kEK;
+        const dim3 grid((unsigned)tx, (unsigned)ty, (unsigned)ns);
         if (dtype == MXS_BF16)
             hipLaunchKernelGGL((k_outerr<uint16_t>), grid, dim3(256), 0, st, static_cast<const uint16_t *>(X), M, ldx,
-                               static_cast<const uint16_t *>(W), N, ldw, K, Yq, ldy, part);
+                               static_cast<const uint16_t *>(W), N, ldw, K, kper, Yq, ldy, py, part);
         else
             hipLaunchKernelGGL((k_outerr<float>), grid, dim3(256), 0, st, static_cast<const float *>(X), M, ldx,
-                               static_cast<const float *>(W), N, ldw, K, Yq, ldy, part);
-        const hipError_t e = hipGetLastError();
+                               static_cast<const float *>(W), N, ldw, K, kper, Yq, ldy, py, part);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (ns > 1) {
+            hipLaunchKernelGGL(k_outerr_fin, dim3((unsigned)tx, (unsigned)ty), dim3(256), 0, st, py, ns, M, N, Yq,
+                               ldy, part);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     hipLaunchKernelGGL(k_outerr_sum, dim3(1), dim3(256), 0, st, part, (tx > 0 && ty > 0) ? tx * ty : (int64_t)0, err);
     return hipGetLastError();
