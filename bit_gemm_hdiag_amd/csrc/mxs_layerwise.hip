@@ -207,12 +207,12 @@ __global__ __launch_bounds__(256) void k_outerr_sum(const double *__restrict__ p
 
 }  // namespace
 
-// K splits of the output-error product: with fewer 64 x 64 tiles than
-// compute units, up to 4 splits per tile fill the chip (the 1024-row k and
-// v projections have 64 tiles at 256 tokens).
+// K splits of the output-error product: with fewer than four 64 x 64 tiles
+// per compute unit, up to 4 splits per tile fill the chip (the 1024-row k and
+// v projections have 64 tiles at 256 tokens, q and o 512).
 int64_t outerr_splits(int64_t tiles) {
-    if (tiles <= 0 || tiles >= 256) return 1;
-    const int64_t s = ceil_div((int64_t)256, tiles);
+    if (tiles <= 0 || tiles >= 1024) return 1;
+    const int64_t s = ceil_div((int64_t)1024, tiles);
     return s < 4 ? s : 4;
 }
 

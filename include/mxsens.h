@@ -186,7 +186,7 @@ mxs_status mxs_allocate_blocks(const double *score, int64_t K, int32_t n8, int32
  * The product is formed on the fp32 matrix cores (bf16 inputs widen
  * exactly; each element carries at most the rounding of a K-term fp32 sum),
  * the squared differences are summed in fp64 in a fixed order, so the
- * result is deterministic. With fewer than 256 output tiles of 64 x 64 the
+ * result is deterministic. With fewer than 1024 output tiles of 64 x 64 the
  * products are split along K into up to 4 slices whose fp32 partial sums
  * (held in the workspace) are added in slice order. A calibration-time call.
  * X: [M, ldx], W: [N, ldw], both of `dtype`, rows 16-byte aligned; Yq:

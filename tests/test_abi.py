@@ -206,11 +206,11 @@ def test_output_error_and_allocate_blocks_errors(lib):
                   ctypes.c_int64, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
     lib.mxs_output_error_workspace.restype = ctypes.c_size_t
     lib.mxs_output_error_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64]
-    # tile sums (8 B per 64 x 64 tile); under 256 tiles, also up to 4 K splits of
+    # tile sums (8 B per 64 x 64 tile); under 1024 tiles, also up to 4 K splits of
     # fp32 partial products per tile after a 16-byte alignment slack
     assert lib.mxs_output_error_workspace(130, 70) == 3 * 2 * 8 + 16 + 4 * 3 * 2 * 64 * 64 * 4
-    assert lib.mxs_output_error_workspace(64 * 16, 64 * 16) == 256 * 8           # 256 tiles: no split
-    assert lib.mxs_output_error_workspace(64 * 8, 64 * 16) == 128 * 8 + 16 + 2 * 128 * 64 * 64 * 4
+    assert lib.mxs_output_error_workspace(64 * 32, 64 * 32) == 1024 * 8          # 1024 tiles: no split
+    assert lib.mxs_output_error_workspace(64 * 16, 64 * 32) == 512 * 8 + 16 + 2 * 512 * 64 * 64 * 4
     fake = P(4096)          # never dereferenced: every call below fails validation
     need = lib.mxs_output_error_workspace(64, 64)
     assert f(fake, fake, 7, 64, 64, 64, 64, 64, fake, 64, fake, fake, need, None) == -1     # dtype

@@ -37,11 +37,11 @@ def err_bound(X, W, Yq):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-# under 256 output tiles of 64 x 64 the product is split along K (empty
-# trailing splits at K = 32 and 96, an odd tile count at 130 x 3); 256 x 4096
-# has 256 tiles and takes the unsplit kernel
+# under 1024 output tiles of 64 x 64 the product is split along K (empty
+# trailing splits at K = 32 and 96, an odd tile count at 130 x 3, two splits at
+# 256 x 8192); 256 x 16384 has 1024 tiles and takes the unsplit kernel
 @pytest.mark.parametrize("M,N,K", [(64, 64, 32), (70, 130, 96), (256, 200, 1024), (1, 65, 4096), (130, 3, 64),
-                                   (256, 4096, 64)])
+                                   (256, 8192, 64), (256, 16384, 32)])
 def test_output_error_matches_oracle(mx, orc, M, N, K, dtype):
     g = torch.Generator(device="cpu").manual_seed(M * 3 + N + K)
     X = torch.randn(M, K, generator=g).to(dtype).to(DEV)
