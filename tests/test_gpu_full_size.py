@@ -1,5 +1,5 @@
-"""GPU parity at the full sizes of the Llama-3-8B MLP layers and of the
-Llama-2-70B pipeline layers, through the C ABI.
+"""GPU parity at the full sizes of the Llama-3-8B MLP layers, through the C
+ABI (the Llama-2-70B layers are in test_gpu_c5_pipeline.py).
 
 Calibration, scores, the bit map and permutation, and the packed weight
 planes are compared with the oracle in full and bit for bit; the GEMM is
@@ -46,8 +46,13 @@ def check_gemm(Y, Yref, Yabs, what):
 GEMMS = ["mxs_mixed_gemm", "mxs_mixed_gemm_mx"]
 
 
-def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12, n_sample_cols=48,
-                   entry="mxs_mixed_gemm"):
+def per_group_sample(n, group, gen):
+    """One random index in every group of `group` consecutive indices, plus both ends."""
+    picks = [g0 + int(torch.randint(0, min(group, n - g0), (1,), generator=gen)) for g0 in range(0, n, group)]
+    return np.unique(np.array([0, n - 1] + picks))
+
+
+def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, entry="mxs_mixed_gemm"):
     """calibrate -> score -> allocate -> quantize W and X -> mixed GEMM, each against the oracle."""
     gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
     Xc = synth.activations(calib_rows, K, seed + synth.ROLE_CALIB, gains, device=DEV)
@@ -76,8 +81,8 @@ def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12,
     A = mx.mxs_quantize(X, perm, n8, n6, n4)
     Y = getattr(mx, entry)(A, B).cpu().numpy().astype(np.float64)
     g = torch.Generator(device="cpu").manual_seed(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], torch.randint(0, M, (n_sample_rows,), generator=g).numpy()]))
-    cols = np.unique(np.concatenate([[0, N - 1], torch.randint(0, N, (n_sample_cols,), generator=g).numpy()]))
+    rows = per_group_sample(M, 128, g)
+    cols = per_group_sample(N, 128, g)
     A_ref = orc.quantize(host(X[torch.as_tensor(rows, device=DEV)]), p_ref, n8, n6, n4)
     check_planes(A, A_ref, rows)
     B_cols = {k: v[cols] for k, v in B_ref.items() if isinstance(v, np.ndarray)}
@@ -87,26 +92,11 @@ def layer_pipeline(mx, orc, M, N, K, budget, calib_rows, seed, n_sample_rows=12,
 
 
 # Llama-3-8B MLP, 4096 tokens: gate/up 14336 x 4096 at 3/10/87 %, down
-# 4096 x 14336 at 8/20/72 %; calibration over 8 x 2048 tokens
-@pytest.mark.parametrize("N,K,budget", [(14336, 4096, (300, 1000)), (4096, 14336, (800, 2000))])
+# 4096 x 14336 at 8/20/72 %, and the two budgets swapped (gate/up at
+# 8/20/72 %, down at 3/10/87 %); calibration over 8 x 2048 tokens. Y is
+# compared on one token per 128-row group and one column per 128-column group.
+@pytest.mark.parametrize("N,K,budget", [(14336, 4096, (300, 1000)), (4096, 14336, (800, 2000)),
+                                        (14336, 4096, (800, 2000)), (4096, 14336, (300, 1000))])
 @pytest.mark.parametrize("entry", GEMMS)
 def test_mlp_layer_full_size(mx, orc, N, K, budget, entry):
     layer_pipeline(mx, orc, 4096, N, K, budget, 8 * 2048, seed=3000 + K, entry=entry)
-
-
-# Llama-2-70B layer shapes at 2048 prefill tokens, 5/15/80 %: k_proj (1024 x
-# 8192) and down_proj (8192 x 28672); calibration here over 2048 tokens (the
-# full 128 x 2048-token calibration volume is checked below on a column slice)
-@pytest.mark.parametrize("N,K", [(1024, 8192), (8192, 28672)])
-@pytest.mark.parametrize("entry", GEMMS)
-def test_70b_layer_full_size(mx, orc, N, K, entry):
-    layer_pipeline(mx, orc, 2048, N, K, (500, 1500), 2048, seed=5000 + N, entry=entry)
-
-
-def test_70b_calibration_volume_column_slice(mx, orc):
-    # 128 x 2048 calibration tokens (1024 row chunks): the canonical order is
-    # per column, so a 256-column slice checks the long chunk chain exactly
-    gains = synth.outlier_gains(256, 5003)
-    Xc = synth.activations(128 * 2048, 256, 5001, gains, device=DEV)
-    h = mx.mxs_calibrate(Xc)
-    assert np.array_equal(h.cpu().numpy(), orc.calibrate(host(Xc)))

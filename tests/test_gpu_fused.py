@@ -1,12 +1,16 @@
 """The fused entry point (activation quantisation inside the product,
-mxs_mixed_gemm_fused) against the two calls it replaces, through the C ABI:
-mxs_quantize of X into planes, then mxs_mixed_gemm. Both quantise with the
-same rule and feed the same GEMM kernels, so Y must agree bit for bit
-(compared as raw fp32 bits, NaN included). One case is also checked against
-the oracle's quantize + GEMM within the GEMM bound. Shapes cover the fused
-prefill path (64+ rows), the planes path (fewer rows, or rows too long for
-the LDS stage), ragged M and N, a K with a padding block, strided and
-misaligned X, fp32 and bf16, the identity map and non-finite values.
+mxs_mixed_gemm_fused) through the C ABI, against the oracle and against the
+two calls it replaces (mxs_quantize of X into planes, then mxs_mixed_gemm).
+
+Every case is checked against the oracle's quantize + GEMM, componentwise
+within 1e-5 of the fp64 definition (non-finite outputs where the definition
+has them). The fused call and the two calls quantise with the same rule and
+feed the same GEMM kernels, so Y must also agree bit for bit with them
+(compared as raw fp32 bits, NaN included). Shapes cover the fused prefill
+path (64+ rows, up to the 2048 x 4096 x 4096 q_proj layer), the planes path
+(fewer rows, or rows too long for the LDS stage such as K = 28672), ragged
+M and N, a K with a padding block, strided and misaligned X, fp32 and bf16,
+the identity map and non-finite values.
 """
 import numpy as np
 import pytest
@@ -41,6 +45,21 @@ def same_bits(a, b):
     return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
 
 
+def against_oracle(orc, X, W, perm, counts, Y):
+    """Y (device) against the oracle's quantize of X and W, then its GEMM."""
+    p = None if perm is None else perm.cpu().numpy()
+    Qa = orc.quantize(np.ascontiguousarray(X.float().cpu().numpy()), p, *counts)
+    Qw = orc.quantize(np.ascontiguousarray(W.float().cpu().numpy()), p, *counts)
+    Yref, Yabs = orc.mixed_gemm(Qa, Qw)
+    y = Y.cpu().numpy().astype(np.float64)
+    nan_ref = np.isnan(Yref)
+    assert np.array_equal(np.isnan(y), nan_ref), "NaN pattern"
+    y, Yref, Yabs = np.where(nan_ref, 0, y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs)
+    err = np.abs(y - Yref)
+    ok = err <= 1e-5 * Yabs
+    assert ok.all(), f"{int((~ok).sum())} outputs off, worst rel {float((err / np.maximum(Yabs, 1e-300)).max()):.3e}"
+
+
 @pytest.mark.parametrize("M,N,K,budget,dtype,permuted", [
     (64, 128, 256, (500, 1500), torch.bfloat16, True),
     (300, 200, 4096, (500, 1500), torch.bfloat16, True),
@@ -52,8 +71,10 @@ def same_bits(a, b):
     (100, 80, 8192, (500, 1500), torch.float32, True),
     (8, 300, 1024, (500, 1500), torch.bfloat16, True),        # decode kernels
     (40, 64, 512, (500, 1500), torch.float32, True),          # 33..63 rows
+    (40, 96, 28672, (500, 1500), torch.bfloat16, True),       # 33..63 rows, long rows
+    (2048, 4096, 4096, (500, 1500), torch.bfloat16, True),    # the q_proj layer
 ])
-def test_fused_equals_quantize_then_gemm(mx, M, N, K, budget, dtype, permuted):
+def test_fused_equals_quantize_then_gemm(mx, orc, M, N, K, budget, dtype, permuted):
     seed = M + 3 * N + K
     X, W = operands(M, N, K, seed, dtype)
     n8, n6, n4 = mx.mxs_budget_blocks(K, *budget)
@@ -64,9 +85,10 @@ def test_fused_equals_quantize_then_gemm(mx, M, N, K, budget, dtype, permuted):
     ref = unfused(mx, X, perm, Wq)
     assert same_bits(Y, Y2)
     assert same_bits(Y, ref), float((Y - ref).abs().max())
+    against_oracle(orc, X, W, perm, (n8, n6, n4), Y)
 
 
-def test_fused_strided_misaligned_and_nonfinite(mx):
+def test_fused_strided_misaligned_and_nonfinite(mx, orc):
     M, N, K = 200, 130, 2048
     X, W = operands(M, N, K + 8, 77, torch.bfloat16)
     Xs = X[:, 3:3 + K]                        # row stride K + 8, rows start off 16-byte alignment
@@ -80,6 +102,7 @@ def test_fused_strided_misaligned_and_nonfinite(mx):
     ref = unfused(mx, Xs, perm, Wq)
     assert same_bits(Y, ref)
     assert torch.isnan(Y[5]).all() and torch.isnan(Y[17]).all() and (Y[40] == 0).all()
+    against_oracle(orc, Xs, W[:, :K], perm, (n8, n6, n4), Y)
     # into a strided output, with a caller workspace reused twice
     big = torch.full((M, N + 10), 7.0, device=DEV)
     ws = torch.empty(mx.mxs_mixed_gemm_fused_workspace(M, torch.bfloat16, Wq), dtype=torch.uint8, device=DEV)
