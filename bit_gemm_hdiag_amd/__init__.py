@@ -13,7 +13,7 @@ _BINDING_NAMES = None
 
 def __getattr__(name):
     if name.startswith("mxs_") or name in ("MxsError", "QMat", "qmat_alloc", "library_path",
-                                          "STATUS"):
+                                          "STATUS", "NOALLOC_SCRATCH_BYTES"):
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

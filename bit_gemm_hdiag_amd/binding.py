@@ -59,6 +59,7 @@ def _load():
         "mxs_quantize": (S, [P, c_int32, c_int64, P, POINTER(_QMat), P]),
         "mxs_mixed_gemm_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
         "mxs_mixed_gemm": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
+        "mxs_mixed_gemm_noalloc": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P]),
         "mxs_mixed_gemm_mx_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
         "mxs_mixed_gemm_mx": (S, [POINTER(_QMat), POINTER(_QMat), P, c_int64, P, c_size_t, P]),
         "mxs_quantize_kv": (S, [P, c_int32, c_int64, c_int64, c_int64, P, P, P]),
@@ -81,7 +82,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_blocks",
             "mxs_calibrate_workspace", "mxs_score_workspace", "mxs_calibrate", "mxs_score",
-            "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm",
+            "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm", "mxs_mixed_gemm_noalloc",
             "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv", "mxs_allocate_blocks",
             "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget", "mxs_attend_kv4_workspace",
             "mxs_attend_kv4", "mxs_mixed_gemm_fused_workspace", "mxs_mixed_gemm_fused")
@@ -279,6 +280,21 @@ def _gemm(fn, wsfn, name, A: QMat, W: QMat, Y, ws) -> torch.Tensor:
 def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
     """Y [M, N] fp32 = Qa(X) Qw(W)^T with per-block MX scales."""
     return _gemm(_lib.mxs_mixed_gemm, _lib.mxs_mixed_gemm_workspace, "mxs_mixed_gemm", A, W, Y, ws)
+
+
+# bytes of the device scratch array behind mxs_mixed_gemm_noalloc (per GPU)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def mxs_mixed_gemm_noalloc(A: QMat, W: QMat, Y: torch.Tensor) -> torch.Tensor:
+    """mxs_mixed_gemm with its workspace in the library's per-GPU scratch
+    array: the C call allocates nothing (Y is the caller's fp32 [M, N])."""
+    if Y.dtype != torch.float32:
+        raise TypeError("Y must be fp32")
+    py, ldy = _dev2d(Y, "Y")
+    a, w = ctypes.byref(A.c_struct()), ctypes.byref(W.c_struct())
+    _check(_lib.mxs_mixed_gemm_noalloc(a, w, py, ldy, _stream(Y.device)), "mxs_mixed_gemm_noalloc")
+    return Y
 
 
 def mxs_mixed_gemm_fused_workspace(M: int, dtype: torch.dtype, W: QMat) -> int:

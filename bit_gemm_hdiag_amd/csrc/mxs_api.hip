@@ -5,7 +5,16 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mxs_internal.h"
+
+// Workspace of mxs_mixed_gemm_noalloc: one copy per GPU in device memory,
+// loaded with the code object and kept until the process ends. Host code
+// never passes the name itself to a kernel (on the host it stands for a
+// host-side handle, not a device address); it uses the address from
+// hipGetSymbolAddress, looked up per device below.
+static __device__ __align__(256) uint8_t scratch[MXS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -42,6 +51,39 @@ size_t colsum_ws(int64_t rows, int64_t K, bool score) {
 }
 
 bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Device address of `scratch` on the GPU of `stream`, looked up once per GPU
+// with that GPU current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int dev = -1, cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (stream) {
+        if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    } else {
+        dev = cur;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 mxs_status check_qmat(const mxs_qmat *q, const char *name) {
     if (!q) return fail(MXS_ERR_ARG, "%s is NULL", name);
@@ -250,6 +292,23 @@ mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_
     const mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm");
     if (s != MXS_OK) return s;
     return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm");
+}
+
+mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
+                                  hipStream_t stream) {
+    mxs_status s = check_gemm(A, W, Y, ldy, nullptr, 0, 0, "mixed_gemm_noalloc");   // arguments first
+    if (s != MXS_OK) return s;
+    const size_t need = mxs::gemm_workspace(*A, *W);
+    if (need > MXS_NOALLOC_SCRATCH_BYTES)
+        return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm_noalloc: these shapes need %zu bytes of workspace, above the "
+                    "%zu-byte scratch array (use mxs_mixed_gemm with a caller workspace)", need,
+                    (size_t)MXS_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need) {
+        const hipError_t e = scratch_address(stream, &ws);
+        if (e != hipSuccess) return device_status(e, "mixed_gemm_noalloc: scratch address");
+    }
+    return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, need, stream), "mixed_gemm_noalloc");
 }
 
 size_t mxs_mixed_gemm_fused_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W) {

@@ -29,7 +29,8 @@
  *   - Element types: MXS_F32 (fp32) or MXS_BF16 (bfloat16) inputs; bf16
  *     values are widened to fp32 exactly. Sums are fp64 where stated.
  *   - Thread safety: reentrant; the library holds no mutable global state
- *     other than the thread-local error string.
+ *     other than the thread-local error string and, for
+ *     mxs_mixed_gemm_noalloc, one device scratch array per GPU (see there).
  */
 #ifndef MXSENS_H
 #define MXSENS_H
@@ -260,6 +261,31 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W);
  */
 mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the product
+ * of mxs_mixed_gemm, same kernels and the same result bit for bit, with its
+ * workspace taken from a scratch array the library holds in device memory
+ * (MXS_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends) instead
+ * of a caller buffer. The call allocates nothing. The caller still owns A,
+ * W and Y (device memory, layout and alignment as for mxs_mixed_gemm).
+ * Shapes whose mxs_mixed_gemm_workspace(A, W) exceeds
+ * MXS_NOALLOC_SCRATCH_BYTES are rejected with MXS_ERR_UNSUPPORTED (for
+ * example every decode shape of the Llama-2-70B MLP up to 32 tokens and the
+ * 2048 x 4096 x 4096 prefill fit; 2048-token prefill at N = 28672 does not).
+ * The scratch array belongs to the GPU of `stream` (the calling thread's
+ * current device for the null stream); its device address is looked up once
+ * per GPU on the first call there. Every call on one GPU shares that GPU's
+ * array and leaves its contents behind; nothing in it needs clearing before a
+ * call. Calls that overlap on one GPU (other threads, or streams that run
+ * concurrently) race on the array: the caller serialises them.
+ * Errors: as mxs_mixed_gemm, plus MXS_ERR_UNSUPPORTED (workspace above the
+ * scratch size) and MXS_ERR_DEVICE (the scratch address lookup failed).
+ */
+#define MXS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
+                                  hipStream_t stream);
 
 /* Workspace bytes needed by mxs_mixed_gemm_mx for these shapes (may be 0). */
 size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W);
