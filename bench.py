@@ -1,29 +1,34 @@
 """Benchmark of the MXSens hot path on one MI355X.
 
-One step = one pass of every stage over the Llama-3-8B q_proj-shaped layer
-(synthetic, seeded): calibrate over 8 x 2048 tokens, score, allocate,
-quantize W, quantize X, the mixed 8/6/4-bit GEMM (2048 x 4096 x 4096) and
-MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128). Inputs are
-resident in HBM before timing starts.
+Headline (default): one step = one Llama-2-70B block (one of the 80), every
+stage of the path on synthetic, seeded inputs resident in HBM before timing
+starts: calibrate over 128 x 2048 tokens for each of the block's four layer
+inputs (q/k/v share one, o, gate/up share one, down; 27.9 GB of bf16), score,
+allocate (5/15/80 % 8/6/4-bit), quantize W for the seven weights (q 8192 x
+8192, k and v 1024 x 8192, o 8192 x 8192, gate and up 28672 x 8192, down
+8192 x 28672), quantize X and the mixed GEMM at M = 2048 for all seven, and
+MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128).
 
-Prints one JSON line. `value` is the whole step's throughput in GEMM TOPS
-(2 M N K per step over the step time) with mxs_mixed_gemm (int8 block sums);
-per-stage times, TOPS and GB/s are in `stages` (`ms`: median of single
-calls, each after a read pass over 512 MB that evicts the 256 MB Infinity Cache,
-so inputs come from HBM; `warm_ms`: back-to-back calls through the Python
-binding; `warm_graph_ms`: the same calls replayed from one HIP graph; both
-warm figures re-read inputs the cache holds); `roofline` is for the
-dominant kernel; `variant_mx` repeats the step with mxs_mixed_gemm_mx
-(prefill on the block-scaled fp6 matrix cores) and `variant_fused` with
-mxs_mixed_gemm_fused (X quantized inside the product, no quantize_x stage);
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same step.
+Prints one JSON line. `value` is the block's GEMM work (2 M N K summed over
+the seven layers) over the block step time, in TOPS, with mxs_mixed_gemm
+(int8 block sums); `stages` gives every stage's time per step, GB/s (and
+TOPS) and fraction of its peak, from HIP events around every call on the
+library's stream in the timed steps; `roofline` is for the stage with the
+largest share of the step, `roofline_gemm` and `roofline_calibrate` for the
+GEMM and calibration calls; `variant_mx` and `variant_fused` repeat the step
+with mxs_mixed_gemm_mx (fp6 block-scaled MFMA prefill) and
+mxs_mixed_gemm_fused (X quantized inside the product). `cpu_baseline` is the
+CPU oracle on a bounded sample of the step, extrapolated (all host cores,
+and one core in a child process). Extra keys: `q_proj_step` (the Llama-3-8B
+q_proj-shaped layer step), `mlp_gemm` (Llama-3-8B MLP GEMMs at 4096 tokens)
+and `decode` (70B MLP decode GEMMs at 1, 8 and 32 tokens, cache-cold).
 
-The dominant kernel's roofline uses the mixed_gemm call's own duration,
-timed with HIP events on its stream inside every timed step; its HBM
-traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored in
-profiles/ and is reported only while the GEMM source is unchanged since.
+`roofline.traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+stored in profiles/ and is reported only while the kernel source is
+unchanged since they were taken.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+       python bench.py --workload q_proj   (the Llama-3-8B q_proj layer step alone)
        python bench.py --copy-probe   (a plain device copy of known size, to
                                        scale the HBM byte counters)
        python bench.py --overhead     (mixed_gemm under the all-4-bit, 4.03-bit,
@@ -34,11 +39,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --attention    (one query token over the MXINT4 K/V cache,
                                        70B heads, 2048 / 8192 / 32768 tokens)
        python bench.py --decode       (decode-shape GEMMs of the 70B MLP at 1, 8
-                                       and 32 tokens: one JSON line per case, GB/s
-                                       of packed W + scale bytes against HBM peak,
-                                       median of single calls after an Infinity
-                                       Cache flush; `warm_graph_us` is the same
-                                       calls replayed back to back from a graph)
+                                       and 32 tokens: one JSON line per case)
 """
 from __future__ import annotations
 
@@ -98,7 +99,9 @@ def copy_probe(torch):
 
 
 def decode_cases(mx, synth, torch, reps=20):
-    """70B MLP decode GEMMs (up 28672 x 8192, down 8192 x 28672, 5/15/80 %)."""
+    """70B MLP decode GEMMs (up 28672 x 8192, down 8192 x 28672, 5/15/80 %) at
+    1, 8 and 32 tokens: one dict per case."""
+    out = []
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[4]
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
@@ -121,10 +124,13 @@ def decode_cases(mx, synth, torch, reps=20):
             fn = lambda: mx.mxs_mixed_gemm(Aq, Wq, Y, ws=ws)
             tc = time_cold(torch, fn, reps, flush)
             tg = time_graph(torch, fn, reps)
-            print(json.dumps({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": tc * 1e6,
-                              "warm_graph_us": tg * 1e6, "w_bytes": wbytes, "GBps": wbytes / tc / 1e9,
-                              "hbm_frac": wbytes / tc / HBM_PEAK, "warm_hbm_frac": wbytes / tg / HBM_PEAK}),
-                  flush=True)
+            out.append({"case": f"decode {lay['name']} {N}x{K}", "tokens": M, "us": tc * 1e6,
+                        "warm_graph_us": tg * 1e6, "w_bytes": wbytes, "GBps": wbytes / tc / 1e9,
+                        "hbm_frac": wbytes / tc / HBM_PEAK, "warm_hbm_frac": wbytes / tg / HBM_PEAK})
+            log(json.dumps(out[-1]))
+            del X, Aq, Y, ws
+        del Wq
+    return out
 
 
 def overhead_cases(mx, synth, torch, reps=20):
@@ -410,44 +416,432 @@ def cpu_baseline(w, torch, min_seconds=10.0, max_reps=20):
                 step_s=step, stage_s=stage)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--stage-reps", type=int, default=50)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--decode", action="store_true")
-    ap.add_argument("--overhead", action="store_true")
-    ap.add_argument("--layerwise", action="store_true")
-    ap.add_argument("--attention", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(the hot path would shard by rows and columns; no collective is built). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+# ----------------------------------------------------------------------------
+# The Llama-2-70B block step (the headline workload)
+BLOCK_INPUT_K = {0: 8192, 1: 8192, 2: 8192, 3: 28672}   # q/k/v, o, gate/up, down inputs
+BLOCK_INPUT_OF = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
 
-    import torch
-    if args.copy_probe:
-        copy_probe(torch)
-        return
-    import bit_gemm_hdiag_amd as mx
-    from bit_gemm_hdiag_amd import synth
-    if args.decode:
-        decode_cases(mx, synth, torch)
-        return
-    if args.overhead:
-        overhead_cases(mx, synth, torch)
-        return
-    if args.layerwise:
-        layerwise_cases(mx, synth, torch)
-        return
-    if args.attention:
-        attention_cases(mx, synth, torch)
-        return
 
+def packed_row_bytes(K, blocks):
+    n8, n6, n4 = blocks
+    return 32 * n8 + 24 * n6 + 16 * n4 + K // 32
+
+
+def block_workload(mx, synth, torch, dev):
+    """Every input of one 70B block resident in HBM: the four layer inputs'
+    calibration tokens (128 x 2048 each) and prefill tokens (2048), the seven
+    bf16 weights, K and V of 2048 x 8 x 128, and every output buffer."""
+    cfg = synth.CONFIGS[5]
+    M, T = cfg["M"], cfg["calib_rows"]
+    bp8, bp6 = cfg["budget"]
+    u8 = dict(dtype=torch.uint8, device=dev)
+    w = dict(M=M, T=T, bp8=bp8, bp6=bp6, inputs={}, layers=[])
+    for inp, K in BLOCK_INPUT_K.items():
+        seed = 5000 + 16 * inp
+        gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+        log(f"input {inp}: calibration {T} x {K} bf16")
+        w["inputs"][inp] = dict(
+            K=K, Xc=synth.activations(T, K, seed + synth.ROLE_CALIB, gains, device=dev),
+            X=synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev),
+            hdiag=torch.zeros(K, dtype=torch.float64, device=dev),
+            ws=torch.empty(max(1, mx.mxs_calibrate_workspace(T, K)), **u8))
+    for li, lay in enumerate(cfg["layers"]):
+        N, K = lay["N"], lay["K"]
+        blocks = mx.mxs_budget_blocks(K, bp8, bp6)
+        w["layers"].append(dict(
+            name=lay["name"], N=N, K=K, inp=BLOCK_INPUT_OF[lay["name"]], blocks=blocks,
+            W=synth.weights(N, K, 5500 + 16 * li + synth.ROLE_W, device=dev),
+            score=torch.empty(K, dtype=torch.float64, device=dev), bits=torch.empty(K, **u8),
+            perm=torch.empty(K, dtype=torch.int32, device=dev),
+            ws_sc=torch.empty(max(1, mx.mxs_score_workspace(N, K)), **u8),
+            Wq=mx.qmat_alloc(N, K, *blocks, dev), Aq=mx.qmat_alloc(M, K, *blocks, dev)))
+    maxN = max(L["N"] for L in w["layers"])
+    ybuf = torch.empty(M * maxN, dtype=torch.float32, device=dev)
+    for L in w["layers"]:
+        L["Y"] = ybuf[:M * L["N"]].view(M, L["N"])
+    w["ws_g"] = torch.empty(max(max(mx.mxs_mixed_gemm_workspace(L["Aq"], L["Wq"]) for L in w["layers"]), 1), **u8)
+    w["ws_gx"] = torch.empty(max(max(mx.mxs_mixed_gemm_mx_workspace(L["Aq"], L["Wq"]) for L in w["layers"]), 1), **u8)
+    w["ws_gf"] = torch.empty(max(max(mx.mxs_mixed_gemm_fused_workspace(M, torch.bfloat16, L["Wq"])
+                                     for L in w["layers"]), 1), **u8)
+    kv = cfg["kv"]
+    w["kv_shape"] = kv
+    w["Kc"] = synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV, device=dev)
+    w["Vc"] = synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV + 8, device=dev)
+    w["kc"] = [torch.empty((kv["T"], kv["H"], kv["D"] // 2), **u8) for _ in range(2)]
+    w["ks"] = [torch.empty((kv["T"], kv["H"], kv["D"] // 32), **u8) for _ in range(2)]
+    return w
+
+
+def block_calls(mx, w, variant=None):
+    """One block step as (stage, label, fn, work) in stream order; work is the
+    call's algorithmic bytes (and ops for the GEMM). variant "mx": the GEMMs
+    are mxs_mixed_gemm_mx; "fused": quantize_x + GEMM become one
+    mxs_mixed_gemm_fused call per layer."""
+    M, T = w["M"], w["T"]
+    calls = []
+    for inp, I in w["inputs"].items():
+        K = I["K"]
+        calls.append(("calibrate", f"input {inp}",
+                      lambda I=I: (I["hdiag"].zero_(), mx.mxs_calibrate(I["Xc"], I["hdiag"], ws=I["ws"])),
+                      dict(bytes=T * K * 2 + 16 * K)))
+    for L in w["layers"]:
+        h = w["inputs"][L["inp"]]["hdiag"]
+        calls.append(("score", L["name"], lambda L=L, h=h: mx.mxs_score(L["W"], h, L["score"], ws=L["ws_sc"]),
+                      dict(bytes=L["N"] * L["K"] * 2 + 24 * L["K"])))
+    for L in w["layers"]:
+        calls.append(("allocate", L["name"],
+                      lambda L=L: mx.mxs_allocate(L["score"], w["bp8"], w["bp6"], L["bits"], L["perm"]),
+                      dict(bytes=13 * L["K"])))
+    for L in w["layers"]:
+        pr = packed_row_bytes(L["K"], L["blocks"])
+        calls.append(("quantize_w", L["name"], lambda L=L: mx.mxs_quantize(L["W"], L["perm"], *L["blocks"], out=L["Wq"]),
+                      dict(bytes=L["N"] * L["K"] * 2 + L["N"] * pr + 4 * L["K"])))
+    for L in w["layers"]:
+        pr = packed_row_bytes(L["K"], L["blocks"])
+        X = w["inputs"][L["inp"]]["X"]
+        gemm_work = dict(ops=2 * M * L["N"] * L["K"], bytes=(M + L["N"]) * pr + 4 * M * L["N"])
+        if variant == "fused":
+            calls.append(("mixed_gemm", L["name"],
+                          lambda L=L, X=X: mx.mxs_mixed_gemm_fused(X, L["perm"], L["Wq"], L["Y"], ws=w["ws_gf"]),
+                          gemm_work))
+            continue
+        calls.append(("quantize_x", L["name"], lambda L=L, X=X: mx.mxs_quantize(X, L["perm"], *L["blocks"], out=L["Aq"]),
+                      dict(bytes=M * L["K"] * 2 + M * pr + 4 * L["K"])))
+        if variant == "mx":
+            fn = lambda L=L: mx.mxs_mixed_gemm_mx(L["Aq"], L["Wq"], L["Y"], ws=w["ws_gx"])
+        else:
+            fn = lambda L=L: mx.mxs_mixed_gemm(L["Aq"], L["Wq"], L["Y"], ws=w["ws_g"])
+        calls.append(("mixed_gemm", L["name"], fn, gemm_work))
+    kv = w["kv_shape"]
+    kvb = kv["T"] * kv["H"] * kv["D"] * (2 + 0.5 + 1 / 32)
+    calls.append(("quantize_kv", "K", lambda: mx.mxs_quantize_kv(w["Kc"], w["kc"][0], w["ks"][0]), dict(bytes=kvb)))
+    calls.append(("quantize_kv", "V", lambda: mx.mxs_quantize_kv(w["Vc"], w["kc"][1], w["ks"][1]), dict(bytes=kvb)))
+    return calls
+
+
+def run_block_steps(torch, calls, steps, warmup):
+    """warmup untimed steps, then `steps` timed steps between two
+    synchronisations; every call is also bracketed by HIP events on the
+    current stream (the stream the library launches on). Returns the step
+    time and per-stage totals (seconds per step, work per step, calls)."""
+    for _ in range(warmup):
+        for _, _, fn, _ in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = []
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        for stage, label, fn, work in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.append((stage, label, a, b, work))
+    e.record()
+    torch.cuda.synchronize()
+    step_s = s.elapsed_time(e) / steps * 1e-3
+    stages = {}
+    for stage, label, a, b, work in ev:
+        d = stages.setdefault(stage, dict(s=0.0, bytes=0.0, ops=0.0, calls=0, by_call={}))
+        t = a.elapsed_time(b) * 1e-3
+        d["s"] += t / steps
+        d["bytes"] += work.get("bytes", 0) / steps
+        d["ops"] += work.get("ops", 0) / steps
+        d["calls"] += 1
+        d["by_call"][label] = d["by_call"].get(label, 0.0) + t / steps
+    for d in stages.values():
+        d["calls"] //= steps
+    return step_s, stages
+
+
+def stage_summary(stages):
+    out = {}
+    for name, d in stages.items():
+        o = dict(ms=d["s"] * 1e3, calls=d["calls"], GBps=d["bytes"] / d["s"] / 1e9,
+                 hbm_frac=d["bytes"] / d["s"] / HBM_PEAK,
+                 us_by_call={k: v * 1e6 for k, v in d["by_call"].items()})
+        if d["ops"]:
+            o["TOPS"] = d["ops"] / d["s"] / 1e12
+            o["int8_mfma_frac"] = d["ops"] / d["s"] / INT8_PEAK
+        out[name] = o
+    return out
+
+
+def stored_traffic(path, key, source):
+    """Bytes per call from a stored counter summary (key = value lines), or
+    None when the summary is missing or `source` changed since it was taken."""
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        with open(source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return float(kv[key])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+BLOCK_TRAFFIC = os.path.join(ROOT, "profiles", "70b_block.traffic.txt")
+COLSUM_SOURCE = os.path.join(ROOT, "bit_gemm_hdiag_amd", "csrc", "mxs_colsum.hip")
+
+
+def roofline_of(stage, d):
+    """Roofline object of one stage's calls: algorithmic work per call over
+    the mean call duration (Σ work / Σ time over the timed calls)."""
+    per_call_s = d["s"] / d["calls"]
+    if d["ops"]:
+        ach = d["ops"] / d["s"]
+        r = dict(bound="mfma", achieved=ach / 1e12, peak=INT8_PEAK / 1e12, unit="TOP/s", frac=ach / INT8_PEAK,
+                 traffic=stored_traffic(BLOCK_TRAFFIC, "mixed_gemm_bytes_per_call", GEMM_SOURCE),
+                 algorithmic_ops_per_launch=d["ops"] / d["calls"])
+    else:
+        ach = d["bytes"] / d["s"]
+        r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s", frac=ach / HBM_PEAK,
+                 traffic=(stored_traffic(BLOCK_TRAFFIC, "calibrate_bytes_per_call", COLSUM_SOURCE)
+                          if stage == "calibrate" else None))
+    r.update(stage=stage, launch_us=per_call_s * 1e6, algorithmic_bytes_per_launch=d["bytes"] / d["calls"],
+             launches_per_step=d["calls"])
+    return r
+
+
+def mlp_gemms(mx, synth, torch, reps=10):
+    """The Llama-3-8B MLP GEMMs at 4096 tokens (gate/up 14336 x 4096 at
+    3/10/87 %, down 4096 x 14336 at 8/20/72 %), mxs_mixed_gemm and
+    mxs_mixed_gemm_mx, graph-replayed back to back (inputs of 60-240 MB)."""
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[3]
+    M = cfg["M"]
+    out = {}
+    for li, lay in enumerate(cfg["layers"]):
+        if lay["name"] == "up":
+            continue          # the same shape and budget as gate
+        N, K = lay["N"], lay["K"]
+        seed = 3000 + 16 * li
+        gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
+        blocks = mx.mxs_budget_blocks(K, *lay["budget"])
+        perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(dev)
+        Wq = mx.mxs_quantize(synth.weights(N, K, seed + synth.ROLE_W, device=dev), perm, *blocks)
+        Aq = mx.mxs_quantize(synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev), perm, *blocks)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ops = 2 * M * N * K
+        d = dict(shape=f"{M}x{N}x{K}", blocks=list(blocks))
+        for entry in ("mxs_mixed_gemm", "mxs_mixed_gemm_mx"):
+            ws = torch.empty(max(1, getattr(mx, entry + "_workspace")(Aq, Wq)), dtype=torch.uint8, device=dev)
+            f = getattr(mx, entry)
+            t = time_graph(torch, lambda: f(Aq, Wq, Y, ws=ws), reps)
+            d[entry] = dict(us=t * 1e6, TOPS=ops / t / 1e12, int8_mfma_frac=ops / t / INT8_PEAK)
+            del ws
+        out[lay["name"]] = d
+        log("mlp", json.dumps(d))
+        del Wq, Aq, Y
+    return out
+
+
+def block_cpu_sample(w, torch):
+    """Host copies of a bounded sample of the block step for the CPU oracle,
+    with the factor that scales each stage's sample to the whole step."""
+    M, T = w["M"], w["T"]
+    S = dict(calib=[], layers=[], kv=[], scale={})
+    tc = 8192
+    for inp, I in w["inputs"].items():
+        S["calib"].append(I["Xc"][:tc].float().cpu().numpy())
+    S["scale"]["calibrate"] = T / tc
+    wr = 4                    # score and quantize W on 1/4 of every weight's rows
+    xr = 4                    # quantize X on 1/4 of the tokens
+    gr = 256                  # GEMM on 256 tokens against the sampled weight rows
+    for L in w["layers"]:
+        X = w["inputs"][L["inp"]]["X"]
+        S["layers"].append(dict(name=L["name"], K=L["K"], blocks=L["blocks"],
+                                inp_id=L["inp"], W=L["W"][:L["N"] // wr].float().cpu().numpy(),
+                                X=X[:M // xr].float().cpu().numpy()))
+    S["scale"].update(score=wr, quantize_w=wr, quantize_x=xr, mixed_gemm=(M / gr) * wr, allocate=1,
+                      quantize_kv=1)
+    S["gemm_rows"] = gr
+    S["kv"] = [w["Kc"].float().cpu().numpy(), w["Vc"].float().cpu().numpy()]
+    S["bp"] = (w["bp8"], w["bp6"])
+    return S
+
+
+def oracle_stage_times(S, sub=1):
+    """The CPU oracle over the sample S (each stage's rows cut by `sub` more),
+    in the step's order; returns seconds per stage scaled to the whole step."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    t = {}
+
+    def timed(stage, f):
+        t0 = time.perf_counter()
+        r = f()
+        t[stage] = t.get(stage, 0.0) + (time.perf_counter() - t0) * S["scale"][stage] * sub
+        return r
+    hd = [timed("calibrate", lambda X=X: oracle.calibrate(np.ascontiguousarray(X[:X.shape[0] // sub])))
+          for X in S["calib"]]
+    bp8, bp6 = S["bp"]
+    for L in S["layers"]:
+        W = np.ascontiguousarray(L["W"][:max(1, L["W"].shape[0] // sub)])
+        X = np.ascontiguousarray(L["X"][:max(1, L["X"].shape[0] // sub)])
+        sc = timed("score", lambda: oracle.score(W, hd[L["inp_id"]]))
+        _, perm = timed("allocate", lambda: oracle.allocate(sc, bp8, bp6))
+        Wq = timed("quantize_w", lambda: oracle.quantize(W, perm, *L["blocks"]))
+        Aq = timed("quantize_x", lambda: oracle.quantize(X, perm, *L["blocks"]))
+        g = max(1, S["gemm_rows"] // sub)
+        Ag = {k: (v[:g] if isinstance(v, np.ndarray) else v) for k, v in Aq.items()}
+        timed("mixed_gemm", lambda: oracle.mixed_gemm(Ag, Wq))
+    for kv in S["kv"]:
+        timed("quantize_kv", lambda kv=kv: oracle.quantize_kv(np.ascontiguousarray(kv[:max(1, kv.shape[0] // sub)])))
+    return t
+
+
+def save_sample(S, sub, path):
+    """The sample as one .npz of arrays plus a JSON file of the rest."""
+    import numpy as np
+    arrays = {f"calib{i}": X for i, X in enumerate(S["calib"])}
+    arrays.update({f"kv{i}": X for i, X in enumerate(S["kv"])})
+    meta = dict(sub=sub, scale=S["scale"], gemm_rows=S["gemm_rows"], bp=list(S["bp"]), layers=[])
+    for i, L in enumerate(S["layers"]):
+        arrays[f"W{i}"], arrays[f"X{i}"] = L["W"], L["X"]
+        meta["layers"].append(dict(name=L["name"], K=L["K"], blocks=list(L["blocks"]), inp_id=L["inp_id"]))
+    np.savez(os.path.join(path, "sample.npz"), **arrays)
+    with open(os.path.join(path, "sample.json"), "w") as f:
+        json.dump(meta, f)
+
+
+def load_sample(path):
+    import numpy as np
+    with open(os.path.join(path, "sample.json")) as f:
+        meta = json.load(f)
+    z = np.load(os.path.join(path, "sample.npz"))
+    n_in = sum(1 for k in z.files if k.startswith("calib"))
+    S = dict(calib=[z[f"calib{i}"] for i in range(n_in)], kv=[z["kv0"], z["kv1"]], scale=meta["scale"],
+             gemm_rows=meta["gemm_rows"], bp=tuple(meta["bp"]), layers=[])
+    for i, L in enumerate(meta["layers"]):
+        S["layers"].append(dict(name=L["name"], K=L["K"], blocks=tuple(L["blocks"]), inp_id=L["inp_id"],
+                                W=z[f"W{i}"], X=z[f"X{i}"]))
+    return S, meta["sub"]
+
+
+def oracle_child(path):
+    """1-thread oracle timing in a child process (OMP_NUM_THREADS=1): loads the
+    sample the parent saved and prints the scaled stage times."""
+    S, sub = load_sample(path)
+    print(json.dumps(oracle_stage_times(S, sub)), flush=True)
+
+
+def block_cpu_baseline(w, torch, gemm_ops):
+    """The CPU oracle on a bounded sample of the block step, on all host cores
+    and on one core; stage times are extrapolated to the whole step."""
+    import shutil
+    import subprocess
+    import tempfile
+    S = block_cpu_sample(w, torch)
+    t0 = time.perf_counter()
+    t_all = oracle_stage_times(S)
+    wall_all = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    step_all = sum(t_all.values())
+    res = dict(value=gemm_ops / step_all / 1e12, unit="TOPS", cores=cores, kind="oracle",
+               sample=(f"extrapolated: calibrate on 8192 of the 262144 tokens of each input (x32), score and "
+                       f"quantize W on 1/4 of every weight's rows (x4), quantize X on 512 of 2048 tokens (x4), "
+                       f"the GEMM on 256 tokens x 1/4 of the weight rows (x32), K/V in full; "
+                       f"{wall_all:.1f} s of CPU work on {cores} threads"),
+               step_s=step_all, stage_s=t_all)
+    sub = 8
+    tmp = tempfile.mkdtemp(prefix="mxs_oracle_")
+    try:
+        save_sample(S, sub, tmp)
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        t0 = time.perf_counter()
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-child", tmp], env=env,
+                           capture_output=True, text=True, timeout=600)
+        wall_one = time.perf_counter() - t0
+        if r.returncode == 0:
+            t_one = json.loads(r.stdout.strip().splitlines()[-1])
+            step_one = sum(t_one.values())
+            res["one_core"] = dict(value=gemm_ops / step_one / 1e12, cores=1, step_s=step_one, stage_s=t_one,
+                                   sample=f"the same sample cut 8x further (x8 more extrapolation), "
+                                          f"{wall_one:.1f} s wall in a child process with OMP_NUM_THREADS=1")
+        else:
+            res["one_core"] = dict(error=r.stderr[-500:])
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return res
+
+
+def block_line(mx, synth, torch, args):
+    """The headline: one Llama-2-70B block step per `step`."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("building the 70B block workload")
+    w = block_workload(mx, synth, torch, dev)
+    M = w["M"]
+    gemm_ops = sum(2 * M * L["N"] * L["K"] for L in w["layers"])
+    log(f"warmup {args.warmup}, timing {args.steps} block steps")
+    step_s, stages = run_block_steps(torch, block_calls(mx, w), args.steps, args.warmup)
+    log(f"block step {step_s * 1e3:.3f} ms")
+    dominant = max(stages, key=lambda k: stages[k]["s"])
+    out = {
+        "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
+        "value": gemm_ops / step_s / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded outlier-channel activations, Student-t weights, bf16)",
+        "config": {"workload": "Llama-2-70B block (one of 80): calibrate 128x2048 tokens for each of the 4 layer "
+                               "inputs (K 8192 x3, 28672), score/allocate/quantize W for q 8192x8192, k and v "
+                               "1024x8192, o 8192x8192, gate and up 28672x8192, down 8192x28672 (5/15/80% "
+                               "8/6/4-bit), quantize X and mixed GEMM at M=2048 for all 7, MXINT4 K and V "
+                               "2048x8x128; one step = one block",
+                   "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)",
+                   "pipeline_80_layers_s": step_s * 80},
+        "gemm_ops_per_step": gemm_ops,
+        "stages": stage_summary(stages),
+        "roofline": roofline_of(dominant, stages[dominant]),
+        "roofline_gemm": roofline_of("mixed_gemm", stages["mixed_gemm"]),
+        "roofline_calibrate": roofline_of("calibrate", stages["calibrate"]),
+    }
+    if not args.no_extras:
+        for variant, key, entry in (("mx", "variant_mx", "mxs_mixed_gemm_mx (fp6 block-scaled MFMA prefill)"),
+                                    ("fused", "variant_fused", "mxs_mixed_gemm_fused (X quantized inside the "
+                                                               "product; no quantize_x stage)")):
+            log(f"the block step with {entry}")
+            sv, st = run_block_steps(torch, block_calls(mx, w, variant), max(3, args.steps // 2), 2)
+            g = st["mixed_gemm"]
+            out[key] = dict(entry=entry, value=gemm_ops / sv / 1e12, ms_per_step=sv * 1e3,
+                            gemm_ms_per_step=g["s"] * 1e3, gemm_TOPS=g["ops"] / g["s"] / 1e12,
+                            int8_peak_frac=g["ops"] / g["s"] / INT8_PEAK,
+                            fp6_peak_frac=g["ops"] / g["s"] / FP6_PEAK if variant == "mx" else None)
+    if not args.no_cpu:
+        log("cpu baseline (oracle, sampled)")
+        out["cpu_baseline"] = block_cpu_baseline(w, torch, gemm_ops)
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("q_proj layer step (Llama-3-8B)")
+        qa = argparse.Namespace(**vars(args))
+        qa.no_cpu = True
+        q = q_proj_line(mx, synth, torch, qa)
+        out["q_proj_step"] = {k: q[k] for k in ("value", "ms_per_step", "gemm_tops", "quantize_gbps", "roofline",
+                                                 "variant_mx", "variant_fused", "stages")}
+        out["mlp_gemm"] = mlp_gemms(mx, synth, torch)
+        out["decode"] = decode_cases(mx, synth, torch)
+    return out
+
+
+def q_proj_line(mx, synth, torch, args):
+    """The q_proj-shaped layer step (2048 x 4096 x 4096) as one JSON object."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("building workload")
@@ -566,7 +960,60 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, torch)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="70B block step only (no variants, no q_proj / MLP / decode keys)")
+    ap.add_argument("--workload", choices=("70b_block", "q_proj"), default="70b_block")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--overhead", action="store_true")
+    ap.add_argument("--layerwise", action="store_true")
+    ap.add_argument("--attention", action="store_true")
+    ap.add_argument("--oracle-child", default=None, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.oracle_child:
+        oracle_child(args.oracle_child)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(the hot path would shard by rows and columns; no collective is built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    import bit_gemm_hdiag_amd as mx
+    from bit_gemm_hdiag_amd import synth
+    if args.decode:
+        for d in decode_cases(mx, synth, torch):
+            print(json.dumps(d), flush=True)
+        return
+    if args.overhead:
+        overhead_cases(mx, synth, torch)
+        return
+    if args.layerwise:
+        layerwise_cases(mx, synth, torch)
+        return
+    if args.attention:
+        attention_cases(mx, synth, torch)
+        return
+    if args.workload == "q_proj":
+        print(json.dumps(q_proj_line(mx, synth, torch, args)), flush=True)
+        return
+    print(json.dumps(block_line(mx, synth, torch, args)), flush=True)
 
 
 if __name__ == "__main__":
