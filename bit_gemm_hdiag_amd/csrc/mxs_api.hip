@@ -220,7 +220,10 @@ mxs_status mxs_output_error(const void *X, const void *W, mxs_dtype dtype, int64
     const size_t es = dtype == MXS_BF16 ? 2 : 4;
     if ((M > 0 && (!aligned(X, 16) || (ldx * es) % 16)) || (N > 0 && (!aligned(W, 16) || (ldw * es) % 16)))
         return fail(MXS_ERR_UNSUPPORTED, "output_error: X and W rows need 16-byte alignment");
-    if (ws_bytes < mxs::output_error_workspace(M, N)) return fail(MXS_ERR_WORKSPACE, "output_error: workspace too small");
+    if (M > (int64_t)65535 * 64) return fail(MXS_ERR_UNSUPPORTED, "output_error: M=%lld above 65535 * 64", (long long)M);
+    if (ws_bytes < mxs::output_error_workspace(M, N) || !aligned(ws, 16))
+        return fail(MXS_ERR_WORKSPACE, "output_error: workspace smaller than %zu bytes or not 16-byte aligned",
+                    mxs::output_error_workspace(M, N));
     return device_status(mxs::launch_output_error(X, W, dtype, M, N, K, ldx, ldw, Yq, ldy, err, ws, stream),
                          "output_error");
 }

@@ -193,9 +193,13 @@ mxs_status mxs_allocate_blocks(const double *score, int64_t K, int32_t n8, int32
  * X: [M, ldx], W: [N, ldw], both of `dtype`, rows 16-byte aligned; Yq:
  * [M, ldy] fp32; err: one fp64 on the device (written). ws >=
  * mxs_output_error_workspace(M, N) bytes. All device pointers, owned by
- * the caller; asynchronous on `stream`.
+ * the caller; asynchronous on `stream`. The workspace holds one fp64 per
+ * tile and, when the product is split, 16 KiB of fp32 partial products per
+ * tile and slice (fewer than 2048 tile slices, under 32 MiB); it must be
+ * 16-byte aligned.
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (M or N < 0, K % 32, ld too small),
- * MXS_ERR_UNSUPPORTED (alignment), MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ * MXS_ERR_UNSUPPORTED (alignment of X or W, M > 65535 * 64),
+ * MXS_ERR_WORKSPACE (too small or misaligned), MXS_ERR_DEVICE.
  */
 size_t mxs_output_error_workspace(int64_t M, int64_t N);
 mxs_status mxs_output_error(const void *X, const void *W, mxs_dtype dtype, int64_t M, int64_t N,

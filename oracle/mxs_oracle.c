@@ -11,7 +11,8 @@
  *   [NL]  gist.science/nl/paper/2607.17733, "Technische Samenvatting"
  *         (section numbers below refer to it),
  *   [REV] romaanj.github.io/reviews/mxsens ("Method", "Key idea"),
- *   [RP]  researchpod.app summary (bullet "Triplet Quantization").
+ *   [RP]  researchpod.app summary (bullet "Triplet Quantization"),
+ *   [KR]  insight.artgrammer.co.kr/papers/21466 (English abstract).
  * Where the pages leave a step open, the reading taken is stated next to the
  * code as "Reading:". All parity is pinned by the CPU test suite against
  * closed forms, brute force and invariants (see tests/test_oracle_*.py).

@@ -222,6 +222,9 @@ def test_output_error_and_allocate_blocks_errors(lib):
     assert f(P(4100), fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, fake, need, None) == -6  # alignment
     assert f(fake, fake, 1, 64, 64, 64, 68, 64, fake, 64, fake, fake, need, None) == -6     # bf16 row pitch
     assert f(fake, fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, fake, need - 1, None) == -4  # workspace
+    assert f(fake, fake, 0, 64, 64, 64, 64, 64, fake, 64, fake, P(4104), need, None) == -4   # ws alignment
+    big = 65535 * 64 + 1                                                                     # grid rows
+    assert f(fake, fake, 0, big, 64, 64, 64, 64, fake, 64, fake, fake, 1 << 40, None) == -6
     g = lib.mxs_allocate_blocks
     g.restype = ctypes.c_int32
     g.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]
