@@ -463,12 +463,13 @@ def block_workload(mx, synth, torch, dev):
     w["ws_gx"] = torch.empty(max(max(mx.mxs_mixed_gemm_mx_workspace(L["Aq"], L["Wq"]) for L in w["layers"]), 1), **u8)
     w["ws_gf"] = torch.empty(max(max(mx.mxs_mixed_gemm_fused_workspace(M, torch.bfloat16, L["Wq"])
                                      for L in w["layers"]), 1), **u8)
+    # the layer's K and V stacked as one [2 T, H, D] tensor: one quantize_kv launch
     kv = cfg["kv"]
     w["kv_shape"] = kv
-    w["Kc"] = synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV, device=dev)
-    w["Vc"] = synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV + 8, device=dev)
-    w["kc"] = [torch.empty((kv["T"], kv["H"], kv["D"] // 2), **u8) for _ in range(2)]
-    w["ks"] = [torch.empty((kv["T"], kv["H"], kv["D"] // 32), **u8) for _ in range(2)]
+    w["KV"] = torch.cat([synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV, device=dev),
+                         synth.kv(kv["T"], kv["H"], kv["D"], 5000 + synth.ROLE_KV + 8, device=dev)])
+    w["kvc"] = torch.empty((2 * kv["T"], kv["H"], kv["D"] // 2), **u8)
+    w["kvs"] = torch.empty((2 * kv["T"], kv["H"], kv["D"] // 32), **u8)
     return w
 
 
@@ -513,9 +514,8 @@ def block_calls(mx, w, variant=None):
             fn = lambda L=L: mx.mxs_mixed_gemm(L["Aq"], L["Wq"], L["Y"], ws=w["ws_g"])
         calls.append(("mixed_gemm", L["name"], fn, gemm_work))
     kv = w["kv_shape"]
-    kvb = kv["T"] * kv["H"] * kv["D"] * (2 + 0.5 + 1 / 32)
-    calls.append(("quantize_kv", "K", lambda: mx.mxs_quantize_kv(w["Kc"], w["kc"][0], w["ks"][0]), dict(bytes=kvb)))
-    calls.append(("quantize_kv", "V", lambda: mx.mxs_quantize_kv(w["Vc"], w["kc"][1], w["ks"][1]), dict(bytes=kvb)))
+    kvb = 2 * kv["T"] * kv["H"] * kv["D"] * (2 + 0.5 + 1 / 32)
+    calls.append(("quantize_kv", "K and V", lambda: mx.mxs_quantize_kv(w["KV"], w["kvc"], w["kvs"]), dict(bytes=kvb)))
     return calls
 
 
@@ -663,7 +663,8 @@ def block_cpu_sample(w, torch):
     S["scale"].update(score=wr, quantize_w=wr, quantize_x=xr, mixed_gemm=(M / gr) * wr, allocate=1,
                       quantize_kv=1)
     S["gemm_rows"] = gr
-    S["kv"] = [w["Kc"].float().cpu().numpy(), w["Vc"].float().cpu().numpy()]
+    T = w["kv_shape"]["T"]
+    S["kv"] = [w["KV"][:T].float().cpu().numpy(), w["KV"][T:].float().cpu().numpy()]
     S["bp"] = (w["bp8"], w["bp6"])
     return S
 

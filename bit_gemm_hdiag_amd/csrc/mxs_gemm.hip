@@ -170,7 +170,9 @@ QView view_of(const mxs_qmat &q) {
 //
 // Prepared operand (workspace), per matrix with R rows padded to Rp and K
 // padded to Kp = whole windows:
-//   codes int8 [Rp, Kp]   shifted codes, natural k order inside each block
+//   codes int8 [Rp, Kp]   shifted codes, natural k order inside each block;
+//                         W row-major, A (activations) in fragment order
+//                         (afrag_off: 1 KiB per 32 rows and block)
 //   cs    f32  [nbp, Rp]  code scale of (row, block); negative when the
 //                         row's window is not aligned; -Inf for a NaN/Inf block
 // Padding rows and blocks hold zero codes and scale +1.
@@ -223,7 +225,17 @@ struct PrepJob {
     int8_t *codes;
     float *cs;
     int64_t tiles_r;      // Rp / 64
+    int32_t frag;         // codes in fragment order (afrag_off) rather than row-major
 };
+
+// Fragment order of the activation operand: for each group of 32 rows and
+// each block, 1 KiB holding k-half 0 of the 32 rows (16 bytes each) and then
+// k-half 1, so that the 64 lanes of a 32x32x32 MFMA fetch their A fragment
+// of that block with one contiguous 16-byte load each (lane l: row l mod 32,
+// k-half l / 32, bytes 16 l).
+__host__ __device__ inline int64_t afrag_off(int64_t row, int64_t b, int h, int64_t nbp) {
+    return (((row >> 5) * nbp + b) << 10) + ((int64_t)h << 9) + ((row & 31) << 4);
+}
 
 // Windows start at the first block of each width class: window j of class
 // segment [lo, hi) covers blocks lo + kG j .. min(hi, lo + kG (j + 1)) - 1.
@@ -320,9 +332,15 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
             w[k] = v;
         }
         if (in_range && (real_blk || b >= nb)) {
-            uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * b);
-            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            if (J.frag) {
+                int8_t *dst = J.codes + afrag_off(r, b, 0, nbp);
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4 *>(dst + 512) = make_uint4(w[4], w[5], w[6], w[7]);
+            } else {
+                uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * b);
+                dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
         }
         s_cs[blk][lr] = scale;
     }
@@ -473,52 +491,54 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
             lo = (lo << shift) & keep;
             hi = (hi << shift) & keep;
             if (b < nbp && (real_blk || b >= nb)) {
-                *reinterpret_cast<uint2 *>(codes + row * Kp + 32 * b + 8 * q) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2 *>(codes + afrag_off(row, b, q >> 1, nbp) + 8 * (q & 1)) = make_uint2(lo, hi);
                 if (q == 0) cs[b * Rp + row] = scale;
             }
         }
     }
 }
 
-// Grouped int8 GEMM over prepared operands.
+// Grouped int8 GEMM over prepared operands (the prefill kernel of
+// mxs_mixed_gemm and mxs_mixed_gemm_fused).
 //
-// Workgroup: 8 waves (4 x 2), tile 256 (A rows) x 128 (W rows); each wave
-// owns 64 x 64 outputs as 2 x 2 MFMA tiles (64 int32 + 64 fp32 accumulators
-// per lane, two waves per SIMD). Operands move from global memory straight
-// into LDS (global_load_lds_dwordx4), so no registers hold data in flight
-// and four stages can be in flight at once. (A version that staged through
-// registers one stage ahead ran 4-5 % slower at the q_proj and MLP shapes.)
+// Workgroup: 8 waves (8 x 1), tile 256 (A rows) x 128 (W rows); wave w owns
+// A rows 32 w .. 32 w + 31 against all 128 W rows, i.e. 1 x 4 MFMA tiles
+// (64 int32 + 64 fp32 accumulators per lane, two waves per SIMD). Every A
+// fragment therefore belongs to one wave: it is fetched from the
+// fragment-ordered operand (afrag_off) with one 16-byte load per lane and
+// block, four stages ahead, into a register ring that follows the LDS ring's
+// slots. W codes and both operands' scales move from global memory straight
+// into LDS (global_load_lds_dwordx4), which no register holds in flight.
+// (An earlier version also streamed A through LDS by DMA; the DMA path, not
+// the matrix cores, then bounded it, and moving A to registers took two
+// thirds of the bytes off that path.)
 //
-// Stage = kDSB = 2 blocks (64 bytes of every row) plus their scales, 27 KiB;
-// a ring of five stage slots. Iteration s: wait for this wave's loads of
-// stage s (the loads of stages s+1 .. s+3 stay in flight), barrier (every
-// wave's loads of stage s have landed and every wave is done with stage
-// s-1), issue stage s+4 into the slot of stage s-1, compute s.
+// Stage = kDSB = 2 blocks (64 bytes of every W row) plus the scales of both
+// operands, 11 KiB; a ring of five stage slots. Iteration s: wait for this
+// wave's loads of stage s (the loads of stages s+1 .. s+3 stay in flight),
+// barrier (every wave's loads of stage s have landed and every wave is done
+// with stage s-1), issue stage s+4 into the slot of stage s-1, compute s.
 // A DMA instruction writes 64 consecutive 16-byte LDS slots, lane by lane;
 // lanes pick their global chunk so that row r keeps chunk c at slot
 // c ^ ((r >> 2) & 3) of its 64 bytes: the 16 lanes of one LDS read pass
 // (16 consecutive rows, same chunk) then hit 16 distinct 16-byte bank groups.
+//
+// A block whose integer sums end (the last block of its window, or any
+// block of a window whose rows are not all aligned) needs an epilogue.
+// Inside a stage it is left pending: the next block runs it (by then the
+// block's MFMAs have finished, so the vector ALU does not wait for them),
+// tile by tile, each tile followed by a restart MFMA that zeroes its integer
+// sums in place (the matrix core has slack, the vector ALU has none), then
+// the new block's MFMAs accumulate as usual. The last block of a stage runs
+// its epilogue at once: the next step's DMA refills the slot of the stage
+// before the one it computes, so scales cannot be read across that step.
+// After the loop no DMA follows, so a pending epilogue of the final stage
+// runs there.
 constexpr int kGBM = 256, kGBN = 128;        // workgroup tile
 constexpr int kDSB = 2;                      // blocks per stage
 constexpr int kDRow = kDSB * 32;             // 64 bytes per row per stage
-constexpr int kDStA = kGBM * kDRow;          // 16 KiB
-constexpr int kDStW = kGBN * kDRow;          //  8 KiB
-constexpr int kDStCA = kDSB * kGBM * 4;      //  2 KiB
-constexpr int kDStCW = kDSB * kGBN * 4;      //  1 KiB
-constexpr int kDSlot = kDStA + kDStW + kDStCA + kDStCW;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__shared__ __attribute__((aligned(16))) int8_t g_dslot0[kDSlot];
-__shared__ __attribute__((aligned(16))) int8_t g_dslot1[kDSlot];
-__shared__ __attribute__((aligned(16))) int8_t g_dslot2[kDSlot];
-__shared__ __attribute__((aligned(16))) int8_t g_dslot3[kDSlot];
-__shared__ __attribute__((aligned(16))) int8_t g_dslot4[kDSlot];
-
-template <int SL>
-__device__ __forceinline__ int8_t *dslot() {
-    return SL == 0 ? g_dslot0 : (SL == 1 ? g_dslot1 : (SL == 2 ? g_dslot2 : (SL == 3 ? g_dslot3 : g_dslot4)));
-}
 
 // LDS byte address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -537,31 +557,47 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
                  : "memory", "m0");
 }
 
-struct DmaLanes {
-    const int8_t *a0, *a1, *w;   // this lane's global chunk addresses at stage 0
-    const float *c;              // scales (waves 0..2)
-    int64_t cstep;               // scale address step per stage
-    int oa0, oa1, ow, oc;        // wave-uniform LDS offsets inside a slot
+constexpr int kAW = kGBN * kDRow;            // 8 KiB: W codes of a stage
+constexpr int kACA = kDSB * kGBM * 4;        // 2 KiB: A scales
+constexpr int kACW = kDSB * kGBN * 4;        // 1 KiB: W scales
+constexpr int kASlot = kAW + kACA + kACW;
+
+__shared__ __attribute__((aligned(16))) int8_t g_aslot0[kASlot];
+__shared__ __attribute__((aligned(16))) int8_t g_aslot1[kASlot];
+__shared__ __attribute__((aligned(16))) int8_t g_aslot2[kASlot];
+__shared__ __attribute__((aligned(16))) int8_t g_aslot3[kASlot];
+__shared__ __attribute__((aligned(16))) int8_t g_aslot4[kASlot];
+
+template <int SL>
+__device__ __forceinline__ int8_t *aslot() {
+    return SL == 0 ? g_aslot0 : (SL == 1 ? g_aslot1 : (SL == 2 ? g_aslot2 : (SL == 3 ? g_aslot3 : g_aslot4)));
+}
+
+struct A2RLanes {
+    const int8_t *w;          // this lane's W chunk at stage 0
+    const float *c;           // scales (waves 0..2)
+    int64_t cstep;            // scale address step per stage
+    int ow, oc;               // wave-uniform LDS offsets inside a slot
+    const v4i *a;             // this lane's A fragment of block 0
 };
 
 template <int SL>
-__device__ __forceinline__ void dma_issue(const DmaLanes &D, int st, int nstage, bool has_c) {
+__device__ __forceinline__ void a2r_issue(const A2RLanes &D, int st, int nstage, bool has_c, v4i (&ar)[5][kDSB]) {
     const int s = st < nstage ? st : nstage - 1;      // past the end: reload the last stage
-    const uint32_t slot = lds_addr(dslot<SL>());
-    const int64_t kb = (int64_t)s * kDRow;
-    dma16(D.a0 + kb, slot + D.oa0);
-    dma16(D.a1 + kb, slot + D.oa1);
-    dma16(D.w + kb, slot + D.ow);
+    const uint32_t slot = lds_addr(aslot<SL>());
+    dma16(D.w + (int64_t)s * kDRow, slot + D.ow);
     if (has_c) dma16(D.c + s * D.cstep, slot + D.oc);
+#pragma unroll
+    for (int blk = 0; blk < kDSB; ++blk) ar[SL][blk] = D.a[(int64_t)(s * kDSB + blk) * 64];
 }
 
-__global__ __launch_bounds__(512, 1) void k_gemm_dma(
-    const int8_t *__restrict__ Aq, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
+__global__ __launch_bounds__(512, 1) void k_gemm_a2r(
+    const int8_t *__restrict__ Af, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
     const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
     int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy, int32_t gm) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+    const int l32 = lane & 31, h = lane >> 5;
 
     // tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
     // takes a contiguous run of tiles; runs sweep groups of gm row-tiles
@@ -574,108 +610,87 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
     const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
     const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
     const int nstage = (nb + kDSB - 1) / kDSB;
+    const int64_t nbp = Kp / 32;
     const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
 
-    // DMA roles: A rows 32 wave .. +31 (two instructions of 16 rows), W rows
-    // 16 wave .. +15; waves 0, 1: A scales of block 0 / 1; wave 2: W scales
-    DmaLanes D;
+    // DMA roles: W rows 16 wave .. +15; waves 0, 1: A scales of block 0 / 1;
+    // wave 2: W scales
+    A2RLanes D;
     {
         const int rsub = lane >> 2, sl = lane & 3;
-        const int ra0 = 32 * wave + rsub, ra1 = ra0 + 16, rw = 16 * wave + rsub;
-        D.a0 = Aq + (m0 + ra0) * Kp + ((sl ^ ((ra0 >> 2) & 3)) << 4);
-        D.a1 = Aq + (m0 + ra1) * Kp + ((sl ^ ((ra1 >> 2) & 3)) << 4);
+        const int rw = 16 * wave + rsub;
         D.w = Wq + (n0 + rw) * Kp + ((sl ^ ((rw >> 2) & 3)) << 4);
-        D.oa0 = 32 * wave * kDRow;
-        D.oa1 = D.oa0 + 16 * kDRow;
-        D.ow = kDStA + 16 * wave * kDRow;
+        D.ow = 16 * wave * kDRow;
         if (wave < 2) {
             D.c = csA + (int64_t)wave * Mp + m0 + 4 * lane;
             D.cstep = kDSB * Mp;
-            D.oc = kDStA + kDStW + wave * (kGBM * 4);
+            D.oc = kAW + wave * (kGBM * 4);
         } else {
             D.c = csW + (int64_t)(lane >> 5) * Np + n0 + 4 * (lane & 31);
             D.cstep = kDSB * Np;
-            D.oc = kDStA + kDStW + kDStCA;
+            D.oc = kAW + kACA;
         }
+        D.a = reinterpret_cast<const v4i *>(Af + afrag_off(m0 + 32 * wave, 0, 0, nbp)) + lane;
     }
     const bool has_c = wave < 3;
 
-    // LDS offset of this lane's fragment of block blk: fb ^ (blk << 5)
-    int fbA[2], fbW[2];
+    // LDS offset of this lane's W fragment j of block blk: fbW[j] ^ (blk << 5)
+    int fbW[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
-        fbA[i] = ra * kDRow + ((h ^ ((ra >> 2) & 3)) << 4);
-        fbW[i] = kDStA + rw * kDRow + ((h ^ ((rw >> 2) & 3)) << 4);
+    for (int j = 0; j < 4; ++j) {
+        const int rw = j * 32 + l32;
+        fbW[j] = rw * kDRow + ((h ^ ((rw >> 2) & 3)) << 4);
     }
 
-    float acc[2][2][16];
-    v16i I[2][2];
+    float acc[4][16];
+    v16i I[4];
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    // two zero B operands the compiler cannot see through, so the restart
-    // MFMAs stay distinct and write the accumulators in place
-    v4i zb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    v4i zb;   // a zero B operand the compiler cannot see through (restart MFMAs stay distinct)
+    {
         int z;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        zb[j] = v4i{z, z, z, z};
+        zb = v4i{z, z, z, z};
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+        I[j] = zero;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            I[i][j] = zero;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-        }
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    }
+    v4i ar[5][kDSB];
 
-    // A block whose integer sums end (the last block of its window, or any
-    // block of a window whose rows are not all aligned) needs an epilogue.
-    // Inside a stage it is left pending: the next block runs it (by then the
-    // block's MFMAs have finished, so the vector ALU does not wait for them),
-    // tile by tile, each tile followed by a restart MFMA that zeroes its
-    // integer sums in place (the matrix core has slack, the vector ALU has
-    // none), then the new block's MFMAs accumulate as usual. The last block of
-    // a stage runs its epilogue at once: the next step's DMA refills the slot
-    // of the stage before the one it computes, so scales cannot be read across
-    // that step. After the loop no DMA follows, so a pending epilogue of the
-    // final stage runs there. pCA / pCW: the pending block's code scales.
     bool aligned = true, pend = false;
     const float *pCA = nullptr, *pCW = nullptr;
-    auto load_sa = [&](int i, f32x4_t sa[4]) {
+    auto epi_all = [&](const v4i &fa) {   // epilogue of the pending block, tile by tile, each with its restart
+        f32x4_t sa[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sa[q] = *reinterpret_cast<const f32x4_t *>(pCA + i * 32 + 8 * q + 4 * h);
-    };
-    auto epi = [&](int i, int j, const f32x4_t sa[4]) {
-        const float cw = __builtin_fabsf(pCW[j * 32 + l32]);
+        for (int q = 0; q < 4; ++q) sa[q] = *reinterpret_cast<const f32x4_t *>(pCA + 8 * q + 4 * h);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < 4; ++j) {
+            const float cw = __builtin_fabsf(pCW[j * 32 + l32]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[i][j][4 * q + e] =
-                    __builtin_fmaf((float)I[i][j][4 * q + e], __builtin_fabsf(sa[q][e]) * cw, acc[i][j][4 * q + e]);
-    };
-    auto compute = [&](int st, const int8_t *sbase) {
-        const float *sCA = reinterpret_cast<const float *>(sbase + kDStA + kDStW);
-        const float *sCW = sCA + kDSB * kGBM;
-        v4i fa[2], fw[2], na[2], nw[2];
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            na[i] = *reinterpret_cast<const v4i *>(sbase + fbA[i]);
-            nw[i] = *reinterpret_cast<const v4i *>(sbase + fbW[i]);
+                for (int e = 0; e < 4; ++e)
+                    acc[j][4 * q + e] =
+                        __builtin_fmaf((float)I[j][4 * q + e], __builtin_fabsf(sa[q][e]) * cw, acc[j][4 * q + e]);
+            I[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 0);
         }
+    };
+    auto compute = [&](int st, const int8_t *sbase, const v4i (&fa)[kDSB]) {
+        const float *sCA = reinterpret_cast<const float *>(sbase + kAW);
+        const float *sCW = sCA + kDSB * kGBM;
+        v4i fw[4], nw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nw[j] = *reinterpret_cast<const v4i *>(sbase + fbW[j]);
 #pragma unroll
         for (int blk = 0; blk < kDSB; ++blk) {
             const int b = st * kDSB + blk;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) { fa[i] = na[i]; fw[i] = nw[i]; }
+            for (int j = 0; j < 4; ++j) fw[j] = nw[j];
             if (blk + 1 < kDSB) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    na[i] = *reinterpret_cast<const v4i *>(sbase + (fbA[i] ^ ((blk + 1) << 5)));
-                    nw[i] = *reinterpret_cast<const v4i *>(sbase + (fbW[i] ^ ((blk + 1) << 5)));
-                }
+                for (int j = 0; j < 4; ++j) nw[j] = *reinterpret_cast<const v4i *>(sbase + (fbW[j] ^ ((blk + 1) << 5)));
             }
             if (b >= nb) break;
             const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
@@ -684,96 +699,78 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(
             const bool first = (off % kG) == 0;
             const bool last = (off % kG) == kG - 1 || b == hi - 1;
             if (first) {
-                const float va = sCA[blk * kGBM + wm * 64 + lane];
-                const float vw = sCW[blk * kGBN + wn * 64 + lane];
-                aligned = __all(va > 0.f && vw > 0.f);
+                const float va = sCA[blk * kGBM + 32 * wave + l32];
+                const float vw0 = sCW[blk * kGBN + lane], vw1 = sCW[blk * kGBN + 64 + lane];
+                aligned = __all(va > 0.f && vw0 > 0.f && vw1 > 0.f);
             }
-            if (pend) {
+            if (pend) epi_all(fa[blk]);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    f32x4_t sa[4];
-                    load_sa(i, sa);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        epi(i, j, sa);
-                        I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fw[j], I[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) I[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[blk], fw[j], I[j], 0, 0, 0);
             pend = last || !aligned;
             if (pend) {
-                pCA = sCA + blk * kGBM + wm * 64;
-                pCW = sCW + blk * kGBN + wn * 64;
+                pCA = sCA + blk * kGBM + 32 * wave;
+                pCW = sCW + blk * kGBN;
                 if (blk == kDSB - 1) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        f32x4_t sa[4];
-                        load_sa(i, sa);
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            epi(i, j, sa);
-                            I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], zb[j], zero, 0, 0, 0);
-                        }
-                    }
+                    epi_all(fa[blk]);
                     pend = false;
                 }
             }
         }
     };
 
-    // own loads of stage s done once at most two later stages are in flight
-#define MXS_DSTEP(s_, CUR, NXT)                                                               \
+    // own loads of stage s done once at most three later stages are in flight
+    // (per stage: one W DMA, two A fragments, and a scale DMA on waves 0..2)
+#define MXS_ASTEP(s_, CUR, NXT)                                                               \
     do {                                                                                      \
         if ((s_) >= nstage) goto done;                                                        \
         if (has_c) __builtin_amdgcn_s_waitcnt(0x0F70 | 12); /* vmcnt(12) */                   \
         else __builtin_amdgcn_s_waitcnt(0x0F70 | 9);        /* vmcnt(9) */                    \
         lds_barrier();                                                                        \
-        dma_issue<NXT>(D, (s_) + 4, nstage, has_c);                                           \
-        compute((s_), dslot<CUR>());                                                          \
+        a2r_issue<NXT>(D, (s_) + 4, nstage, has_c, ar);                                       \
+        compute((s_), aslot<CUR>(), ar[CUR]);                                                 \
     } while (0)
 
-    dma_issue<0>(D, 0, nstage, has_c);
-    dma_issue<1>(D, 1, nstage, has_c);
-    dma_issue<2>(D, 2, nstage, has_c);
-    dma_issue<3>(D, 3, nstage, has_c);
+    a2r_issue<0>(D, 0, nstage, has_c, ar);
+    a2r_issue<1>(D, 1, nstage, has_c, ar);
+    a2r_issue<2>(D, 2, nstage, has_c, ar);
+    a2r_issue<3>(D, 3, nstage, has_c, ar);
     for (int s = 0; s < nstage; s += 5) {
-        MXS_DSTEP(s, 0, 4);
-        MXS_DSTEP(s + 1, 1, 0);
-        MXS_DSTEP(s + 2, 2, 1);
-        MXS_DSTEP(s + 3, 3, 2);
-        MXS_DSTEP(s + 4, 4, 3);
+        MXS_ASTEP(s, 0, 4);
+        MXS_ASTEP(s + 1, 1, 0);
+        MXS_ASTEP(s + 2, 2, 1);
+        MXS_ASTEP(s + 3, 3, 2);
+        MXS_ASTEP(s + 4, 4, 3);
     }
 done:
-#undef MXS_DSTEP
+#undef MXS_ASTEP
     if (pend) {
+        f32x4_t sa[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            f32x4_t sa[4];
-            load_sa(i, sa);
+        for (int q = 0; q < 4; ++q) sa[q] = *reinterpret_cast<const f32x4_t *>(pCA + 8 * q + 4 * h);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) epi(i, j, sa);
+        for (int j = 0; j < 4; ++j) {
+            const float cw = __builtin_fabsf(pCW[j * 32 + l32]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[j][4 * q + e] =
+                        __builtin_fmaf((float)I[j][4 * q + e], __builtin_fabsf(sa[q][e]) * cw, acc[j][4 * q + e]);
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + j * 32 + l32;
+        if (col >= N) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 32 + l32;
-            if (col >= N) continue;
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * q + 4 * h + r;
-                    if (row < M) Y[row * ldy + col] = acc[i][j][4 * q + r];
-                }
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 32 * wave + 8 * q + 4 * h + r;
+                if (row < M) Y[row * ldy + col] = acc[j][4 * q + r];
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1771,7 +1768,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ p
     Y[t * ldy + n] = v;
 }
 
-// Row-tiles per group of k_gemm_dma's tile order. When every tile runs in
+// Row-tiles per group of k_gemm_a2r's tile order. When every tile runs in
 // the first wave of workgroups, each XCD's run of 32 tiles then spans 4 row-
 // by 8 column-tiles (8 MB of int8 operands at K = 4096 rather than 10 MB with
 // 8 by 4), which measured 2-3 % faster at 2048 x 4096 x 4096; shapes with
@@ -1942,14 +1939,14 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int
     const Segs S = make_segs(A.n8, A.n6, A.n4);
     const int64_t nb = A.K / 32, nbp = L.Kp / 32;
     const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
-    PrepJob ja{view_of(A), M, L.Mp, ac, acs, L.Mp / 64};
-    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
+    PrepJob ja{view_of(A), M, L.Mp, ac, acs, L.Mp / 64, 1};
+    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64, 0};
     const int64_t ta = ja.tiles_r * windows, tw = jw.tiles_r * windows;
     hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
                        M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
     return hipGetLastError();
 }
@@ -2077,13 +2074,13 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
     const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
     hipError_t e = launch_quant_prep(X, dt, M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs, st);
     if (e != hipSuccess) return e;
-    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64};
+    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64, 0};
     const int64_t tw = jw.tiles_r * windows;
     hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, A.K, L.Kp, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_dma, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
+    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
                        M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
     return hipGetLastError();
 }

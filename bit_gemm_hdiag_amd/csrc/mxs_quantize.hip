@@ -176,6 +176,12 @@ __global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X
     }
 }
 
+// Rows up to kStageLdsLong bytes of LDS (permutation + row) still stream
+// through the register ring: one workgroup per CU for the longest rows (the
+// 28672-column down-projection input in bf16 needs 112 KiB), rather than
+// gathering every element from global memory.
+constexpr int64_t kStageLdsLong = 144 * 1024;
+
 template <typename T, int PPT>
 hipError_t launch_gather_pf(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
                             int64_t lds_bytes, hipStream_t st) {
@@ -185,7 +191,7 @@ hipError_t launch_gather_pf(const T *X, int64_t ldx, const int32_t *perm, const 
     // measured 24 % slower for 4096 x 4096.)
     constexpr int DEPTH = 2;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_pf<T, PPT, DEPTH>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLdsLong);
     if (e != hipSuccess) return e;
     const int64_t per_cu = (160 * 1024) / lds_bytes;
     int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
@@ -211,7 +217,7 @@ hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Plan
     const int64_t lds_bytes = ((2 * P.K + 15) / 16) * 16 + P.K * (int64_t)sizeof(T);
     const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
     const int64_t ppt = ceil_div(P.K * (int64_t)sizeof(T) / 16, 256);
-    if (vec && lds_bytes <= kStageLds && P.K <= 65536 && ppt <= 16) {
+    if (vec && lds_bytes <= kStageLdsLong && P.K <= 65536 && ppt <= 16) {
         if (ppt <= 1) return launch_gather_pf<T, 1>(X, ldx, perm, P, R, lds_bytes, st);
         if (ppt <= 2) return launch_gather_pf<T, 2>(X, ldx, perm, P, R, lds_bytes, st);
         if (ppt <= 4) return launch_gather_pf<T, 4>(X, ldx, perm, P, R, lds_bytes, st);
