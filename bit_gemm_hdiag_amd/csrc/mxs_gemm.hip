@@ -645,7 +645,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     float acc[4][16];
     v16i I[4];
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    v4i zb;   // a zero B operand the compiler cannot see through (restart MFMAs stay distinct)
+    // a zero B operand the compiler cannot see through, for the restart
+    // MFMAs; the four tiles' restarts share their A operand too, so each uses
+    // its own B lane-broadcast pattern (blgp = j; a zero B stays zero under
+    // any of them): otherwise they would be merged into one MFMA plus vector
+    // copies of its result
+    v4i zb;
     {
         int z;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -674,7 +679,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
                 for (int e = 0; e < 4; ++e)
                     acc[j][4 * q + e] =
                         __builtin_fmaf((float)I[j][4 * q + e], __builtin_fabsf(sa[q][e]) * cw, acc[j][4 * q + e]);
-            I[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 0);
+            switch (j) {   // blgp must be a constant
+            case 0: I[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 0); break;
+            case 1: I[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 1); break;
+            case 2: I[2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 2); break;
+            default: I[3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, zb, zero, 0, 0, 3); break;
+            }
         }
     };
     auto compute = [&](int st, const int8_t *sbase, const v4i (&fa)[kDSB]) {
