@@ -568,9 +568,10 @@ def stage_summary(stages):
     return out
 
 
-def stored_traffic(path, key, source):
+def stored_traffic(path, key, source, sha_key="source_sha256"):
     """Bytes per call from a stored counter summary (key = value lines), or
-    None when the summary is missing or `source` changed since it was taken."""
+    None when the summary is missing or `source` changed since it was taken
+    (its hash no longer equals the summary's `sha_key`)."""
     try:
         kv = {}
         with open(path) as f:
@@ -580,7 +581,7 @@ def stored_traffic(path, key, source):
                     kv[k.strip()] = v.strip()
         with open(source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        if kv.get("source_sha256") != sha:
+        if kv.get(sha_key) != sha:
             return None
         return float(kv[key])
     except (OSError, KeyError, ValueError):
@@ -603,8 +604,8 @@ def roofline_of(stage, d):
     else:
         ach = d["bytes"] / d["s"]
         r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s", frac=ach / HBM_PEAK,
-                 traffic=(stored_traffic(BLOCK_TRAFFIC, "calibrate_bytes_per_call", COLSUM_SOURCE)
-                          if stage == "calibrate" else None))
+                 traffic=(stored_traffic(BLOCK_TRAFFIC, "calibrate_bytes_per_call", COLSUM_SOURCE,
+                                         "colsum_source_sha256") if stage == "calibrate" else None))
     r.update(stage=stage, launch_us=per_call_s * 1e6, algorithmic_bytes_per_launch=d["bytes"] / d["calls"],
              launches_per_step=d["calls"])
     return r
