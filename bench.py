@@ -614,7 +614,9 @@ def roofline_of(stage, d):
 def mlp_gemms(mx, synth, torch, reps=10):
     """The Llama-3-8B MLP GEMMs at 4096 tokens (gate/up 14336 x 4096 at
     3/10/87 %, down 4096 x 14336 at 8/20/72 %), mxs_mixed_gemm and
-    mxs_mixed_gemm_mx, graph-replayed back to back (inputs of 60-240 MB)."""
+    mxs_mixed_gemm_mx, graph-replayed back to back (inputs of 60-240 MB).
+    The channel map is the method's own: calibrate over 8 x 2048 tokens,
+    score, allocate."""
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[3]
     M = cfg["M"]
@@ -626,8 +628,11 @@ def mlp_gemms(mx, synth, torch, reps=10):
         seed = 3000 + 16 * li
         gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
         blocks = mx.mxs_budget_blocks(K, *lay["budget"])
-        perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(dev)
-        Wq = mx.mxs_quantize(synth.weights(N, K, seed + synth.ROLE_W, device=dev), perm, *blocks)
+        W = synth.weights(N, K, seed + synth.ROLE_W, device=dev)
+        h = mx.mxs_calibrate(synth.activations(cfg["calib_rows"], K, seed + synth.ROLE_CALIB, gains, device=dev))
+        _, perm = mx.mxs_allocate(mx.mxs_score(W, h), *lay["budget"])
+        Wq = mx.mxs_quantize(W, perm, *blocks)
+        del W
         Aq = mx.mxs_quantize(synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev), perm, *blocks)
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ops = 2 * M * N * K
