@@ -68,23 +68,10 @@ def log(*a):
 
 
 def measured_traffic(key="traffic_bytes_per_call"):
-    """HBM bytes per mixed_gemm call (key traffic_bytes_per_call_mx: per
-    mixed_gemm_mx call) from the stored counter summary, or None when the
+    """HBM bytes per q_proj mixed_gemm call (key traffic_bytes_per_call_mx:
+    per mixed_gemm_mx call) from the stored counter summary, or None when the
     summary is missing or the GEMM source changed since it was taken."""
-    try:
-        kv = {}
-        with open(GEMM_TRAFFIC) as f:
-            for line in f:
-                if "=" in line and not line.lstrip().startswith("#"):
-                    k, v = line.split("=", 1)
-                    kv[k.strip()] = v.strip()
-        with open(GEMM_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if kv.get("source_sha256") != sha:
-            return None
-        return float(kv[key])
-    except (OSError, KeyError, ValueError):
-        return None
+    return stored_traffic(GEMM_TRAFFIC, key, GEMM_SOURCE)
 
 
 def copy_probe(torch):
@@ -654,13 +641,13 @@ def block_cpu_sample(w, torch):
     with the factor that scales each stage's sample to the whole step."""
     M, T = w["M"], w["T"]
     S = dict(calib=[], layers=[], kv=[], scale={})
-    tc = 8192
+    tc = 16384
     for inp, I in w["inputs"].items():
         S["calib"].append(I["Xc"][:tc].float().cpu().numpy())
     S["scale"]["calibrate"] = T / tc
-    wr = 4                    # score and quantize W on 1/4 of every weight's rows
-    xr = 4                    # quantize X on 1/4 of the tokens
-    gr = 256                  # GEMM on 256 tokens against the sampled weight rows
+    wr = 2                    # score and quantize W on 1/2 of every weight's rows
+    xr = 2                    # quantize X on 1/2 of the tokens
+    gr = 512                  # GEMM on 512 tokens against the sampled weight rows
     for L in w["layers"]:
         X = w["inputs"][L["inp"]]["X"]
         S["layers"].append(dict(name=L["name"], K=L["K"], blocks=L["blocks"],
@@ -754,9 +741,9 @@ def block_cpu_baseline(w, torch, gemm_ops):
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     step_all = sum(t_all.values())
     res = dict(value=gemm_ops / step_all / 1e12, unit="TOPS", cores=cores, kind="oracle",
-               sample=(f"extrapolated: calibrate on 8192 of the 262144 tokens of each input (x32), score and "
-                       f"quantize W on 1/4 of every weight's rows (x4), quantize X on 512 of 2048 tokens (x4), "
-                       f"the GEMM on 256 tokens x 1/4 of the weight rows (x32), K/V in full; "
+               sample=(f"extrapolated: calibrate on 16384 of the 262144 tokens of each input (x16), score and "
+                       f"quantize W on 1/2 of every weight's rows (x2), quantize X on 1024 of 2048 tokens (x2), "
+                       f"the GEMM on 512 tokens x 1/2 of the weight rows (x8), K/V in full; "
                        f"{wall_all:.1f} s of CPU work on {cores} threads"),
                step_s=step_all, stage_s=t_all)
     sub = 8
@@ -922,7 +909,7 @@ def q_proj_line(mx, synth, torch, args):
     achieved = ops / gemm_call_s / 1e12
     roofline = dict(bound="mfma", achieved=achieved, peak=INT8_PEAK / 1e12, unit="TOP/s",
                     frac=achieved * 1e12 / INT8_PEAK, traffic=measured_traffic(),
-                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_dma (int8 MFMA)",
+                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_a2r (int8 MFMA)",
                     algorithmic_ops_per_launch=ops, launch_us=gemm_call_s * 1e6,
                     algorithmic_bytes_per_launch=work["mixed_gemm"]["bytes"])
     ach_x = ops / gemm_x / 1e12
@@ -934,7 +921,7 @@ def q_proj_line(mx, synth, torch, args):
     qx = stage_out["quantize_x"]
     ach_f = ops / gemm_f / 1e12
     fused = {"entry": "mxs_mixed_gemm_fused (X quantized into the prefill operand: k_quant_prep + "
-                      "k_gemm_prep of W + k_gemm_dma; the step drops its quantize_x stage)",
+                      "k_gemm_prep of W + k_gemm_a2r; the step drops its quantize_x stage)",
              "value": ops / step_f / 1e12, "ms_per_step": step_f * 1e3, "launch_us": gemm_f * 1e6,
              "achieved": ach_f, "unit": "TOP/s", "peak": INT8_PEAK / 1e12, "frac": ach_f * 1e12 / INT8_PEAK,
              "cold_us": stage_out["mixed_gemm_fused"]["ms"] * 1e3,
