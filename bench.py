@@ -15,9 +15,11 @@ the seven layers) over the block step time, in TOPS, with mxs_mixed_gemm
 TOPS) and fraction of its peak, from HIP events around every call on the
 library's stream in the timed steps; `roofline` is for the stage with the
 largest share of the step, `roofline_gemm` and `roofline_calibrate` for the
-GEMM and calibration calls; `variant_mx` and `variant_fused` repeat the step
-with mxs_mixed_gemm_mx (fp6 block-scaled MFMA prefill) and
-mxs_mixed_gemm_fused (X quantized inside the product). `cpu_baseline` is the
+GEMM and calibration calls; `variant_mx`, `variant_fused` and
+`variant_prepared` repeat the step with mxs_mixed_gemm_mx (fp6 block-scaled
+MFMA prefill), mxs_mixed_gemm_fused (X quantized inside the product) and
+mxs_prepare_weights + mxs_mixed_gemm_prepared (W's operand built once per
+weight, a prepare_w stage). `cpu_baseline` is the
 CPU oracle on a bounded sample of the step, extrapolated (all host cores,
 and one core in a child process). Extra keys: `q_proj_step` (the Llama-3-8B
 q_proj-shaped layer step), `mlp_gemm` (Llama-3-8B MLP GEMMs at 4096 tokens)
@@ -442,6 +444,8 @@ def block_workload(mx, synth, torch, dev):
             perm=torch.empty(K, dtype=torch.int32, device=dev),
             ws_sc=torch.empty(max(1, mx.mxs_score_workspace(N, K)), **u8),
             Wq=mx.qmat_alloc(N, K, *blocks, dev), Aq=mx.qmat_alloc(M, K, *blocks, dev)))
+        L = w["layers"][-1]
+        L["wp"] = torch.empty(max(1, mx.mxs_prepare_weights_size(L["Wq"])), **u8)
     maxN = max(L["N"] for L in w["layers"])
     ybuf = torch.empty(M * maxN, dtype=torch.float32, device=dev)
     for L in w["layers"]:
@@ -450,6 +454,8 @@ def block_workload(mx, synth, torch, dev):
     w["ws_gx"] = torch.empty(max(max(mx.mxs_mixed_gemm_mx_workspace(L["Aq"], L["Wq"]) for L in w["layers"]), 1), **u8)
     w["ws_gf"] = torch.empty(max(max(mx.mxs_mixed_gemm_fused_workspace(M, torch.bfloat16, L["Wq"])
                                      for L in w["layers"]), 1), **u8)
+    w["ws_gp"] = torch.empty(max(max(mx.mxs_mixed_gemm_prepared_workspace(L["Aq"], L["Wq"]) for L in w["layers"]), 1),
+                             **u8)
     # the layer's K and V stacked as one [2 T, H, D] tensor: one quantize_kv launch
     kv = cfg["kv"]
     w["kv_shape"] = kv
@@ -462,9 +468,13 @@ def block_workload(mx, synth, torch, dev):
 
 def block_calls(mx, w, variant=None):
     """One block step as (stage, label, fn, work) in stream order; work is the
-    call's algorithmic bytes (and ops for the GEMM). variant "mx": the GEMMs
-    are mxs_mixed_gemm_mx; "fused": quantize_x + GEMM become one
-    mxs_mixed_gemm_fused call per layer."""
+    call's algorithmic bytes (and ops for the GEMM). By default the GEMMs are
+    mxs_mixed_gemm (both operands prepared inside every call). variant
+    "prepared": each weight's prefill operand is built once after its
+    quantisation (a prepare_w stage) and the GEMMs are
+    mxs_mixed_gemm_prepared; "fused": quantize_x + GEMM become one
+    mxs_mixed_gemm_fused call per layer; "mx": the GEMMs are
+    mxs_mixed_gemm_mx."""
     M, T = w["M"], w["T"]
     calls = []
     for inp, I in w["inputs"].items():
@@ -484,6 +494,11 @@ def block_calls(mx, w, variant=None):
         pr = packed_row_bytes(L["K"], L["blocks"])
         calls.append(("quantize_w", L["name"], lambda L=L: mx.mxs_quantize(L["W"], L["perm"], *L["blocks"], out=L["Wq"]),
                       dict(bytes=L["N"] * L["K"] * 2 + L["N"] * pr + 4 * L["K"])))
+    if variant == "prepared":
+        for L in w["layers"]:
+            pr = packed_row_bytes(L["K"], L["blocks"])
+            calls.append(("prepare_w", L["name"], lambda L=L: mx.mxs_prepare_weights(L["Wq"], out=L["wp"]),
+                          dict(bytes=L["N"] * pr + mx.mxs_prepare_weights_size(L["Wq"]))))
     for L in w["layers"]:
         pr = packed_row_bytes(L["K"], L["blocks"])
         X = w["inputs"][L["inp"]]["X"]
@@ -497,6 +512,8 @@ def block_calls(mx, w, variant=None):
                       dict(bytes=M * L["K"] * 2 + M * pr + 4 * L["K"])))
         if variant == "mx":
             fn = lambda L=L: mx.mxs_mixed_gemm_mx(L["Aq"], L["Wq"], L["Y"], ws=w["ws_gx"])
+        elif variant == "prepared":
+            fn = lambda L=L: mx.mxs_mixed_gemm_prepared(L["Aq"], L["Wq"], L["wp"], L["Y"], ws=w["ws_gp"])
         else:
             fn = lambda L=L: mx.mxs_mixed_gemm(L["Aq"], L["Wq"], L["Y"], ws=w["ws_g"])
         calls.append(("mixed_gemm", L["name"], fn, gemm_work))
@@ -579,14 +596,16 @@ BLOCK_TRAFFIC = os.path.join(ROOT, "profiles", "70b_block.traffic.txt")
 COLSUM_SOURCE = os.path.join(ROOT, "bit_gemm_hdiag_amd", "csrc", "mxs_colsum.hip")
 
 
-def roofline_of(stage, d):
+def roofline_of(stage, d, prepared=False):
     """Roofline object of one stage's calls: algorithmic work per call over
-    the mean call duration (Σ work / Σ time over the timed calls)."""
+    the mean call duration (Σ work / Σ time over the timed calls). prepared:
+    the GEMM calls are mxs_mixed_gemm_prepared (their own stored traffic)."""
     per_call_s = d["s"] / d["calls"]
     if d["ops"]:
         ach = d["ops"] / d["s"]
+        key = "mixed_gemm_prepared_bytes_per_call" if prepared else "mixed_gemm_bytes_per_call"
         r = dict(bound="mfma", achieved=ach / 1e12, peak=INT8_PEAK / 1e12, unit="TOP/s", frac=ach / INT8_PEAK,
-                 traffic=stored_traffic(BLOCK_TRAFFIC, "mixed_gemm_bytes_per_call", GEMM_SOURCE),
+                 traffic=stored_traffic(BLOCK_TRAFFIC, key, GEMM_SOURCE),
                  algorithmic_ops_per_launch=d["ops"] / d["calls"])
     else:
         ach = d["bytes"] / d["s"]
@@ -600,7 +619,8 @@ def roofline_of(stage, d):
 
 def mlp_gemms(mx, synth, torch, reps=10):
     """The Llama-3-8B MLP GEMMs at 4096 tokens (gate/up 14336 x 4096 at
-    3/10/87 %, down 4096 x 14336 at 8/20/72 %), mxs_mixed_gemm and
+    3/10/87 %, down 4096 x 14336 at 8/20/72 %), mxs_mixed_gemm,
+    mxs_mixed_gemm_prepared (W prepared once, outside the timing) and
     mxs_mixed_gemm_mx, graph-replayed back to back (inputs of 60-240 MB).
     The channel map is the method's own: calibrate over 8 x 2048 tokens,
     score, allocate."""
@@ -624,12 +644,17 @@ def mlp_gemms(mx, synth, torch, reps=10):
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ops = 2 * M * N * K
         d = dict(shape=f"{M}x{N}x{K}", blocks=list(blocks))
-        for entry in ("mxs_mixed_gemm", "mxs_mixed_gemm_mx"):
+        wp = mx.mxs_prepare_weights(Wq)
+        for entry in ("mxs_mixed_gemm", "mxs_mixed_gemm_prepared", "mxs_mixed_gemm_mx"):
             ws = torch.empty(max(1, getattr(mx, entry + "_workspace")(Aq, Wq)), dtype=torch.uint8, device=dev)
             f = getattr(mx, entry)
-            t = time_graph(torch, lambda: f(Aq, Wq, Y, ws=ws), reps)
+            if entry == "mxs_mixed_gemm_prepared":
+                t = time_graph(torch, lambda: f(Aq, Wq, wp, Y, ws=ws), reps)
+            else:
+                t = time_graph(torch, lambda: f(Aq, Wq, Y, ws=ws), reps)
             d[entry] = dict(us=t * 1e6, TOPS=ops / t / 1e12, int8_mfma_frac=ops / t / INT8_PEAK)
             del ws
+        del wp
         out[lay["name"]] = d
         log("mlp", json.dumps(d))
         del Wq, Aq, Y
@@ -809,7 +834,10 @@ def block_line(mx, synth, torch, args):
     if not args.no_extras:
         for variant, key, entry in (("mx", "variant_mx", "mxs_mixed_gemm_mx (fp6 block-scaled MFMA prefill)"),
                                     ("fused", "variant_fused", "mxs_mixed_gemm_fused (X quantized inside the "
-                                                               "product; no quantize_x stage)")):
+                                                               "product; no quantize_x stage)"),
+                                    ("prepared", "variant_prepared", "mxs_prepare_weights once per weight after "
+                                                                     "its quantisation (prepare_w stage), then "
+                                                                     "mxs_mixed_gemm_prepared")):
             log(f"the block step with {entry}")
             sv, st = run_block_steps(torch, block_calls(mx, w, variant), max(3, args.steps // 2), 2)
             g = st["mixed_gemm"]
@@ -817,6 +845,10 @@ def block_line(mx, synth, torch, args):
                             gemm_ms_per_step=g["s"] * 1e3, gemm_TOPS=g["ops"] / g["s"] / 1e12,
                             int8_peak_frac=g["ops"] / g["s"] / INT8_PEAK,
                             fp6_peak_frac=g["ops"] / g["s"] / FP6_PEAK if variant == "mx" else None)
+            if variant == "prepared":
+                p = st["prepare_w"]
+                out[key].update(prepare_w_ms_per_step=p["s"] * 1e3,
+                                roofline_gemm=roofline_of("mixed_gemm", g, prepared=True))
     if not args.no_cpu:
         log("cpu baseline (oracle, sampled)")
         out["cpu_baseline"] = block_cpu_baseline(w, torch, gemm_ops)

@@ -72,6 +72,13 @@ def _load():
         "mxs_attend_kv4": (S, [P, P, P, P, P, c_int64, c_int64, c_int64, c_int64, ctypes.c_float, P, P, c_size_t, P]),
         "mxs_mixed_gemm_fused_workspace": (c_size_t, [c_int64, c_int32, POINTER(_QMat)]),
         "mxs_mixed_gemm_fused": (S, [P, c_int32, c_int64, c_int64, P, POINTER(_QMat), P, c_int64, P, c_size_t, P]),
+        "mxs_prepare_weights_size": (c_size_t, [POINTER(_QMat)]),
+        "mxs_prepare_weights": (S, [POINTER(_QMat), P, c_size_t, P]),
+        "mxs_mixed_gemm_prepared_workspace": (c_size_t, [POINTER(_QMat), POINTER(_QMat)]),
+        "mxs_mixed_gemm_prepared": (S, [POINTER(_QMat), POINTER(_QMat), P, c_size_t, P, c_int64, P, c_size_t, P]),
+        "mxs_mixed_gemm_fused_prepared_workspace": (c_size_t, [c_int64, c_int32, POINTER(_QMat)]),
+        "mxs_mixed_gemm_fused_prepared": (S, [P, c_int32, c_int64, c_int64, P, POINTER(_QMat), P, c_size_t, P,
+                                              c_int64, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -85,7 +92,9 @@ EXPORTED = ("mxs_status_string", "mxs_last_error", "mxs_version", "mxs_budget_bl
             "mxs_allocate", "mxs_quantize", "mxs_mixed_gemm_workspace", "mxs_mixed_gemm", "mxs_mixed_gemm_noalloc",
             "mxs_mixed_gemm_mx_workspace", "mxs_mixed_gemm_mx", "mxs_quantize_kv", "mxs_allocate_blocks",
             "mxs_output_error_workspace", "mxs_output_error", "mxs_layer_budget", "mxs_attend_kv4_workspace",
-            "mxs_attend_kv4", "mxs_mixed_gemm_fused_workspace", "mxs_mixed_gemm_fused")
+            "mxs_attend_kv4", "mxs_mixed_gemm_fused_workspace", "mxs_mixed_gemm_fused",
+            "mxs_prepare_weights_size", "mxs_prepare_weights", "mxs_mixed_gemm_prepared_workspace",
+            "mxs_mixed_gemm_prepared", "mxs_mixed_gemm_fused_prepared_workspace", "mxs_mixed_gemm_fused_prepared")
 
 
 def _check(status: int, where: str):
@@ -302,9 +311,7 @@ def mxs_mixed_gemm_fused_workspace(M: int, dtype: torch.dtype, W: QMat) -> int:
     return int(_lib.mxs_mixed_gemm_fused_workspace(M, dt, ctypes.byref(W.c_struct())))
 
 
-def mxs_mixed_gemm_fused(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, Y: torch.Tensor | None = None,
-                         ws=None) -> torch.Tensor:
-    """Y [M, N] fp32 = mixed_gemm(quantize(X[:, perm] at W's block counts), W), X quantized inside the call."""
+def _fused_args(X: torch.Tensor, perm, W: QMat, Y):
     px, ldx = _dev2d(X, "X")
     M, K = X.shape
     if K != W.K:
@@ -317,6 +324,13 @@ def mxs_mixed_gemm_fused(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, Y:
     if Y.dtype != torch.float32:
         raise TypeError("Y must be fp32")
     py, ldy = _dev2d(Y, "Y")
+    return px, ldx, M, Y, py, ldy
+
+
+def mxs_mixed_gemm_fused(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, Y: torch.Tensor | None = None,
+                         ws=None) -> torch.Tensor:
+    """Y [M, N] fp32 = mixed_gemm(quantize(X[:, perm] at W's block counts), W), X quantized inside the call."""
+    px, ldx, M, Y, py, ldy = _fused_args(X, perm, W, Y)
     w = W.c_struct()
     dt = _dtype(X)
     if ws is None:
@@ -325,6 +339,69 @@ def mxs_mixed_gemm_fused(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, Y:
         p, n = ws.data_ptr(), ws.numel() * ws.element_size()
     _check(_lib.mxs_mixed_gemm_fused(px, dt, M, ldx, _ptr(perm), ctypes.byref(w), py, ldy, p, n,
                                      _stream(X.device)), "mxs_mixed_gemm_fused")
+    return Y
+
+
+# ------------------------------------------------------------ prepared weights
+def mxs_prepare_weights_size(W: QMat) -> int:
+    return int(_lib.mxs_prepare_weights_size(ctypes.byref(W.c_struct())))
+
+
+def mxs_prepare_weights(W: QMat, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W's prefill operand built once (uint8 device buffer, contents private
+    to the library), for mxs_mixed_gemm_prepared / mxs_mixed_gemm_fused_prepared."""
+    n = mxs_prepare_weights_size(W)
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.uint8, device=W.sc.device)
+    if out.dtype != torch.uint8 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 GPU tensor")
+    _check(_lib.mxs_prepare_weights(ctypes.byref(W.c_struct()), out.data_ptr(), out.numel(),
+                                    _stream(out.device)), "mxs_prepare_weights")
+    return out
+
+
+def mxs_mixed_gemm_prepared_workspace(A: QMat, W: QMat) -> int:
+    return int(_lib.mxs_mixed_gemm_prepared_workspace(ctypes.byref(A.c_struct()), ctypes.byref(W.c_struct())))
+
+
+def mxs_mixed_gemm_prepared(A: QMat, W: QMat, wprep: torch.Tensor, Y: torch.Tensor | None = None,
+                            ws=None) -> torch.Tensor:
+    """mxs_mixed_gemm with W's operand taken from mxs_prepare_weights(W)."""
+    dev = A.sc.device
+    if Y is None:
+        Y = torch.empty((A.rows, W.rows), dtype=torch.float32, device=dev)
+    if Y.dtype != torch.float32:
+        raise TypeError("Y must be fp32")
+    py, ldy = _dev2d(Y, "Y")
+    a, w = ctypes.byref(A.c_struct()), ctypes.byref(W.c_struct())
+    if ws is None:
+        p, n = _workspace(int(_lib.mxs_mixed_gemm_prepared_workspace(a, w)), dev, None)
+    else:
+        p, n = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check(_lib.mxs_mixed_gemm_prepared(a, w, wprep.data_ptr(), wprep.numel() * wprep.element_size(), py, ldy,
+                                        p, n, _stream(dev)), "mxs_mixed_gemm_prepared")
+    return Y
+
+
+def mxs_mixed_gemm_fused_prepared_workspace(M: int, dtype: torch.dtype, W: QMat) -> int:
+    dt = MXS_BF16 if dtype == torch.bfloat16 else MXS_F32
+    return int(_lib.mxs_mixed_gemm_fused_prepared_workspace(M, dt, ctypes.byref(W.c_struct())))
+
+
+def mxs_mixed_gemm_fused_prepared(X: torch.Tensor, perm: torch.Tensor | None, W: QMat, wprep: torch.Tensor,
+                                  Y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """mxs_mixed_gemm_fused with W's operand taken from mxs_prepare_weights(W)."""
+    px, ldx, M, Y, py, ldy = _fused_args(X, perm, W, Y)
+    w = W.c_struct()
+    dt = _dtype(X)
+    if ws is None:
+        p, n = _workspace(int(_lib.mxs_mixed_gemm_fused_prepared_workspace(M, dt, ctypes.byref(w))), X.device,
+                          None)
+    else:
+        p, n = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check(_lib.mxs_mixed_gemm_fused_prepared(px, dt, M, ldx, _ptr(perm), ctypes.byref(w), wprep.data_ptr(),
+                                              wprep.numel() * wprep.element_size(), py, ldy, p, n,
+                                              _stream(X.device)), "mxs_mixed_gemm_fused_prepared")
     return Y
 
 

@@ -262,7 +262,17 @@ mxs_status mxs_quantize(const void *X, mxs_dtype dtype, int64_t ldx, const int32
 
 size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W) {
     if (!A || !W) return 0;
-    return mxs::gemm_workspace(*A, *W);
+    return mxs::gemm_workspace(*A, *W, false);
+}
+
+size_t mxs_mixed_gemm_prepared_workspace(const mxs_qmat *A, const mxs_qmat *W) {
+    if (!A || !W) return 0;
+    return mxs::gemm_workspace(*A, *W, true);
+}
+
+size_t mxs_prepare_weights_size(const mxs_qmat *W) {
+    if (!W || W->rows < 0 || W->K <= 0 || W->K % 32) return 0;
+    return mxs::wprep_bytes(*W);
 }
 
 // Operand loads are 16/4/8-byte vector loads per row.
@@ -289,19 +299,46 @@ static mxs_status check_gemm(const mxs_qmat *A, const mxs_qmat *W, const float *
     return MXS_OK;
 }
 
+// The prepared-weights buffer: mxs_prepare_weights_size(W) bytes, 256-byte
+// aligned.
+static mxs_status check_wprep(const mxs_qmat *W, const void *wprep, size_t wprep_bytes, const char *name) {
+    const size_t need = mxs::wprep_bytes(*W);
+    if (need && (!wprep || wprep_bytes < need || !aligned(wprep, 256)))
+        return fail(MXS_ERR_WORKSPACE, "%s: prepared weights need %zu bytes, 256-byte aligned (got %zu)", name, need,
+                    wprep ? wprep_bytes : 0);
+    return MXS_OK;
+}
+
 mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
-    const size_t need = A && W ? mxs::gemm_workspace(*A, *W) : 0;
+    const size_t need = A && W ? mxs::gemm_workspace(*A, *W, false) : 0;
     const mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm");
     if (s != MXS_OK) return s;
-    return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, ws_bytes, stream), "mixed_gemm");
+    return device_status(mxs::launch_mixed_gemm(*A, *W, nullptr, Y, ldy, ws, stream), "mixed_gemm");
+}
+
+mxs_status mxs_prepare_weights(const mxs_qmat *W, void *wprep, size_t wprep_bytes, hipStream_t stream) {
+    mxs_status s = check_qmat(W, "W");
+    if (s != MXS_OK) return s;
+    if ((s = check_planes_aligned(W, "prepare_weights")) != MXS_OK) return s;
+    if ((s = check_wprep(W, wprep, wprep_bytes, "prepare_weights")) != MXS_OK) return s;
+    return device_status(mxs::launch_prepare_weights(*W, wprep, stream), "prepare_weights");
+}
+
+mxs_status mxs_mixed_gemm_prepared(const mxs_qmat *A, const mxs_qmat *W, const void *wprep, size_t wprep_bytes,
+                                   float *Y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const size_t need = A && W ? mxs::gemm_workspace(*A, *W, true) : 0;
+    mxs_status s = check_gemm(A, W, Y, ldy, ws, ws_bytes, need, "mixed_gemm_prepared");
+    if (s != MXS_OK) return s;
+    if ((s = check_wprep(W, wprep, wprep_bytes, "mixed_gemm_prepared")) != MXS_OK) return s;
+    return device_status(mxs::launch_mixed_gemm(*A, *W, wprep, Y, ldy, ws, stream), "mixed_gemm_prepared");
 }
 
 mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
                                   hipStream_t stream) {
     mxs_status s = check_gemm(A, W, Y, ldy, nullptr, 0, 0, "mixed_gemm_noalloc");   // arguments first
     if (s != MXS_OK) return s;
-    const size_t need = mxs::gemm_workspace(*A, *W);
+    const size_t need = mxs::gemm_workspace(*A, *W, false);
     if (need > MXS_NOALLOC_SCRATCH_BYTES)
         return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm_noalloc: these shapes need %zu bytes of workspace, above the "
                     "%zu-byte scratch array (use mxs_mixed_gemm with a caller workspace)", need,
@@ -311,31 +348,56 @@ mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y
         const hipError_t e = scratch_address(stream, &ws);
         if (e != hipSuccess) return device_status(e, "mixed_gemm_noalloc: scratch address");
     }
-    return device_status(mxs::launch_mixed_gemm(*A, *W, Y, ldy, ws, need, stream), "mixed_gemm_noalloc");
+    return device_status(mxs::launch_mixed_gemm(*A, *W, nullptr, Y, ldy, ws, stream), "mixed_gemm_noalloc");
 }
 
 size_t mxs_mixed_gemm_fused_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W) {
     if (!W || !dtype_ok(dtype) || M < 0 || W->K <= 0 || W->K % 32) return 0;
-    return mxs::gemm_fused_workspace(M, dtype, *W);
+    return mxs::gemm_fused_workspace(M, dtype, *W, false);
+}
+
+size_t mxs_mixed_gemm_fused_prepared_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W) {
+    if (!W || !dtype_ok(dtype) || M < 0 || W->K <= 0 || W->K % 32) return 0;
+    return mxs::gemm_fused_workspace(M, dtype, *W, true);
+}
+
+// Argument checks shared by both fused entry points.
+static mxs_status check_fused(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx, const mxs_qmat *W,
+                              const float *Y, int64_t ldy, const void *ws, size_t ws_bytes, bool w_prepared,
+                              const char *name) {
+    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "%s: unknown dtype %d", name, (int)dtype);
+    mxs_status s = check_qmat(W, "W");
+    if (s != MXS_OK) return s;
+    if (M < 0 || ldx < W->K) return fail(MXS_ERR_SHAPE, "%s: M=%lld ldx=%lld K=%lld", name, (long long)M, (long long)ldx, (long long)W->K);
+    if (M > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "%s: more than 4194304 rows in X", name);
+    const bool work = M > 0 && W->rows > 0;
+    if (work && !X) return fail(MXS_ERR_ARG, "%s: X is NULL", name);
+    if (ldy < W->rows || (!Y && work)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "%s: Y NULL or ldy < N", name);
+    if ((s = check_planes_aligned(W, name)) != MXS_OK) return s;
+    const size_t need = mxs::gemm_fused_workspace(M, dtype, *W, w_prepared);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return fail(MXS_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", name, need, ws ? ws_bytes : 0);
+    return MXS_OK;
 }
 
 mxs_status mxs_mixed_gemm_fused(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx, const int32_t *perm,
                                 const mxs_qmat *W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
                                 hipStream_t stream) {
-    if (!dtype_ok(dtype)) return fail(MXS_ERR_ARG, "mixed_gemm_fused: unknown dtype %d", (int)dtype);
-    mxs_status s = check_qmat(W, "W");
+    const mxs_status s = check_fused(X, dtype, M, ldx, W, Y, ldy, ws, ws_bytes, false, "mixed_gemm_fused");
     if (s != MXS_OK) return s;
-    if (M < 0 || ldx < W->K) return fail(MXS_ERR_SHAPE, "mixed_gemm_fused: M=%lld ldx=%lld K=%lld", (long long)M, (long long)ldx, (long long)W->K);
-    if (M > (int64_t)1 << 22) return fail(MXS_ERR_UNSUPPORTED, "mixed_gemm_fused: more than 4194304 rows in X");
-    const bool work = M > 0 && W->rows > 0;
-    if (work && !X) return fail(MXS_ERR_ARG, "mixed_gemm_fused: X is NULL");
-    if (ldy < W->rows || (!Y && work)) return fail(Y ? MXS_ERR_SHAPE : MXS_ERR_ARG, "mixed_gemm_fused: Y NULL or ldy < N");
-    if ((s = check_planes_aligned(W, "mixed_gemm_fused")) != MXS_OK) return s;
-    const size_t need = mxs::gemm_fused_workspace(M, dtype, *W);
-    if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
-        return fail(MXS_ERR_WORKSPACE, "mixed_gemm_fused: workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
-    return device_status(mxs::launch_mixed_gemm_fused(X, dtype, M, ldx, perm, *W, Y, ldy, ws, ws_bytes, stream),
+    return device_status(mxs::launch_mixed_gemm_fused(X, dtype, M, ldx, perm, *W, nullptr, Y, ldy, ws, stream),
                          "mixed_gemm_fused");
+}
+
+mxs_status mxs_mixed_gemm_fused_prepared(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx,
+                                         const int32_t *perm, const mxs_qmat *W, const void *wprep,
+                                         size_t wprep_bytes, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+    mxs_status s = check_fused(X, dtype, M, ldx, W, Y, ldy, ws, ws_bytes, true, "mixed_gemm_fused_prepared");
+    if (s != MXS_OK) return s;
+    if ((s = check_wprep(W, wprep, wprep_bytes, "mixed_gemm_fused_prepared")) != MXS_OK) return s;
+    return device_status(mxs::launch_mixed_gemm_fused(X, dtype, M, ldx, perm, *W, wprep, Y, ldy, ws, stream),
+                         "mixed_gemm_fused_prepared");
 }
 
 size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W) {

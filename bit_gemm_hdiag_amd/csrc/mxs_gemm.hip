@@ -1791,26 +1791,61 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ p
 // more tiles than CUs keep groups of 8 (4 measured 1-2 % slower there).
 int32_t tile_group(int64_t ntiles) { return ntiles <= 256 ? 4 : 8; }
 
+// Prepared operands of the int8 prefill kernel: codes (A in fragment order,
+// W row-major, rows padded to the tile and K to whole 4-block units) and
+// fp32 window scales [block][row]. A's part comes first in the workspace;
+// W's part is the same bytes whether it sits there or in a buffer filled
+// once by mxs_prepare_weights.
 struct PrepLayout {
     int64_t Mp, Np, Kp;
-    size_t a_codes, a_cs, w_codes, w_cs, total;   // byte offsets
+    size_t a_codes, a_cs, a_bytes;   // offsets inside A's part
+    size_t w_codes, w_cs, w_bytes;   // offsets inside W's part
+    size_t total;                    // both parts
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) {
+PrepLayout prep_layout(int64_t M, int64_t N, int64_t K) {
     PrepLayout L;
-    L.Mp = ceil_div(A.rows, kGBM) * kGBM;
-    L.Np = ceil_div(W.rows, kGBN) * kGBN;
-    L.Kp = ceil_div(A.K, 128) * 128;   // whole 4-block units (prep pads the tail)
+    L.Mp = ceil_div(M, kGBM) * kGBM;
+    L.Np = ceil_div(N, kGBN) * kGBN;
+    L.Kp = ceil_div(K, 128) * 128;   // whole 4-block units (prep pads the tail)
     const int64_t nbp = L.Kp / 32;
-    size_t off = 0;
-    L.a_codes = off; off = align256(off + (size_t)L.Mp * L.Kp);
-    L.w_codes = off; off = align256(off + (size_t)L.Np * L.Kp);
-    L.a_cs = off;    off = align256(off + (size_t)nbp * L.Mp * 4);
-    L.w_cs = off;    off = align256(off + (size_t)nbp * L.Np * 4);
-    L.total = off;
+    L.a_codes = 0;
+    L.a_cs = align256((size_t)L.Mp * L.Kp);
+    L.a_bytes = L.a_cs + align256((size_t)nbp * L.Mp * 4);
+    L.w_codes = 0;
+    L.w_cs = align256((size_t)L.Np * L.Kp);
+    L.w_bytes = L.w_cs + align256((size_t)nbp * L.Np * 4);
+    L.total = L.a_bytes + L.w_bytes;
     return L;
+}
+
+PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) { return prep_layout(A.rows, W.rows, A.K); }
+
+int64_t prep_windows(const Segs &S, int64_t K, int64_t Kp) {
+    return S.win_base[3] + ceil_div(Kp / 32 - K / 32, kG);
+}
+
+// W's prepared operand (k_gemm_prep, W job only) into wp
+hipError_t launch_prep_w(const mxs_qmat &W, const PrepLayout &L, const Segs &S, uint8_t *wp, hipStream_t st) {
+    PrepJob jw{view_of(W), W.rows, L.Np, reinterpret_cast<int8_t *>(wp + L.w_codes),
+               reinterpret_cast<float *>(wp + L.w_cs), L.Np / 64, 0};
+    const int64_t tw = jw.tiles_r * prep_windows(S, W.K, L.Kp);
+    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, W.K, L.Kp, S);
+    return hipGetLastError();
+}
+
+// The int8 prefill product over prepared operands at ap (A's part) and wp
+// (W's part).
+hipError_t launch_a2r(const PrepLayout &L, const Segs &S, int64_t M, int64_t N, int64_t K, const uint8_t *ap,
+                      const uint8_t *wp, float *Y, int64_t ldy, hipStream_t st) {
+    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
+    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st,
+                       reinterpret_cast<const int8_t *>(ap + L.a_codes), reinterpret_cast<const float *>(ap + L.a_cs),
+                       reinterpret_cast<const int8_t *>(wp + L.w_codes), reinterpret_cast<const float *>(wp + L.w_cs),
+                       M, N, L.Mp, L.Np, L.Kp, (int32_t)(K / 32), S, Y, ldy, tile_group(ntiles));
+    return hipGetLastError();
 }
 
 bool use_prefill(const mxs_qmat &A) { return A.rows >= kPrefillMinRows; }
@@ -1927,11 +1962,23 @@ hipError_t launch_small(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t 
 
 }  // namespace
 
-size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W) {
+size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W, bool w_prepared) {
     if (W.rows == 0 || A.rows == 0) return 0;
     if (use_gemv(A, W)) return decode_workspace(A, W);
     if (!use_prefill(A)) return 0;
-    return prep_layout(A, W).total;
+    const PrepLayout L = prep_layout(A, W);
+    return w_prepared ? L.a_bytes : L.total;
+}
+
+size_t wprep_bytes(const mxs_qmat &W) {
+    if (W.rows == 0) return 0;
+    return prep_layout(0, W.rows, W.K).w_bytes;
+}
+
+hipError_t launch_prepare_weights(const mxs_qmat &W, void *wprep, hipStream_t st) {
+    if (W.rows == 0) return hipSuccess;
+    const PrepLayout L = prep_layout(0, W.rows, W.K);
+    return launch_prep_w(W, L, make_segs(W.n8, W.n6, W.n4), static_cast<uint8_t *>(wprep), st);
 }
 
 size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W) {
@@ -1941,30 +1988,32 @@ size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W) {
     return mx_layout(A, W).total;
 }
 
-hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,
-                             void *ws, size_t, hipStream_t st) {
+hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, const void *wprep, float *Y, int64_t ldy,
+                             void *ws, hipStream_t st) {
     const int64_t M = A.rows, N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
     if (!use_prefill(A) || use_gemv(A, W)) return launch_small(A, W, Y, ldy, ws, st);
     const PrepLayout L = prep_layout(A, W);
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    int8_t *ac = reinterpret_cast<int8_t *>(base + L.a_codes);
-    int8_t *wc = reinterpret_cast<int8_t *>(base + L.w_codes);
-    float *acs = reinterpret_cast<float *>(base + L.a_cs);
-    float *wcs = reinterpret_cast<float *>(base + L.w_cs);
+    uint8_t *ap = static_cast<uint8_t *>(ws);
     const Segs S = make_segs(A.n8, A.n6, A.n4);
-    const int64_t nb = A.K / 32, nbp = L.Kp / 32;
-    const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
-    PrepJob ja{view_of(A), M, L.Mp, ac, acs, L.Mp / 64, 1};
-    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64, 0};
-    const int64_t ta = ja.tiles_r * windows, tw = jw.tiles_r * windows;
-    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
+    const int64_t windows = prep_windows(S, A.K, L.Kp);
+    PrepJob ja{view_of(A), M, L.Mp, reinterpret_cast<int8_t *>(ap + L.a_codes), reinterpret_cast<float *>(ap + L.a_cs),
+               L.Mp / 64, 1};
+    const int64_t ta = ja.tiles_r * windows;
+    const uint8_t *wp = static_cast<const uint8_t *>(wprep);
+    if (wp) {   // W prepared already: A's operand only
+        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)ta), dim3(256), 0, st, ja, ja, ta, A.K, L.Kp, S);
+    } else {    // both operands in one launch, W's part after A's
+        uint8_t *wq = ap + L.a_bytes;
+        PrepJob jw{view_of(W), N, L.Np, reinterpret_cast<int8_t *>(wq + L.w_codes),
+                   reinterpret_cast<float *>(wq + L.w_cs), L.Np / 64, 0};
+        const int64_t tw = jw.tiles_r * windows;
+        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
+        wp = wq;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
-                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
-    return hipGetLastError();
+    return launch_a2r(L, S, M, N, A.K, ap, wp, Y, ldy, st);
 }
 
 
@@ -2055,15 +2104,18 @@ hipError_t launch_quant_prep(const void *X, mxs_dtype dt, int64_t M, int64_t ldx
     return launch_quant_prep_d(static_cast<const float *>(X), M, ldx, perm, K, Mp, Kp, S, ac, acs, lds, st);
 }
 
-size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W) {
+size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W, bool w_prepared) {
     if (M == 0 || W.rows == 0) return 0;
     const mxs_qmat A = act_shape(M, W);
-    if (fused_prefill(M, W.K, dt) && !use_gemv(A, W)) return prep_layout(A, W).total;
-    return act_planes(A).total + gemm_workspace(A, W);
+    if (fused_prefill(M, W.K, dt) && !use_gemv(A, W)) {
+        const PrepLayout L = prep_layout(A, W);
+        return w_prepared ? L.a_bytes : L.total;
+    }
+    return act_planes(A).total + gemm_workspace(A, W, w_prepared);
 }
 
 hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64_t ldx, const int32_t *perm,
-                                   const mxs_qmat &W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                   const mxs_qmat &W, const void *wprep, float *Y, int64_t ldy, void *ws,
                                    hipStream_t st) {
     const int64_t N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
@@ -2081,27 +2133,21 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
         A.lds = P.lds;
         hipError_t e = launch_quantize(X, dt, ldx, perm, A, st);
         if (e != hipSuccess) return e;
-        return launch_mixed_gemm(A, W, Y, ldy, base + P.total, ws_bytes - P.total, st);
+        return launch_mixed_gemm(A, W, wprep, Y, ldy, base + P.total, st);
     }
     const PrepLayout L = prep_layout(A, W);
-    int8_t *ac = reinterpret_cast<int8_t *>(base + L.a_codes);
-    int8_t *wc = reinterpret_cast<int8_t *>(base + L.w_codes);
-    float *acs = reinterpret_cast<float *>(base + L.a_cs);
-    float *wcs = reinterpret_cast<float *>(base + L.w_cs);
     const Segs S = make_segs(A.n8, A.n6, A.n4);
-    const int64_t nb = A.K / 32, nbp = L.Kp / 32;
-    const int64_t windows = S.win_base[3] + ceil_div(nbp - nb, kG);
-    hipError_t e = launch_quant_prep(X, dt, M, ldx, perm, A.K, L.Mp, L.Kp, S, ac, acs, st);
+    hipError_t e = launch_quant_prep(X, dt, M, ldx, perm, A.K, L.Mp, L.Kp, S,
+                                     reinterpret_cast<int8_t *>(base + L.a_codes),
+                                     reinterpret_cast<float *>(base + L.a_cs), st);
     if (e != hipSuccess) return e;
-    PrepJob jw{view_of(W), N, L.Np, wc, wcs, L.Np / 64, 0};
-    const int64_t tw = jw.tiles_r * windows;
-    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, A.K, L.Kp, S);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st, ac, acs, wc, wcs,
-                       M, N, L.Mp, L.Np, L.Kp, (int32_t)nb, S, Y, ldy, tile_group(ntiles));
-    return hipGetLastError();
+    const uint8_t *wp = static_cast<const uint8_t *>(wprep);
+    if (!wp) {
+        e = launch_prep_w(W, L, S, base + L.a_bytes, st);
+        if (e != hipSuccess) return e;
+        wp = base + L.a_bytes;
+    }
+    return launch_a2r(L, S, M, N, A.K, base, wp, Y, ldy, st);
 }
 
 hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,

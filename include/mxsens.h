@@ -291,6 +291,37 @@ mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_
 mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
                                   hipStream_t stream);
 
+/*
+ * Weights prepared once for the prefill product ([NL] §1 and §5: no
+ * separate dequantisation pass inside the product). mxs_mixed_gemm expands
+ * both operands' codes into the prefill kernel's exponent-aligned int8
+ * operand, with fp32 window scales, in every call. Weights do not change
+ * between calls, so mxs_prepare_weights builds W's half once, and
+ * mxs_mixed_gemm_prepared and mxs_mixed_gemm_fused_prepared reuse it for any
+ * number of tokens. Their results are bit-identical to mxs_mixed_gemm and
+ * mxs_mixed_gemm_fused on the same planes.
+ * wprep: device buffer of mxs_prepare_weights_size(W) bytes (0 when W has
+ * no rows), 256-byte aligned, owned by the caller. Its contents are private
+ * to the library (W's int8 codes with rows padded to 128 and K to a multiple
+ * of 128, then fp32 scales per block and row). It stays valid while W's
+ * planes and shape are unchanged; a buffer prepared from other planes of the
+ * same shape gives wrong results but no out-of-bounds access.
+ * mxs_mixed_gemm_prepared: A, W, Y, ldy as for mxs_mixed_gemm (W's planes
+ * are still read by the kernels for up to 63 rows of A), ws >=
+ * mxs_mixed_gemm_prepared_workspace(A, W) bytes, 256-byte aligned (A's
+ * prepared operand only). mxs_mixed_gemm_fused_prepared: arguments as
+ * mxs_mixed_gemm_fused, ws >= mxs_mixed_gemm_fused_prepared_workspace(M,
+ * dtype, W) bytes. All asynchronous on `stream`.
+ * Errors: as the calls without preparation, plus MXS_ERR_WORKSPACE when
+ * wprep is NULL, too small or misaligned. mxs_prepare_weights_size returns
+ * 0 for a NULL W or a K that is not a positive multiple of 32.
+ */
+size_t mxs_prepare_weights_size(const mxs_qmat *W);
+mxs_status mxs_prepare_weights(const mxs_qmat *W, void *wprep, size_t wprep_bytes, hipStream_t stream);
+size_t mxs_mixed_gemm_prepared_workspace(const mxs_qmat *A, const mxs_qmat *W);
+mxs_status mxs_mixed_gemm_prepared(const mxs_qmat *A, const mxs_qmat *W, const void *wprep, size_t wprep_bytes,
+                                   float *Y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by mxs_mixed_gemm_mx for these shapes (may be 0). */
 size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W);
 
@@ -321,7 +352,7 @@ mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int
  * kept in the workspace and run the mxs_mixed_gemm kernels.
  * X: [M, ldx >= K] row-major of `dtype` (device); perm: [K] int32 gather
  * form (X column perm[j] becomes position j) or NULL for the identity;
- * W: prepared weights (device planes, the plane alignment mxs_mixed_gemm
+ * W: quantised weights (device planes, the plane alignment mxs_mixed_gemm
  * asks for); Y: [M, ldy >= N] fp32 (device). ws >=
  * mxs_mixed_gemm_fused_workspace(M, dtype, W) bytes, 256-byte aligned, owned
  * by the caller; asynchronous on `stream`.
@@ -332,6 +363,11 @@ size_t mxs_mixed_gemm_fused_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat
 mxs_status mxs_mixed_gemm_fused(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx, const int32_t *perm,
                                 const mxs_qmat *W, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
+size_t mxs_mixed_gemm_fused_prepared_workspace(int64_t M, mxs_dtype dtype, const mxs_qmat *W);
+mxs_status mxs_mixed_gemm_fused_prepared(const void *X, mxs_dtype dtype, int64_t M, int64_t ldx,
+                                         const int32_t *perm, const mxs_qmat *W, const void *wprep,
+                                         size_t wprep_bytes, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                                         hipStream_t stream);
 
 /*
  * KV-cache quantisation (W4A4KV4, [NL] §4 and [REV] "Validation": keys and

@@ -284,3 +284,46 @@ def test_gemm_fused_errors(lib):
     assert wsf(0, 1, w) == 0
     assert wsf(128, 9, w) == 0
 
+
+
+def test_prepared_weights_errors(lib):
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    size = lib.mxs_prepare_weights_size
+    size.restype, size.argtypes = SZ, [P]
+    prep = lib.mxs_prepare_weights
+    prep.restype, prep.argtypes = ctypes.c_int32, [P, P, SZ, P]
+    g = lib.mxs_mixed_gemm_prepared
+    g.restype, g.argtypes = ctypes.c_int32, [P, P, P, SZ, P, I64, P, SZ, P]
+    gws = lib.mxs_mixed_gemm_prepared_workspace
+    gws.restype, gws.argtypes = SZ, [P, P]
+    full = lib.mxs_mixed_gemm_workspace
+    full.restype, full.argtypes = SZ, [P, P]
+    W = qm(rows=16)
+    w = ctypes.byref(W)
+    n = size(w)
+    assert n > 0 and size(None) == 0 and size(ctypes.byref(qm(rows=0))) == 0
+    assert size(ctypes.byref(qm(rows=16, K=48))) == 0                          # K not a multiple of 32
+    assert prep(None, FAKE, n, None) == -1
+    assert prep(w, None, 0, None) == -4
+    assert prep(w, FAKE, n - 1, None) == -4
+    assert prep(w, ctypes.c_void_p(0x10010), n, None) == -4                     # not 256-byte aligned
+    assert prep(ctypes.byref(qm(rows=16, q4=0x20004)), FAKE, n, None) == -6     # misaligned plane
+    A = qm(rows=128)
+    a = ctypes.byref(A)
+    need = gws(a, w)
+    assert 0 < need < full(a, w)                                                # A's operand only
+    assert gws(ctypes.byref(qm(rows=8)), w) == full(ctypes.byref(qm(rows=8)), w)   # decode: same kernels
+    assert g(a, w, None, 0, FAKE, 16, FAKE, need, None) == -4                  # no prepared weights
+    assert g(a, w, FAKE, n - 1, FAKE, 16, FAKE, need, None) == -4
+    assert g(a, w, FAKE, n, FAKE, 16, FAKE, need - 1, None) == -4              # workspace too small
+    assert g(a, ctypes.byref(qm(rows=16, n6=0, n4=2)), FAKE, n, FAKE, 16, FAKE, need, None) == -2
+    f = lib.mxs_mixed_gemm_fused_prepared
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, ctypes.c_int32, I64, I64, P, P, P, SZ, P, I64, P, SZ, P]
+    fws = lib.mxs_mixed_gemm_fused_prepared_workspace
+    fws.restype, fws.argtypes = SZ, [I64, ctypes.c_int32, P]
+    fneed = fws(128, 1, w)
+    assert fneed > 0
+    assert f(FAKE, 1, 128, 64, None, w, None, 0, FAKE, 16, FAKE, fneed, None) == -4
+    assert f(FAKE, 1, 128, 64, None, w, FAKE, n, FAKE, 16, FAKE, fneed - 1, None) == -4
+    assert f(FAKE, 1, 128, 32, None, w, FAKE, n, FAKE, 16, FAKE, fneed, None) == -2   # ldx < K
