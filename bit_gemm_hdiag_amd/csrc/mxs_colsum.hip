@@ -62,13 +62,34 @@ __device__ __forceinline__ uint32_t oct_max_u32(uint32_t x) {
 // block hold the rest of it), squared into the fp64 partial sums.
 // d = v - c * 2^s is exact in fp32 (fma with a power of two whose result is
 // representable), its square exact in fp64.
+// With 8 values per lane the code stays a float: fma(v, 2^-s, 1.5 * 2^23)
+// rounds v / 2^s to nearest even in the low mantissa bits, a median against
+// 1.5 * 2^23 -+ 7 clamps it and subtracting 1.5 * 2^23 gives c exactly (the
+// rule of the packing quantizer); a non-finite block's residual is NaN.
 template <int CPL>
 __device__ __forceinline__ void acc_residual_sq(const float v[CPL], double acc[CPL]) {
+    if constexpr (CPL == 8) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+            a = a > b ? a : b;
+        }
+        const BlockScale bs = block_scale(quad_max_u32(a), 4);
+        const float magic = 12582912.0f, cm = cmax_of(4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], bs.inv, magic), magic - cm, magic + cm);
+            float d = __builtin_fmaf(-(t - magic), bs.scale, v[i]);
+            d = bs.bad ? __builtin_nanf("") : d;
+            const double dd = (double)d;
+            acc[i] = __builtin_fma(dd, dd, acc[i]);
+        }
+        return;
+    }
     int c[CPL];
     BlockScale bs;
-    if constexpr (CPL == 8) {
-        bs = quantize8(v, 4, c);
-    } else {
+    {
         uint32_t a = 0;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
