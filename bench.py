@@ -802,7 +802,7 @@ def block_line(mx, synth, torch, args):
     M = w["M"]
     gemm_ops = sum(2 * M * L["N"] * L["K"] for L in w["layers"])
     log(f"warmup {args.warmup}, timing {args.steps} block steps")
-    step_s, stages = run_block_steps(torch, block_calls(mx, w), args.steps, args.warmup)
+    step_s, stages = run_block_steps(torch, block_calls(mx, w, args.block_variant), args.steps, args.warmup)
     log(f"block step {step_s * 1e3:.3f} ms")
     dominant = max(stages, key=lambda k: stages[k]["s"])
     out = {
@@ -824,11 +824,11 @@ def block_line(mx, synth, torch, args):
                                "8/6/4-bit), quantize X and mixed GEMM at M=2048 for all 7, MXINT4 K and V "
                                "2048x8x128; one step = one block",
                    "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)",
-                   "pipeline_80_layers_s": step_s * 80},
+                   "pipeline_80_layers_s": step_s * 80, "gemm_variant": args.block_variant or "mxs_mixed_gemm"},
         "gemm_ops_per_step": gemm_ops,
         "stages": stage_summary(stages),
         "roofline": roofline_of(dominant, stages[dominant]),
-        "roofline_gemm": roofline_of("mixed_gemm", stages["mixed_gemm"]),
+        "roofline_gemm": roofline_of("mixed_gemm", stages["mixed_gemm"], prepared=args.block_variant == "prepared"),
         "roofline_calibrate": roofline_of("calibrate", stages["calibrate"]),
     }
     if not args.no_extras:
@@ -1001,6 +1001,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="70B block step only (no variants, no q_proj / MLP / decode keys)")
     ap.add_argument("--workload", choices=("70b_block", "q_proj"), default="70b_block")
+    ap.add_argument("--block-variant", choices=("mx", "fused", "prepared"), default=None,
+                    help="run the block step's timed steps with this GEMM variant (for profiling it; "
+                         "the headline is the default step)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--overhead", action="store_true")
