@@ -13,7 +13,7 @@
 // whose partial counts are added with integer atomics (order-independent). The
 // perm output buffer holds the ranks until the last kernel overwrites it.
 // (A one-workgroup bitonic sort in LDS measured 54 us at K = 4096, against
-// 16 us for these three launches.)
+// 15 us for these three launches; 23 us at K = 8192, 97 us at K = 28672.)
 #include "mxs_device.h"
 #include "mxs_internal.h"
 
@@ -22,7 +22,6 @@ namespace mxs {
 namespace {
 
 constexpr int kRankThreads = 256;
-constexpr int kRankPer = 1;        // columns k per thread
 constexpr int kRankMaxSlice = 4096;
 constexpr int kScanThreads = 1024;
 constexpr int64_t kPermLdsMaxK = 32768;   // ranks staged in LDS by the fused class+perm kernel
@@ -32,31 +31,65 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t n, int32_t
     if (i < n) p[i] = v;
 }
 
-// Workgroup (x, y): columns k in [x * 1024, x * 1024 + 1024) (4 per thread,
-// strided by 256) against keys j in slice y; partial counts are added with
-// integer atomics, so the result does not depend on the order.
+// Workgroup (x, y): columns k in [x * 256 PER, (x + 1) * 256 PER) (PER per
+// thread, strided by 256) against keys j in slice y, staged in LDS. Each LDS
+// read (two keys) serves the thread's PER columns, so with PER = 4 the loop
+// issues one LDS instruction per eight comparisons. A slice wholly before or
+// after the workgroup's columns decides ties the same way for all of them;
+// only a slice that overlaps them compares indices. Partial counts are added
+// with integer atomics, so the result does not depend on the order.
+template <int kRankPer>
 __global__ __launch_bounds__(kRankThreads) void k_rank(const double *__restrict__ score, int64_t K,
                                                        int32_t slice, int32_t *__restrict__ rank) {
-    __shared__ uint64_t keys[kRankMaxSlice];
+    __shared__ __attribute__((aligned(16))) uint64_t keys[kRankMaxSlice];
     const int64_t j0 = (int64_t)blockIdx.y * slice;
     const int jn = (int)(K - j0 < slice ? K - j0 : slice);
     for (int t = threadIdx.x; t < jn; t += kRankThreads) keys[t] = order_key(score[j0 + t]);
     __syncthreads();
-    const int64_t kbase = (int64_t)blockIdx.x * (kRankThreads * kRankPer) + threadIdx.x;
+    const int64_t kb0 = (int64_t)blockIdx.x * (kRankThreads * kRankPer);
+    uint64_t kk[kRankPer];
+    int32_t cnt[kRankPer];
 #pragma unroll
     for (int u = 0; u < kRankPer; ++u) {
-        const int64_t k = kbase + u * kRankThreads;
-        if (k >= K) break;
-        const uint64_t kk = order_key(score[k]);
-        int32_t cnt = 0;
-        if (j0 + jn <= k) {            // every j of the slice precedes k: ties count
-            for (int t = 0; t < jn; ++t) cnt += keys[t] >= kk;
-        } else if (j0 > k) {           // every j follows k: ties do not count
-            for (int t = 0; t < jn; ++t) cnt += keys[t] > kk;
-        } else {
-            for (int t = 0; t < jn; ++t) cnt += (keys[t] > kk) || (keys[t] == kk && j0 + t < k);
+        const int64_t k = kb0 + threadIdx.x + u * kRankThreads;
+        kk[u] = k < K ? order_key(score[k]) : 0;
+        cnt[u] = 0;
+    }
+    const int np = jn >> 1;
+    if (j0 + jn <= kb0) {                                   // every j precedes every k: ties count
+        for (int t = 0; t < np; ++t) {
+            const uint64_t a = keys[2 * t], b = keys[2 * t + 1];
+#pragma unroll
+            for (int u = 0; u < kRankPer; ++u) cnt[u] += (int32_t)(a >= kk[u]) + (int32_t)(b >= kk[u]);
         }
-            if (cnt) atomicAdd(rank + k, cnt);
+        if (jn & 1) {
+#pragma unroll
+            for (int u = 0; u < kRankPer; ++u) cnt[u] += keys[jn - 1] >= kk[u];
+        }
+    } else if (j0 >= kb0 + kRankThreads * kRankPer) {       // every j follows every k: ties do not count
+        for (int t = 0; t < np; ++t) {
+            const uint64_t a = keys[2 * t], b = keys[2 * t + 1];
+#pragma unroll
+            for (int u = 0; u < kRankPer; ++u) cnt[u] += (int32_t)(a > kk[u]) + (int32_t)(b > kk[u]);
+        }
+        if (jn & 1) {
+#pragma unroll
+            for (int u = 0; u < kRankPer; ++u) cnt[u] += keys[jn - 1] > kk[u];
+        }
+    } else {
+        for (int t = 0; t < jn; ++t) {
+            const uint64_t a = keys[t];
+#pragma unroll
+            for (int u = 0; u < kRankPer; ++u) {
+                const int64_t k = kb0 + threadIdx.x + u * kRankThreads;
+                cnt[u] += (a > kk[u]) || (a == kk[u] && j0 + t < k);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kRankPer; ++u) {
+        const int64_t k = kb0 + threadIdx.x + u * kRankThreads;
+        if (k < K && cnt[u]) atomicAdd(rank + k, cnt[u]);
     }
 }
 
@@ -153,12 +186,24 @@ hipError_t launch_allocate(const double *score, int64_t K, int32_t c8, int32_t c
     hipLaunchKernelGGL(k_fill_i32, dim3(gk), dim3(256), 0, st, perm, K, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // slices small enough for ~1000+ workgroups, large enough to bound the atomics
-    const int64_t colblocks = ceil_div(K, kRankThreads * kRankPer);
-    int64_t slice = K * colblocks / 1024;
-    slice = slice < 64 ? 64 : (slice > kRankMaxSlice ? kRankMaxSlice : slice);
-    hipLaunchKernelGGL(k_rank, dim3((unsigned)colblocks, (unsigned)ceil_div(K, slice)), dim3(kRankThreads), 0, st,
-                       score, K, (int32_t)slice, perm);
+    // Up to K = 4096 one column per thread (more threads, the latency of a
+    // short launch dominates); above, four per thread and slices sized for
+    // ~4096 workgroups (measured at K = 28672: 96 us against 261 us for one
+    // column per thread and ~1000 workgroups; the atomics grow with the
+    // number of slices, K per slice)
+    if (K <= 4096) {
+        const int64_t colblocks = ceil_div(K, kRankThreads);
+        int64_t slice = K * colblocks / 1024;
+        slice = slice < 64 ? 64 : (slice > kRankMaxSlice ? kRankMaxSlice : slice);
+        hipLaunchKernelGGL((k_rank<1>), dim3((unsigned)colblocks, (unsigned)ceil_div(K, slice)), dim3(kRankThreads),
+                           0, st, score, K, (int32_t)slice, perm);
+    } else {
+        const int64_t colblocks = ceil_div(K, kRankThreads * 4);
+        int64_t slice = K * colblocks / 4096;
+        slice = slice < 64 ? 64 : (slice > kRankMaxSlice ? kRankMaxSlice : slice);
+        hipLaunchKernelGGL((k_rank<4>), dim3((unsigned)colblocks, (unsigned)ceil_div(K, slice)), dim3(kRankThreads),
+                           0, st, score, K, (int32_t)slice, perm);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (K <= kPermLdsMaxK) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_class_perm),
