@@ -1,18 +1,22 @@
 """GPU parity for the Llama-2-70B-shaped pipeline at full size, through the C ABI.
 
-Every linear layer of one 70B block (q 8192x8192, k and v 1024x8192,
-o 8192x8192, gate and up 28672x8192, down 8192x28672) runs the whole path:
+Every linear layer of three of the 80 70B blocks (layers 0, 39 and 79; q
+8192x8192, k and v 1024x8192, o 8192x8192, gate and up 28672x8192, down
+8192x28672) runs the whole path:
 calibrate over 128 x 2048 synthetic tokens of its input (one call, 1024 row
 chunks), score, allocate (5/15/80 % 8/6/4-bit), quantize W and X, then the
-product at M = 2048 prefill tokens through all three GEMM entry points
-(mxs_mixed_gemm, mxs_mixed_gemm_mx, mxs_mixed_gemm_fused).
+product at M = 2048 prefill tokens through every GEMM entry point
+(mxs_mixed_gemm, mxs_mixed_gemm_mx, mxs_mixed_gemm_fused and, with W prepared
+once, mxs_mixed_gemm_prepared). Seeds: input i of block l draws from
+5000 + 16 (4 l + i), weight j (q, k, v, o, gate, up, down) from
+5500 + 16 (7 l + j); block 0 is the benchmarked block.
 
 Bar: Hdiag of every column, the scores, the bit map, the permutation and all
 weight planes bit for bit against the oracle; activation planes on the
 sampled rows bit for bit; Y componentwise within 1e-5 of the fp64 definition
 on one sampled token per 64-row group and one sampled output column per
 64-column group (every wave tile of every workgroup tile is hit); the fused
-entry bit-identical to quantize + mxs_mixed_gemm. The oracle computes Hdiag
+entry and the prepared entry bit-identical to quantize + mxs_mixed_gemm. The oracle computes Hdiag
 column slice by column slice (the canonical order runs down each column, so
 the slices give the full result).
 """
@@ -43,16 +47,23 @@ def calib():
     return {}
 
 
-def input_seed(inp):
-    return 5000 + 16 * inp
+BLOCKS = (0, 39, 79)
 
 
-def hdiag_of_input(mx, orc, cache, inp, K):
+def input_seed(block, inp):
+    return 5000 + 16 * (4 * block + inp)
+
+
+def weight_seed(block, li):
+    return 5500 + 16 * (7 * block + li)
+
+
+def hdiag_of_input(mx, orc, cache, block, inp, K):
     """GPU and oracle Hdiag of one layer input over 128 x 2048 tokens, compared
     in full; cached per input (q/k/v and gate/up share theirs)."""
-    if inp in cache:
-        return cache[inp]
-    seed = input_seed(inp)
+    if (block, inp) in cache:
+        return cache[(block, inp)]
+    seed = input_seed(block, inp)
     gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
     Xc = synth.activations(C5["calib_rows"], K, seed + synth.ROLE_CALIB, gains, device=DEV)
     h = mx.mxs_calibrate(Xc)
@@ -65,9 +76,10 @@ def hdiag_of_input(mx, orc, cache, inp, K):
     del Xc
     torch.cuda.empty_cache()
     bad = np.flatnonzero(h.cpu().numpy() != h_ref)
-    assert bad.size == 0, f"Hdiag input {inp}: {bad.size} columns differ, first {bad[:5].tolist()}"
-    cache[inp] = (h, h_ref, gains)
-    return cache[inp]
+    assert bad.size == 0, f"Hdiag block {block} input {inp}: {bad.size} columns differ, first {bad[:5].tolist()}"
+    cache.clear()                          # one block's inputs at a time
+    cache[(block, inp)] = (h, h_ref, gains)
+    return cache[(block, inp)]
 
 
 def per_group_sample(n, group, gen):
@@ -94,16 +106,17 @@ def assert_gemm(Y, Yref, Yabs, what):
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
-def test_70b_block_layer(mx, orc, calib, name):
+@pytest.mark.parametrize("block", BLOCKS)
+def test_70b_block_layer(mx, orc, calib, block, name):
     lay = LAYERS[name]
     N, K, M = lay["N"], lay["K"], C5["M"]
     bp8, bp6 = C5["budget"]
     li = list(LAYERS).index(name)
     inp = INPUT_OF[name]
-    print(f"70B {name}: N={N} K={K} M={M}", flush=True)
-    h, h_ref, gains = hdiag_of_input(mx, orc, calib, inp, K)
+    print(f"70B block {block} {name}: N={N} K={K} M={M}", flush=True)
+    h, h_ref, gains = hdiag_of_input(mx, orc, calib, block, inp, K)
 
-    W = synth.weights(N, K, 5500 + 16 * li + synth.ROLE_W, device=DEV)
+    W = synth.weights(N, K, weight_seed(block, li) + synth.ROLE_W, device=DEV)
     s = mx.mxs_score(W, h)
     Wh = W.float().cpu().numpy()
     s_ref = orc.score(Wh, h_ref)
@@ -120,9 +133,9 @@ def test_70b_block_layer(mx, orc, calib, name):
     assert_planes(B, B_ref, what="W planes")
     del Wh
 
-    X = synth.activations(M, K, input_seed(inp) + synth.ROLE_X, gains, device=DEV)
+    X = synth.activations(M, K, input_seed(block, inp) + synth.ROLE_X, gains, device=DEV)
     A = mx.mxs_quantize(X, perm, n8, n6, n4)
-    g = torch.Generator(device="cpu").manual_seed(5500 + li)
+    g = torch.Generator(device="cpu").manual_seed(weight_seed(block, li))
     rows = per_group_sample(M, 64, g)
     cols = per_group_sample(N, 64, g)
     A_ref = orc.quantize(X[torch.as_tensor(rows, device=DEV)].float().cpu().numpy(), p_ref, n8, n6, n4)
@@ -137,7 +150,10 @@ def test_70b_block_layer(mx, orc, calib, name):
     del Yx
     Yf = mx.mxs_mixed_gemm_fused(X, perm, B)
     assert torch.equal(Yf.view(torch.int32), Y.view(torch.int32)), f"{name}: fused differs from quantize + GEMM"
-    del Y, Yf, A, B, W, X
+    wp = mx.mxs_prepare_weights(B)
+    Yp = mx.mxs_mixed_gemm_prepared(A, B, wp)
+    assert torch.equal(Yp.view(torch.int32), Y.view(torch.int32)), f"{name}: prepared differs from mixed_gemm"
+    del Y, Yf, Yp, wp, A, B, W, X
     torch.cuda.empty_cache()
 
 
