@@ -126,16 +126,19 @@ __global__ __launch_bounds__(256) void k_quant_gather_lds(const T *__restrict__ 
 // The same LDS-staged gather with rows streamed ahead: each thread holds
 // its PPT 16-byte pieces of the next DEPTH rows in a register ring, so a
 // row's HBM latency overlaps the gathers and stores of the rows before it.
-// Requires 16-byte aligned rows.
-template <typename T, int PPT, int DEPTH>
+// Requires 16-byte aligned rows. PG: the permutation is read from global
+// memory (L2) per group instead of being staged in LDS, so that long rows
+// (only the row in LDS) still fit two workgroups per CU; requires a 16-byte
+// aligned permutation.
+template <typename T, int PPT, int DEPTH, bool PG>
 __global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X, int64_t R, int64_t ldx,
                                                          const int32_t *__restrict__ perm, Planes P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int64_t K = P.K;
     uint16_t *sperm = reinterpret_cast<uint16_t *>(lds);
-    u32x4 *srow = reinterpret_cast<u32x4 *>(lds + ((2 * K + 15) / 16) * 16);
+    u32x4 *srow = reinterpret_cast<u32x4 *>(lds + (PG ? 0 : ((2 * K + 15) / 16) * 16));
     const int tid = threadIdx.x;
-    stage_perm(perm, K, sperm, tid);
+    if (!PG) stage_perm(perm, K, sperm, tid);
     const int nvec = (int)(K * (int64_t)sizeof(T) / 16);
     const int64_t G = gridDim.x;
     u32x4 ring[DEPTH][PPT];
@@ -161,13 +164,22 @@ __global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X
             lds_barrier();
             if (row + DEPTH * G < R) fetch(ring[d], row + DEPTH * G);
             for (int64_t cg = tid; cg * 8 < K; cg += 256) {   // whole quads stay together
-                const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + cg * 8);
-                const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
                 float v[8];
+                if (PG) {
+                    const uint32_t kmax = (uint32_t)K - 1u;
+                    const uint4 a = reinterpret_cast<const uint4 *>(perm + cg * 8)[0];
+                    const uint4 b = reinterpret_cast<const uint4 *>(perm + cg * 8)[1];
+                    const uint32_t j[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[2 * i] = load1<T>(s + (w[i] & 0xFFFFu));
-                    v[2 * i + 1] = load1<T>(s + (w[i] >> 16));
+                    for (int i = 0; i < 8; ++i) v[i] = load1<T>(s + (j[i] < kmax ? j[i] : kmax));
+                } else {
+                    const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + cg * 8);
+                    const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = load1<T>(s + (w[i] & 0xFFFFu));
+                        v[2 * i + 1] = load1<T>(s + (w[i] >> 16));
+                    }
                 }
                 emit(P, row, cg >> 2, (int)(cg & 3), v);
             }
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X
 // gathering every element from global memory.
 constexpr int64_t kStageLdsLong = 144 * 1024;
 
-template <typename T, int PPT>
+template <typename T, int PPT, bool PG>
 hipError_t launch_gather_pf(const T *X, int64_t ldx, const int32_t *perm, const Planes &P, int64_t R,
                             int64_t lds_bytes, hipStream_t st) {
     // The gathers, quantisation and packing of a row are the larger cost, so
@@ -190,13 +202,13 @@ hipError_t launch_gather_pf(const T *X, int64_t ldx, const int32_t *perm, const 
     // CU), each streaming its rows two ahead. (512 workgroups four rows deep
     // measured 24 % slower for 4096 x 4096.)
     constexpr int DEPTH = 2;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_pf<T, PPT, DEPTH>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_gather_pf<T, PPT, DEPTH, PG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStageLdsLong);
     if (e != hipSuccess) return e;
     const int64_t per_cu = (160 * 1024) / lds_bytes;
     int64_t blocks = 256 * (per_cu < 8 ? (per_cu < 1 ? 1 : per_cu) : 8);
     blocks = blocks < R ? blocks : R;
-    hipLaunchKernelGGL((k_quant_gather_pf<T, PPT, DEPTH>), dim3((unsigned)blocks), dim3(256), (size_t)lds_bytes, st,
+    hipLaunchKernelGGL((k_quant_gather_pf<T, PPT, DEPTH, PG>), dim3((unsigned)blocks), dim3(256), (size_t)lds_bytes, st,
                        X, R, ldx, perm, P);
     return hipGetLastError();
 }
@@ -217,12 +229,21 @@ hipError_t run_quantize(const T *X, int64_t ldx, const int32_t *perm, const Plan
     const int64_t lds_bytes = ((2 * P.K + 15) / 16) * 16 + P.K * (int64_t)sizeof(T);
     const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
     const int64_t ppt = ceil_div(P.K * (int64_t)sizeof(T) / 16, 256);
+    // rows so long that the permutation and the row leave room for one
+    // workgroup per CU: the permutation is read from L2 instead, and the
+    // row alone fits two
+    const int64_t row_bytes = P.K * (int64_t)sizeof(T);
+    if (vec && P.K <= 65536 && ppt <= 16 && 2 * lds_bytes > 160 * 1024 && 2 * row_bytes <= 160 * 1024 &&
+        reinterpret_cast<uintptr_t>(perm) % 16 == 0) {
+        if (ppt <= 8) return launch_gather_pf<T, 8, true>(X, ldx, perm, P, R, row_bytes, st);
+        return launch_gather_pf<T, 16, true>(X, ldx, perm, P, R, row_bytes, st);
+    }
     if (vec && lds_bytes <= kStageLdsLong && P.K <= 65536 && ppt <= 16) {
-        if (ppt <= 1) return launch_gather_pf<T, 1>(X, ldx, perm, P, R, lds_bytes, st);
-        if (ppt <= 2) return launch_gather_pf<T, 2>(X, ldx, perm, P, R, lds_bytes, st);
-        if (ppt <= 4) return launch_gather_pf<T, 4>(X, ldx, perm, P, R, lds_bytes, st);
-        if (ppt <= 8) return launch_gather_pf<T, 8>(X, ldx, perm, P, R, lds_bytes, st);
-        return launch_gather_pf<T, 16>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 1) return launch_gather_pf<T, 1, false>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 2) return launch_gather_pf<T, 2, false>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 4) return launch_gather_pf<T, 4, false>(X, ldx, perm, P, R, lds_bytes, st);
+        if (ppt <= 8) return launch_gather_pf<T, 8, false>(X, ldx, perm, P, R, lds_bytes, st);
+        return launch_gather_pf<T, 16, false>(X, ldx, perm, P, R, lds_bytes, st);
     }
     if (lds_bytes <= kStageLds && P.K <= 65536) {
         int64_t blocks = R < 512 ? R : 512;   // each workgroup stages the permutation once

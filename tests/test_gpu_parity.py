@@ -72,6 +72,25 @@ def test_quantize_identity_and_perm(mx, orc, dtype, R, K, budget):
         assert_planes(Q, R_, f"R={R} K={K} perm={p is not None}")
 
 
+@pytest.mark.parametrize("dtype,R,K", [(torch.bfloat16, 37, 28672), (torch.float32, 21, 16384),
+                                       (torch.bfloat16, 300, 14336)])
+def test_quantize_long_rows(mx, orc, dtype, R, K):
+    # rows whose row and permutation do not fit twice in a CU's LDS read the
+    # permutation from global memory (a second, unaligned view of the same
+    # permutation takes the LDS-staged path); both must match the oracle
+    gains = synth.outlier_gains(K, 31, max(1, K // 1000), max(2, K // 100))
+    X = synth.activations(R, K, 32, gains, dtype=dtype, device=DEV)
+    n8, n6, n4 = mx.mxs_budget_blocks(K, 800, 2000)
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(K)).to(torch.int32).to(DEV)
+    buf = torch.empty(K + 1, dtype=torch.int32, device=DEV)
+    buf[1:] = perm
+    Xh = host(X)
+    ref = orc.quantize(Xh, perm.cpu().numpy(), n8, n6, n4)
+    for p in (perm, buf[1:]):
+        Q = mx.mxs_quantize(X, p, n8, n6, n4)
+        assert_planes(Q, ref, f"R={R} K={K} {dtype} perm offset {p.data_ptr() % 16}")
+
+
 def test_quantize_edge_values(mx, orc):
     # zeros, subnormals, exponent clamp, huge values, NaN/Inf blocks, ties
     K = 256
