@@ -183,33 +183,40 @@ __device__ __forceinline__ int sext(uint32_t v, int bits) {
     return (int)(v << (32 - bits)) >> (32 - bits);
 }
 
-// codes c[0..31] of block `b` (global block index) of row r
-__device__ __forceinline__ void unpack_block(const QView &Q, int64_t r, int64_t b, int cls,
-                                             int32_t n8, int32_t n6, int c[32]) {
+// The packed bytes of one row's block (8, 6 or 4 bits: 32, 24 or 16 bytes)
+// as little-endian words, and their codes; split so that a thread can issue
+// the loads of several rows before it unpacks any of them.
+__device__ __forceinline__ void load_block_raw(const QView &Q, int64_t r, int64_t b, int cls, int32_t n8,
+                                               int32_t n6, uint32_t w[8]) {
     if (cls == 8) {
         const uint4 *p = reinterpret_cast<const uint4 *>(Q.q8 + r * Q.ld8 + 32 * b);
         const uint4 x = p[0], y = p[1];
-        const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w; w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+    } else if (cls == 6) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(Q.q6 + r * Q.ld6 + 24 * (b - n8));
+#pragma unroll
+        for (int i = 0; i < 6; ++i) w[i] = p[i];
+        w[6] = 0; w[7] = 0;
+    } else {
+        const uint2 *p = reinterpret_cast<const uint2 *>(Q.q4 + r * Q.ld4 + 16 * (b - n8 - n6));
+        const uint2 x = p[0], y = p[1];
+        w[0] = x.x; w[1] = x.y; w[2] = y.x; w[3] = y.y; w[4] = 0; w[5] = 0; w[6] = 0; w[7] = 0;
+    }
+}
+
+__device__ __forceinline__ void unpack_raw(const uint32_t w[8], int cls, int c[32]) {
+    if (cls == 8) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 2] >> (8 * (i & 3))) & 255u, 8);
     } else if (cls == 6) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(Q.q6 + r * Q.ld6 + 24 * (b - n8));
-        uint32_t w[7];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) w[i] = p[i];
-        w[6] = 0;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
-            // 24-bit group g starts at bit 24 g of the 192-bit little-endian stream
             const int bit = 24 * g;
             const uint32_t grp = __builtin_amdgcn_alignbit(w[(bit >> 5) + 1], w[bit >> 5], bit & 31);
 #pragma unroll
             for (int j = 0; j < 4; ++j) c[4 * g + j] = sext((grp >> (6 * j)) & 63u, 6);
         }
     } else {
-        const uint2 *p = reinterpret_cast<const uint2 *>(Q.q4 + r * Q.ld4 + 16 * (b - n8 - n6));
-        const uint2 x = p[0], y = p[1];
-        const uint32_t w[4] = {x.x, x.y, y.x, y.y};
 #pragma unroll
         for (int i = 0; i < 32; ++i) c[i] = sext((w[i >> 3] >> (4 * (i & 7))) & 15u, 4);
     }
@@ -263,12 +270,15 @@ __host__ __device__ inline Segs make_segs(int32_t n8, int32_t n6, int32_t n4) {
 
 // One workgroup prepares a 64-row x (one window) tile of one matrix: thread t
 // takes block t % 16 of the window for rows t / 16 + 16 i (reads and code
-// writes run along the row), the window reduction is a 16-lane butterfly, and
-// the scales are transposed through LDS to be written 64 rows at a time.
+// writes run along the row); it issues the loads of its four rows before it
+// unpacks the first. The window reduction is a 16-lane butterfly, and the
+// scales are transposed through LDS (rows padded to 68 floats, so the 64
+// lanes of a store hit 64 distinct banks) to be written 64 rows at a time.
 // Prepared rows are padded to a multiple of 16 blocks with zero codes.
+constexpr int kPrepCsPitch = 68;
 __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64_t ntiles_a, int64_t K,
                                                    int64_t Kp, Segs S) {
-    __shared__ float s_cs[kG][64];
+    __shared__ __attribute__((aligned(16))) float s_cs[kG][kPrepCsPitch];
     const bool is_a = blockIdx.x < ntiles_a;
     const PrepJob &J = is_a ? ja : jw;
     const int64_t tile = is_a ? blockIdx.x : blockIdx.x - ntiles_a;
@@ -288,7 +298,16 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
     }
     const int cls = S.cls[sg], F = S.F[sg];
     const bool in_range = b < nbp;
-#pragma unroll 1
+    uint32_t raw[4][8], sbyte[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = rt * 64 + (tid >> 4) + 16 * i;
+        if (real_blk && r < J.R) {
+            load_block_raw(J.Q, r, b, cls, S.hi[0], S.hi[1] - S.hi[0], raw[i]);
+            sbyte[i] = J.Q.sc[r * J.Q.lds + b];
+        }
+    }
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int lr = (tid >> 4) + 16 * i;
         const int64_t r = rt * 64 + lr;
@@ -297,8 +316,8 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
         int s = 0;
         bool bad = false, nz = false;
         if (real) {
-            unpack_block(J.Q, r, b, cls, S.hi[0], S.hi[1] - S.hi[0], c);
-            const uint32_t byte = J.Q.sc[r * J.Q.lds + b];
+            unpack_raw(raw[i], cls, c);
+            const uint32_t byte = sbyte[i];
             bad = byte == 0xFFu;
             s = (int)byte - 127;
 #pragma unroll
