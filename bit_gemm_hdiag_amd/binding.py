@@ -292,7 +292,7 @@ def mxs_mixed_gemm(A: QMat, W: QMat, Y: torch.Tensor | None = None, ws=None) -> 
 
 
 # bytes of the device scratch array behind mxs_mixed_gemm_noalloc (per GPU)
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 def mxs_mixed_gemm_noalloc(A: QMat, W: QMat, Y: torch.Tensor) -> torch.Tensor:

@@ -156,26 +156,42 @@ QView view_of(const mxs_qmat &q) {
 // Prefill path (M >= kPrefillMinRows): operand preparation + grouped GEMM.
 //
 // The per-block epilogue above costs 3 VALU operations per output and block,
-// six times the MFMA time of the block. The prefill path removes it by exact
-// exponent alignment over groups = aligned windows of kG consecutive blocks.
-// If a window lies inside one width class and a row's nonzero blocks in it
-// have scale exponents within F of each other (F = 4, 2, 0 for 4-, 6-, 8-bit
-// codes: the headroom an int8 byte has over the code), code c of block b is
-// stored as c << (s_b - base) with base = max s_b - F; aligned A and W rows
-// make the int32 MFMA sum over the window exact, times 2^(base_a + base_w):
-// one epilogue per window. Other rows keep c << F with scale 2^(s_b - F) and
-// the wave takes one epilogue per block for that window. Window sums stay
-// below 2^24 (16 * 32 * 127^2), so the int32 -> fp32 conversion is exact and
-// only the fp32 accumulation across windows rounds.
+// six times the MFMA time of the block. The prefill path removes it in two
+// ways, both exact.
 //
-// Prepared operand (workspace), per matrix with R rows padded to Rp and K
-// padded to Kp = whole windows:
-//   codes int8 [Rp, Kp]   shifted codes, natural k order inside each block;
-//                         W row-major, A (activations) in fragment order
-//                         (afrag_off: 1 KiB per 32 rows and block)
-//   cs    f32  [nbp, Rp]  code scale of (row, block); negative when the
-//                         row's window is not aligned; -Inf for a NaN/Inf block
-// Padding rows and blocks hold zero codes and scale +1.
+// Narrow blocks (4-bit codes): exponent alignment over windows of kG
+// consecutive blocks. If a row's nonzero blocks in a window have scale
+// exponents within F = 4 of each other (the headroom an int8 byte has over a
+// 4-bit code), code c of block b is stored as c << (s_b - base) with base =
+// max s_b - F; aligned A and W rows make the int32 MFMA sum over the window
+// exact, times 2^(base_a + base_w): one epilogue per window. Other rows keep
+// c << F with scale 2^(s_b - F) and the wave takes one epilogue per block for
+// that window. Window sums stay below 2^24 (16 * 32 * 127^2), so the int32 ->
+// fp32 conversion is exact and only the fp32 accumulation across windows
+// rounds.
+//
+// Wide blocks (the 8- and 6-bit classes, whose codes leave an int8 byte no or
+// two bits of headroom, so their windows practically never align): each
+// element is stored as the bf16 value c * 2^s, which is exact (|c| <= 127 has
+// at most 7 significant bits, bf16 keeps 8, and its exponent range is fp32's),
+// and the bf16 matrix cores (v_mfma_f32_32x32x16_bf16) accumulate the exact
+// products straight into the fp32 sums: no epilogue at all. The wide run is
+// rounded up to a multiple of five blocks with the first 4-bit blocks (also
+// exact in bf16), so that the GEMM's five-slot stage ring leaves the wide
+// loop at slot 0; all blocks are wide when fewer 4-bit blocks remain.
+//
+// Prepared operand (workspace), per matrix with R rows padded to Rp; a row is
+// a sequence of 32-byte units: units 2b and 2b + 1 hold wide block b < hw
+// (bf16 elements 0..15 and 16..31), unit b + hw holds narrow block b >= hw,
+// and the row is padded with zero units to Kp bytes (a multiple of 128):
+//   codes [Rp, Kp]        W row-major, A (activations) in fragment order
+//                         (afrag_off: 1 KiB per 32 rows and unit)
+//   cs    f32 [Kp/32, Rp] narrow units: code scale of (row, block), negative
+//                         when the row's window is not aligned, -Inf for a
+//                         NaN/Inf block; wide units: 1 (never read)
+// Padding rows hold zero units; padding units zero codes and scale +1. A
+// NaN/Inf wide block is stored as bf16 NaN (the product is NaN for its whole
+// row or column, as the definition gives).
 constexpr int kG = 16;              // blocks per alignment window
 constexpr int kPrefillMinRows = 64; // smaller M uses the per-block kernel
 
@@ -244,60 +260,77 @@ __host__ __device__ inline int64_t afrag_off(int64_t row, int64_t b, int h, int6
     return (((row >> 5) * nbp + b) << 10) + ((int64_t)h << 9) + ((row & 31) << 4);
 }
 
-// Windows start at the first block of each width class: window j of class
-// segment [lo, hi) covers blocks lo + kG j .. min(hi, lo + kG (j + 1)) - 1.
+// Four segments of blocks: 8-bit, 6-bit and 4-bit wide blocks, then the
+// narrow 4-bit blocks. The preparation works in windows that start at the
+// first block of each segment: window j of segment [lo, hi) covers blocks
+// lo + kG j .. min(hi, lo + kG (j + 1)) - 1; only the narrow segment's
+// windows are alignment windows.
+constexpr int kWideStep = 5;   // the wide run is a multiple of this many blocks
 struct Segs {
-    int32_t lo[3], hi[3], F[3], cls[3];
-    int32_t win_base[4];   // prefix count of windows per segment
+    int32_t lo[4], hi[4], cls[4];
+    int32_t win_base[5];   // prefix count of windows per segment
+    int32_t hw;            // wide blocks (units 0 .. 2 hw - 1)
+    int32_t nq;            // units of a row before padding: 2 hw + (nb - hw)
 };
 
 __host__ __device__ inline Segs make_segs(int32_t n8, int32_t n6, int32_t n4) {
     Segs S;
-    const int32_t n[3] = {n8, n6, n4};
+    const int32_t nb = n8 + n6 + n4, h1 = n8 + n6;
+    const int32_t up = (h1 + kWideStep - 1) / kWideStep * kWideStep;
+    S.hw = up < nb ? up : nb;
+    S.nq = nb + S.hw;
+    const int32_t n[4] = {n8, n6, S.hw - h1, nb - S.hw};
     int32_t lo = 0, wb = 0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
         S.lo[i] = lo;
         S.hi[i] = lo + n[i];
-        S.F[i] = i == 0 ? 0 : (i == 1 ? 2 : 4);
         S.cls[i] = i == 0 ? 8 : (i == 1 ? 6 : 4);
         S.win_base[i] = wb;
         wb += (n[i] + kG - 1) / kG;
         lo += n[i];
     }
-    S.win_base[3] = wb;
+    S.win_base[4] = wb;
     return S;
+}
+
+// bf16 bits of c * 2^s for an integer code |c| <= 127 (exact: see above)
+__device__ __forceinline__ uint32_t bf16_of_code(int c, int s) {
+    return __float_as_uint(__builtin_ldexpf((float)c, s)) >> 16;
 }
 
 // One workgroup prepares a 64-row x (one window) tile of one matrix: thread t
 // takes block t % 16 of the window for rows t / 16 + 16 i (reads and code
 // writes run along the row); it issues the loads of its four rows before it
-// unpacks the first. The window reduction is a 16-lane butterfly, and the
-// scales are transposed through LDS (rows padded to 68 floats, so the 64
-// lanes of a store hit 64 distinct banks) to be written 64 rows at a time.
-// Prepared rows are padded to a multiple of 16 blocks with zero codes.
+// unpacks the first. A wide window writes bf16 values (64 bytes per row and
+// block). A narrow window reduces its scale exponents with a 16-lane
+// butterfly and transposes the scales through LDS (rows padded to 68 floats,
+// so the 64 lanes of a store hit 64 distinct banks) to write them 64 rows at
+// a time. Padding windows cover units nq .. Kp/32 - 1, 16 per window.
 constexpr int kPrepCsPitch = 68;
-__global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64_t ntiles_a, int64_t K,
-                                                   int64_t Kp, Segs S) {
+__global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64_t ntiles_a, int64_t Kp, Segs S) {
     __shared__ __attribute__((aligned(16))) float s_cs[kG][kPrepCsPitch];
     const bool is_a = blockIdx.x < ntiles_a;
     const PrepJob &J = is_a ? ja : jw;
     const int64_t tile = is_a ? blockIdx.x : blockIdx.x - ntiles_a;
     const int64_t rt = tile % J.tiles_r, win = tile / J.tiles_r;   // win < windows + pad windows
     const int tid = threadIdx.x, blk = tid & 15;
-    const int64_t nb = K / 32, nbp = Kp / 32;
-    int sg = 0;
-    int64_t b;
+    const int64_t nup = Kp / 32;
+    const bool pad = win >= S.win_base[4];
+    int sg = 3;
+    int64_t b, u;   // block (real windows) and unit of this thread's column
     bool real_blk;
-    if (win < S.win_base[3]) {
-        sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : 2);
+    if (!pad) {
+        sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : (win < S.win_base[3] ? 2 : 3));
         b = S.lo[sg] + (win - S.win_base[sg]) * kG + blk;
         real_blk = b < S.hi[sg];
-    } else {   // padding blocks nb .. nbp - 1, 16 per pad window
-        b = nb + (win - S.win_base[3]) * kG + blk;
+        u = sg < 3 ? 2 * b : b + S.hw;
+    } else {
+        b = -1;
+        u = S.nq + (win - S.win_base[4]) * kG + blk;
         real_blk = false;
     }
-    const int cls = S.cls[sg], F = S.F[sg];
-    const bool in_range = b < nbp;
+    const bool wide = !pad && sg < 3;
+    const int cls = S.cls[sg];
     uint32_t raw[4][8], sbyte[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -307,6 +340,47 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
             sbyte[i] = J.Q.sc[r * J.Q.lds + b];
         }
     }
+    if (wide) {   // uniform over the workgroup
+        {   // the units' scale entries (never read) hold 1, so that every byte of the operand is set
+            const int64_t u0 = 2 * (b - blk), uu = u0 + (tid >> 3);
+            if (uu < 2 * (int64_t)S.hi[sg]) {
+                float4 *dst = reinterpret_cast<float4 *>(J.cs + uu * J.Rp + rt * 64 + 8 * (tid & 7));
+                dst[0] = make_float4(1.f, 1.f, 1.f, 1.f);
+                dst[1] = make_float4(1.f, 1.f, 1.f, 1.f);
+            }
+        }
+        if (!real_blk) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = rt * 64 + (tid >> 4) + 16 * i;
+            uint32_t w[16];
+            if (r < J.R) {
+                int c[32];
+                unpack_raw(raw[i], cls, c);
+                const uint32_t byte = sbyte[i];
+                const int s = (int)byte - 127;
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    w[k] = byte == 0xFFu ? 0x7FC07FC0u : (bf16_of_code(c[2 * k], s) | (bf16_of_code(c[2 * k + 1], s) << 16));
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) w[k] = 0;
+            }
+            if (J.frag) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)   // elements 8q .. 8q + 7: unit u + q / 2, k-half q % 2
+                    *reinterpret_cast<uint4 *>(J.codes + afrag_off(r, u + (q >> 1), q & 1, nup)) =
+                        make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+            } else {
+                uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * u);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+            }
+        }
+        return;
+    }
+    constexpr int F = 4;   // narrow blocks: 4-bit codes in int8 bytes
+    const bool in_range = u < nup;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int lr = (tid >> 4) + 16 * i;
@@ -350,13 +424,13 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
             for (int j = 0; j < 4; ++j) v |= (((uint32_t)c[4 * k + j] << shift) & 255u) << (8 * j);
             w[k] = v;
         }
-        if (in_range && (real_blk || b >= nb)) {
+        if (in_range && (real_blk || pad)) {
             if (J.frag) {
-                int8_t *dst = J.codes + afrag_off(r, b, 0, nbp);
+                int8_t *dst = J.codes + afrag_off(r, u, 0, nup);
                 *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
                 *reinterpret_cast<uint4 *>(dst + 512) = make_uint4(w[4], w[5], w[6], w[7]);
             } else {
-                uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * b);
+                uint4 *dst = reinterpret_cast<uint4 *>(J.codes + r * Kp + 32 * u);
                 dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
                 dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
             }
@@ -366,11 +440,11 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
     __syncthreads();
     {
         const int bb = tid >> 4, part = tid & 15;
-        const int64_t ob = b - blk + bb;   // block of this transposed slice
-        const bool ok = win < S.win_base[3] ? ob < S.hi[sg] : ob < nbp;
+        const int64_t ou = u - blk + bb;   // unit of this transposed slice
+        const bool ok = pad ? ou < nup : b - blk + bb < S.hi[3];
         if (ok) {
             const float4 v = *reinterpret_cast<const float4 *>(&s_cs[bb][4 * part]);
-            *reinterpret_cast<float4 *>(J.cs + ob * J.Rp + rt * 64 + 4 * part) = v;
+            *reinterpret_cast<float4 *>(J.cs + ou * J.Rp + rt * 64 + 4 * part) = v;
         }
     }
 }
@@ -382,9 +456,10 @@ __global__ __launch_bounds__(256) void k_gemm_prep(PrepJob ja, PrepJob jw, int64
 // lane (block t / 4 of the window, quarter t % 4) gathers its 8 values,
 // quantizes them at the block's width (the quantizer of mxs_quantize: scale
 // from the quad's largest magnitude, codes rounded half to even and clamped
-// symmetrically), and the window's alignment (16-lane-group reduction of the
-// blocks' scale exponents) shifts the codes exactly as k_gemm_prep does.
-// Rows R .. Rp - 1 and padding blocks get zero codes and scale 1.
+// symmetrically); a wide window stores the codes as bf16 values and a narrow
+// window's alignment (16-lane-group reduction of the blocks' scale exponents)
+// shifts them, exactly as k_gemm_prep does. Rows R .. Rp - 1 get zero units,
+// padding units zero codes and scale 1.
 // Rows are streamed one ahead: each thread holds its PPT 16-byte pieces of
 // the workgroup's next row in registers while the current row is quantized
 // (16-byte aligned rows; others are staged element by element).
@@ -404,8 +479,8 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
     } else {
         for (int64_t j = tid; j < K; j += 256) sperm[j] = (uint16_t)j;
     }
-    const int64_t nb = K / 32, nbp = Kp / 32;
-    const int64_t nwin = S.win_base[3] + (nbp - nb + kG - 1) / kG;
+    const int64_t nup = Kp / 32;
+    const int64_t nwin = S.win_base[4] + (nup - S.nq + kG - 1) / kG;
     const int64_t nvec = K * (int64_t)sizeof(T) / 16;
     const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && (ldx * (int64_t)sizeof(T)) % 16 == 0;
     const int64_t G = gridDim.x;
@@ -441,18 +516,21 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
         __syncthreads();
         fetch(row + G);                        // in flight while this row is quantized
         for (int64_t win = wave; win < nwin; win += 4) {
-            int sg = 0;
-            int64_t b;
+            const bool pad = win >= S.win_base[4];
+            int sg = 3;
+            int64_t b, u;
             bool real_blk;
-            if (win < S.win_base[3]) {
-                sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : 2);
+            if (!pad) {
+                sg = win < S.win_base[1] ? 0 : (win < S.win_base[2] ? 1 : (win < S.win_base[3] ? 2 : 3));
                 b = S.lo[sg] + (win - S.win_base[sg]) * kG + blk;
                 real_blk = b < S.hi[sg];
-            } else {   // padding blocks nb .. nbp - 1
-                b = nb + (win - S.win_base[3]) * kG + blk;
+                u = sg < 3 ? 2 * b : b + S.hw;
+            } else {   // padding units nq .. Kp/32 - 1
+                b = 0;
+                u = S.nq + (win - S.win_base[4]) * kG + blk;
                 real_blk = false;
             }
-            const int cls = S.cls[sg], F = S.F[sg];
+            const int cls = S.cls[sg];
             const bool real = real_blk && real_row;
             float v[8];
             if (real) {
@@ -484,8 +562,24 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
             uint32_t lo = __builtin_amdgcn_perm(cb[1], cb[0], 0x0C0C0400u) | __builtin_amdgcn_perm(cb[3], cb[2], 0x04000C0Cu);
             uint32_t hi = __builtin_amdgcn_perm(cb[5], cb[4], 0x0C0C0400u) | __builtin_amdgcn_perm(cb[7], cb[6], 0x04000C0Cu);
             const bool bad = real && bs.bad;
-            if (bad) lo = hi = 0;
             const int s = (int)bs.byte - 127;
+            if (!pad && sg < 3) {   // wide window (uniform over the wave): bf16 c * 2^s
+                if (real_blk) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c0 = (int)(__uint_as_float(cb[2 * i]) - magic);
+                        const int c1 = (int)(__uint_as_float(cb[2 * i + 1]) - magic);
+                        w[i] = !real ? 0u : (bad ? 0x7FC07FC0u : (bf16_of_code(c0, s) | (bf16_of_code(c1, s) << 16)));
+                    }
+                    *reinterpret_cast<uint4 *>(codes + afrag_off(row, u + (q >> 1), q & 1, nup)) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
+                    if (q < 2) cs[(u + q) * Rp + row] = 1.0f;   // never read
+                }
+                continue;
+            }
+            constexpr int F = 4;
+            if (bad) lo = hi = 0;
             const uint32_t anynz = quad_max_u32((lo | hi) != 0 ? 1u : 0u);   // whole quad, unconditionally
             const bool nz = real && !bad && anynz != 0;
             // window reduction over the 16 blocks (lanes 4 apart), one packed
@@ -515,9 +609,9 @@ __global__ __launch_bounds__(256) void k_quant_prep(const T *__restrict__ X, int
             const uint32_t keep = 0x01010101u * ((0xFFu << shift) & 0xFFu);
             lo = (lo << shift) & keep;
             hi = (hi << shift) & keep;
-            if (b < nbp && (real_blk || b >= nb)) {
-                *reinterpret_cast<uint2 *>(codes + afrag_off(row, b, q >> 1, nbp) + 8 * (q & 1)) = make_uint2(lo, hi);
-                if (q == 0) cs[b * Rp + row] = scale;
+            if (u < nup && (real_blk || pad)) {
+                *reinterpret_cast<uint2 *>(codes + afrag_off(row, u, q >> 1, nup) + 8 * (q & 1)) = make_uint2(lo, hi);
+                if (q == 0) cs[u * Rp + row] = scale;
             }
         }
     }
@@ -564,6 +658,8 @@ constexpr int kDSB = 2;                      // blocks per stage
 constexpr int kDRow = kDSB * 32;             // 64 bytes per row per stage
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // LDS byte address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -636,7 +732,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
     const int nstage = (nb + kDSB - 1) / kDSB;
     const int64_t nbp = Kp / 32;
-    const int h0 = __builtin_amdgcn_readfirstlane(S.hi[0]), h1 = __builtin_amdgcn_readfirstlane(S.hi[1]);
+    const int hw = __builtin_amdgcn_readfirstlane(S.hw);   // wide blocks = wide stages
 
     // DMA roles: W rows 16 wave .. +15; waves 0, 1: A scales of block 0 / 1;
     // wave 2: W scales
@@ -667,7 +763,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
         fbW[j] = rw * kDRow + ((h ^ ((rw >> 2) & 3)) << 4);
     }
 
-    float acc[4][16];
+    v16f acc[4];
     v16i I[4];
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // a zero B operand the compiler cannot see through, for the restart
@@ -728,11 +824,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
                 for (int j = 0; j < 4; ++j) nw[j] = *reinterpret_cast<const v4i *>(sbase + (fbW[j] ^ ((blk + 1) << 5)));
             }
             if (b >= nb) break;
-            const int lo = b >= h1 ? h1 : (b >= h0 ? h0 : 0);
-            const int hi = b >= h1 ? nb : (b >= h0 ? h1 : h0);
-            const int off = b - lo;
+            const int off = b - 2 * hw;   // narrow windows start after the wide units
             const bool first = (off % kG) == 0;
-            const bool last = (off % kG) == kG - 1 || b == hi - 1;
+            const bool last = (off % kG) == kG - 1 || b == nb - 1;
             if (first) {
                 const float va = sCA[blk * kGBM + 32 * wave + l32];
                 const float vw0 = sCW[blk * kGBN + lane], vw1 = sCW[blk * kGBN + 64 + lane];
@@ -753,15 +847,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
         }
     };
 
+    // a wide stage: one wide block (two units) of bf16 values, two bf16 MFMAs
+    // per tile straight into the fp32 sums
+    auto compute_wide = [&](const int8_t *sbase, const v4i (&fa)[kDSB]) {
+        v4i fw[4];
+#pragma unroll
+        for (int u = 0; u < kDSB; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const v4i *>(sbase + (fbW[j] ^ (u << 5)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[u]),
+                                                                 __builtin_bit_cast(v8bf, fw[j]), acc[j], 0, 0, 0);
+        }
+    };
+
     // own loads of stage s done once at most three later stages are in flight
     // (per stage: one W DMA, two A fragments, and a scale DMA on waves 0..2)
-#define MXS_ASTEP(s_, CUR, NXT)                                                               \
+#define MXS_WAIT_ISSUE(s_, NXT)                                                               \
     do {                                                                                      \
-        if ((s_) >= nstage) goto done;                                                        \
         if (has_c) __builtin_amdgcn_s_waitcnt(0x0F70 | 12); /* vmcnt(12) */                   \
         else __builtin_amdgcn_s_waitcnt(0x0F70 | 9);        /* vmcnt(9) */                    \
         lds_barrier();                                                                        \
         a2r_issue<NXT>(D, (s_) + 4, nstage, has_c, ar);                                       \
+    } while (0)
+    // the wide stages 0 .. hw - 1 come first; hw is a multiple of five (the
+    // ring's length) unless every stage is wide, so the narrow loop always
+    // starts at slot 0 (entering it at other slots makes the register
+    // allocator spill)
+#define MXS_WSTEP(s_, CUR, NXT)                                                               \
+    do {                                                                                      \
+        if ((s_) >= hw) goto narrow;                                                          \
+        MXS_WAIT_ISSUE(s_, NXT);                                                              \
+        compute_wide(aslot<CUR>(), ar[CUR]);                                                  \
+    } while (0)
+#define MXS_ASTEP(s_, CUR, NXT)                                                               \
+    do {                                                                                      \
+        if ((s_) >= nstage) goto done;                                                        \
+        MXS_WAIT_ISSUE(s_, NXT);                                                              \
         compute((s_), aslot<CUR>(), ar[CUR]);                                                 \
     } while (0)
 
@@ -769,7 +892,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     a2r_issue<1>(D, 1, nstage, has_c, ar);
     a2r_issue<2>(D, 2, nstage, has_c, ar);
     a2r_issue<3>(D, 3, nstage, has_c, ar);
-    for (int s = 0; s < nstage; s += 5) {
+    for (int s = 0;; s += 5) {
+        MXS_WSTEP(s, 0, 4);
+        MXS_WSTEP(s + 1, 1, 0);
+        MXS_WSTEP(s + 2, 2, 1);
+        MXS_WSTEP(s + 3, 3, 2);
+        MXS_WSTEP(s + 4, 4, 3);
+    }
+narrow:
+    for (int s = hw;; s += 5) {
         MXS_ASTEP(s, 0, 4);
         MXS_ASTEP(s + 1, 1, 0);
         MXS_ASTEP(s + 2, 2, 1);
@@ -778,6 +909,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     }
 done:
 #undef MXS_ASTEP
+#undef MXS_WSTEP
+#undef MXS_WAIT_ISSUE
     if (pend) {
         f32x4_t sa[4];
 #pragma unroll
@@ -1048,7 +1181,6 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const v2i lds_v2i_t;
 __device__ __forceinline__ v2i lds_v2(uint32_t a) { return *reinterpret_cast<lds_v2i_t *>((uintptr_t)a); }
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Workgroup: 8 waves (4 x 2), tile 256 x 128; each wave owns 64 x 64 outputs
 // as 2 x 2 MFMA tiles, i.e. one 64-row A group and one 64-row W group. Both
@@ -1824,11 +1956,11 @@ struct PrepLayout {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-PrepLayout prep_layout(int64_t M, int64_t N, int64_t K) {
+PrepLayout prep_layout(int64_t M, int64_t N, const Segs &S) {
     PrepLayout L;
     L.Mp = ceil_div(M, kGBM) * kGBM;
     L.Np = ceil_div(N, kGBN) * kGBN;
-    L.Kp = ceil_div(K, 128) * 128;   // whole 4-block units (prep pads the tail)
+    L.Kp = ceil_div(32 * (int64_t)S.nq, 128) * 128;   // whole 128-byte pieces (prep pads the tail)
     const int64_t nbp = L.Kp / 32;
     L.a_codes = 0;
     L.a_cs = align256((size_t)L.Mp * L.Kp);
@@ -1840,30 +1972,30 @@ PrepLayout prep_layout(int64_t M, int64_t N, int64_t K) {
     return L;
 }
 
-PrepLayout prep_layout(const mxs_qmat &A, const mxs_qmat &W) { return prep_layout(A.rows, W.rows, A.K); }
+Segs segs_of(const mxs_qmat &Q) { return make_segs(Q.n8, Q.n6, Q.n4); }
 
-int64_t prep_windows(const Segs &S, int64_t K, int64_t Kp) {
-    return S.win_base[3] + ceil_div(Kp / 32 - K / 32, kG);
+int64_t prep_windows(const Segs &S, int64_t Kp) {
+    return S.win_base[4] + ceil_div(Kp / 32 - S.nq, kG);
 }
 
 // W's prepared operand (k_gemm_prep, W job only) into wp
 hipError_t launch_prep_w(const mxs_qmat &W, const PrepLayout &L, const Segs &S, uint8_t *wp, hipStream_t st) {
     PrepJob jw{view_of(W), W.rows, L.Np, reinterpret_cast<int8_t *>(wp + L.w_codes),
                reinterpret_cast<float *>(wp + L.w_cs), L.Np / 64, 0};
-    const int64_t tw = jw.tiles_r * prep_windows(S, W.K, L.Kp);
-    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, W.K, L.Kp, S);
+    const int64_t tw = jw.tiles_r * prep_windows(S, L.Kp);
+    hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)tw), dim3(256), 0, st, jw, jw, (int64_t)0, L.Kp, S);
     return hipGetLastError();
 }
 
 // The int8 prefill product over prepared operands at ap (A's part) and wp
 // (W's part).
-hipError_t launch_a2r(const PrepLayout &L, const Segs &S, int64_t M, int64_t N, int64_t K, const uint8_t *ap,
+hipError_t launch_a2r(const PrepLayout &L, const Segs &S, int64_t M, int64_t N, const uint8_t *ap,
                       const uint8_t *wp, float *Y, int64_t ldy, hipStream_t st) {
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
     hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st,
                        reinterpret_cast<const int8_t *>(ap + L.a_codes), reinterpret_cast<const float *>(ap + L.a_cs),
                        reinterpret_cast<const int8_t *>(wp + L.w_codes), reinterpret_cast<const float *>(wp + L.w_cs),
-                       M, N, L.Mp, L.Np, L.Kp, (int32_t)(K / 32), S, Y, ldy, tile_group(ntiles));
+                       M, N, L.Mp, L.Np, L.Kp, S.nq, S, Y, ldy, tile_group(ntiles));
     return hipGetLastError();
 }
 
@@ -1985,19 +2117,19 @@ size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W, bool w_prepared) {
     if (W.rows == 0 || A.rows == 0) return 0;
     if (use_gemv(A, W)) return decode_workspace(A, W);
     if (!use_prefill(A)) return 0;
-    const PrepLayout L = prep_layout(A, W);
+    const PrepLayout L = prep_layout(A.rows, W.rows, segs_of(A));
     return w_prepared ? L.a_bytes : L.total;
 }
 
 size_t wprep_bytes(const mxs_qmat &W) {
     if (W.rows == 0) return 0;
-    return prep_layout(0, W.rows, W.K).w_bytes;
+    return prep_layout(0, W.rows, segs_of(W)).w_bytes;
 }
 
 hipError_t launch_prepare_weights(const mxs_qmat &W, void *wprep, hipStream_t st) {
     if (W.rows == 0) return hipSuccess;
-    const PrepLayout L = prep_layout(0, W.rows, W.K);
-    return launch_prep_w(W, L, make_segs(W.n8, W.n6, W.n4), static_cast<uint8_t *>(wprep), st);
+    const Segs S = segs_of(W);
+    return launch_prep_w(W, prep_layout(0, W.rows, S), S, static_cast<uint8_t *>(wprep), st);
 }
 
 size_t gemm_workspace_mx(const mxs_qmat &A, const mxs_qmat &W) {
@@ -2012,27 +2144,27 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, const void *w
     const int64_t M = A.rows, N = W.rows;
     if (M == 0 || N == 0) return hipSuccess;
     if (!use_prefill(A) || use_gemv(A, W)) return launch_small(A, W, Y, ldy, ws, st);
-    const PrepLayout L = prep_layout(A, W);
+    const Segs S = segs_of(A);
+    const PrepLayout L = prep_layout(M, N, S);
     uint8_t *ap = static_cast<uint8_t *>(ws);
-    const Segs S = make_segs(A.n8, A.n6, A.n4);
-    const int64_t windows = prep_windows(S, A.K, L.Kp);
+    const int64_t windows = prep_windows(S, L.Kp);
     PrepJob ja{view_of(A), M, L.Mp, reinterpret_cast<int8_t *>(ap + L.a_codes), reinterpret_cast<float *>(ap + L.a_cs),
                L.Mp / 64, 1};
     const int64_t ta = ja.tiles_r * windows;
     const uint8_t *wp = static_cast<const uint8_t *>(wprep);
     if (wp) {   // W prepared already: A's operand only
-        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)ta), dim3(256), 0, st, ja, ja, ta, A.K, L.Kp, S);
+        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)ta), dim3(256), 0, st, ja, ja, ta, L.Kp, S);
     } else {    // both operands in one launch, W's part after A's
         uint8_t *wq = ap + L.a_bytes;
         PrepJob jw{view_of(W), N, L.Np, reinterpret_cast<int8_t *>(wq + L.w_codes),
                    reinterpret_cast<float *>(wq + L.w_cs), L.Np / 64, 0};
         const int64_t tw = jw.tiles_r * windows;
-        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, A.K, L.Kp, S);
+        hipLaunchKernelGGL(k_gemm_prep, dim3((unsigned)(ta + tw)), dim3(256), 0, st, ja, jw, ta, L.Kp, S);
         wp = wq;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_a2r(L, S, M, N, A.K, ap, wp, Y, ldy, st);
+    return launch_a2r(L, S, M, N, ap, wp, Y, ldy, st);
 }
 
 
@@ -2127,7 +2259,7 @@ size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W, bool w_p
     if (M == 0 || W.rows == 0) return 0;
     const mxs_qmat A = act_shape(M, W);
     if (fused_prefill(M, W.K, dt) && !use_gemv(A, W)) {
-        const PrepLayout L = prep_layout(A, W);
+        const PrepLayout L = prep_layout(M, W.rows, segs_of(A));
         return w_prepared ? L.a_bytes : L.total;
     }
     return act_planes(A).total + gemm_workspace(A, W, w_prepared);
@@ -2154,8 +2286,8 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
         if (e != hipSuccess) return e;
         return launch_mixed_gemm(A, W, wprep, Y, ldy, base + P.total, st);
     }
-    const PrepLayout L = prep_layout(A, W);
-    const Segs S = make_segs(A.n8, A.n6, A.n4);
+    const Segs S = segs_of(A);
+    const PrepLayout L = prep_layout(M, N, S);
     hipError_t e = launch_quant_prep(X, dt, M, ldx, perm, A.K, L.Mp, L.Kp, S,
                                      reinterpret_cast<int8_t *>(base + L.a_codes),
                                      reinterpret_cast<float *>(base + L.a_cs), st);
@@ -2166,7 +2298,7 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
         if (e != hipSuccess) return e;
         wp = base + L.a_bytes;
     }
-    return launch_a2r(L, S, M, N, A.K, base, wp, Y, ldy, st);
+    return launch_a2r(L, S, M, N, base, wp, Y, ldy, st);
 }
 
 hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,

@@ -287,7 +287,7 @@ mxs_status mxs_mixed_gemm(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_
  * Errors: as mxs_mixed_gemm, plus MXS_ERR_UNSUPPORTED (workspace above the
  * scratch size) and MXS_ERR_DEVICE (the scratch address lookup failed).
  */
-#define MXS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define MXS_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y, int64_t ldy,
                                   hipStream_t stream);
 
