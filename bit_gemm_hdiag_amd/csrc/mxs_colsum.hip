@@ -132,8 +132,23 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 3;
-    const int64_t col0 = (int64_t)blockIdx.x * (32 * CPL) + wave * (8 * CPL) + (lane & 7) * CPL;
-    const int64_t r0 = (chunk0 + blockIdx.y) * kChunkRows;
+    // Workgroup order by XCD: workgroups are dealt to the eight XCDs in
+    // turn, so workgroup w (in launch order) works as v = (w mod 8) G / 8 +
+    // w / 8; each XCD then streams a contiguous run of whole chunks (all
+    // column groups of a chunk's rows) instead of every eighth 512-byte strip
+    // of every row. Measured 7 % faster at 262144 x 8192 (4 % at x 28672).
+    int64_t bx = blockIdx.x, by = blockIdx.y;
+    {
+        const int64_t gx = gridDim.x, G = gx * (int64_t)gridDim.y;
+        if (G % 8 == 0) {
+            const int64_t w = by * gx + bx;
+            const int64_t v = (w & 7) * (G >> 3) + (w >> 3);
+            bx = v % gx;
+            by = v / gx;
+        }
+    }
+    const int64_t col0 = bx * (32 * CPL) + wave * (8 * CPL) + (lane & 7) * CPL;
+    const int64_t r0 = (chunk0 + by) * kChunkRows;
     const int64_t r1 = r0 + kChunkRows < M ? r0 + kChunkRows : M;
 
     double acc[CPL];
@@ -145,6 +160,29 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     if (col0 < K) {
         const T *p = X + col0;
         int64_t r = r0 + g;
+        if constexpr (kScore && VEC && sizeof(T) == 2 && CPL == 8) {
+            // score: the eight rows' raw 16-byte words are all requested
+            // before the first is unpacked (the scheduler otherwise
+            // interleaves loads with the rounding arithmetic and keeps about
+            // half of them in flight); measured 9-28 % faster, bit-identical
+            for (; r + 56 < r1; r += 64) {
+                u32x4 d[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (r + 8 * u) * ldx));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    float v[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = __uint_as_float(d[u][i] << 16);
+                        v[2 * i + 1] = __uint_as_float(d[u][i] & 0xFFFF0000u);
+                    }
+                    acc_residual_sq<CPL>(v, acc);
+                }
+            }
+        }
         // eight rows of the lane's chain in flight, consumed in row order
         for (; r + 56 < r1; r += 64) {
             float v[8][CPL];
@@ -176,7 +214,7 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
     if (g != 0 || col0 >= K) return;
 
     if (MODE == 0 || MODE == 2) {
-        double *dst = out + (int64_t)blockIdx.y * K + col0;
+        double *dst = out + by * K + col0;
 #pragma unroll
         for (int i = 0; i < CPL; i += 2) *reinterpret_cast<double2 *>(dst + i) = make_double2(acc[i], acc[i + 1]);
     } else if (MODE == 1) {
@@ -191,6 +229,10 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
 // Ordered combination of chunk totals.
 // calibrate: acc[k] += part[0][k]; acc[k] += part[1][k]; ...
 // score: e = (init ? 0 : E[k]) + part[0][k] + ...; fin ? score = hdiag*e : E = e
+// One thread per column; its loads run up to 32 chunks ahead of the
+// (ordered) additions. (Deeper batches, 64 or 128 chunks, and staging 256
+// chunks x 32 columns per workgroup in LDS were measured no faster.)
+constexpr int kCmbAhead = 32;
 template <bool SCORE>
 __global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part, int64_t nch,
                                                  int64_t K, double *__restrict__ acc,
@@ -199,14 +241,13 @@ __global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part,
     const int64_t k = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (k >= K) return;
     double e = (SCORE && init) ? 0.0 : acc[k];
-    // loads run up to 32 chunks ahead of the (ordered) additions
-    for (int64_t c = 0; c < nch; c += 32) {
-        double v[32];
+    for (int64_t c = 0; c < nch; c += kCmbAhead) {
+        double v[kCmbAhead];
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
+        for (int u = 0; u < kCmbAhead; ++u)
             if (c + u < nch) v[u] = part[(c + u) * K + k];
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
+        for (int u = 0; u < kCmbAhead; ++u)
             if (c + u < nch) e = e + v[u];
     }
     if (SCORE && fin) score[k] = hdiag[k] * e;

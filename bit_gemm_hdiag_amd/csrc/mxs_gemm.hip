@@ -1942,9 +1942,9 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ p
 // more tiles than CUs keep groups of 8 (4 measured 1-2 % slower there).
 int32_t tile_group(int64_t ntiles) { return ntiles <= 256 ? 4 : 8; }
 
-// Prepared operands of the int8 prefill kernel: codes (A in fragment order,
-// W row-major, rows padded to the tile and K to whole 4-block units) and
-// fp32 window scales [block][row]. A's part comes first in the workspace;
+// Prepared operands of the int8 prefill kernel: 32-byte units (A in
+// fragment order, W row-major; rows padded to the tile and to whole 128-byte
+// pieces) and fp32 window scales [unit][row]. A's part comes first in the workspace;
 // W's part is the same bytes whether it sits there or in a buffer filled
 // once by mxs_prepare_weights.
 struct PrepLayout {
