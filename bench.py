@@ -22,8 +22,10 @@ mxs_prepare_weights + mxs_mixed_gemm_prepared (W's operand built once per
 weight, a prepare_w stage). `cpu_baseline` is the
 CPU oracle on a bounded sample of the step, extrapolated (all host cores,
 and one core in a child process). Extra keys: `q_proj_step` (the Llama-3-8B
-q_proj-shaped layer step), `mlp_gemm` (Llama-3-8B MLP GEMMs at 4096 tokens)
-and `decode` (70B MLP decode GEMMs at 1, 8 and 32 tokens, cache-cold).
+q_proj-shaped layer step), `mlp_gemm` (Llama-3-8B MLP GEMMs at 4096 tokens),
+`decode` (70B MLP decode GEMMs at 1, 8 and 32 tokens, cache-cold) and
+`mixed_vs_uniform` (mixed_gemm under the all-4-bit and the 5/15/80 % maps,
+q_proj prefill and 70B up-projection decode, warm and cold).
 
 `roofline.traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
 stored in profiles/ and is reported only while the kernel source is
@@ -122,14 +124,16 @@ def decode_cases(mx, synth, torch, reps=20):
     return out
 
 
-def overhead_cases(mx, synth, torch, reps=20):
+def overhead_cases(mx, synth, torch, reps=20, brief=False):
     """Cost of the mixed map against uniform MXINT4: mixed_gemm on the same
     layer under the all-4-bit map, the 4.03-bit map (one 8-bit block), the
     binary 4/8 map of the same 8-bit share (5 %), and the 5/15/80 % map, for
     the q_proj prefill (2048 x 4096 x 4096) and the 70B up-projection decode
-    (1 token, 28672 x 8192)."""
+    (1 token, 28672 x 8192). brief: only the all-4-bit and 5/15/80 % maps and
+    mxs_mixed_gemm, returned instead of printed."""
     dev = torch.device("cuda:0")
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    rows = []
     for case, M, N, K, seed in (("prefill q_proj", 2048, 4096, 4096, 5000), ("decode 70B up", 1, 28672, 8192, 5100)):
         nb = K // 32
         gains = synth.outlier_gains(K, seed + synth.ROLE_CHANNELS)
@@ -137,14 +141,17 @@ def overhead_cases(mx, synth, torch, reps=20):
         X = synth.activations(M, K, seed + synth.ROLE_X, gains, device=dev)
         perm = torch.randperm(K, generator=torch.Generator().manual_seed(seed)).to(torch.int32).to(dev)
         base = None
-        for name, (bp8, bp6) in (("uniform 4-bit", (0, 0)), ("one 8-bit block", ((10000 + nb - 1) // nb, 0)),
-                                 ("binary 4/8 (5 % 8-bit)", (500, 0)), ("5/15/80 %", (500, 1500))):
+        maps = (("uniform 4-bit", (0, 0)), ("one 8-bit block", ((10000 + nb - 1) // nb, 0)),
+                ("binary 4/8 (5 % 8-bit)", (500, 0)), ("5/15/80 %", (500, 1500)))
+        if brief:
+            maps = (maps[0], maps[3])
+        for name, (bp8, bp6) in maps:
             n8, n6, n4 = mx.mxs_budget_blocks(K, bp8, bp6)
             Wq = mx.mxs_quantize(W, perm, n8, n6, n4)
             Aq = mx.mxs_quantize(X, perm, n8, n6, n4)
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             out = {"case": case, "map": name, "blocks": [n8, n6, n4], "avg_bits": (8 * n8 + 6 * n6 + 4 * n4) / nb}
-            for entry in ("mxs_mixed_gemm", "mxs_mixed_gemm_mx"):
+            for entry in ("mxs_mixed_gemm",) if brief else ("mxs_mixed_gemm", "mxs_mixed_gemm_mx"):
                 wsf = getattr(mx, entry + "_workspace")
                 ws = torch.empty(max(1, wsf(Aq, Wq)), dtype=torch.uint8, device=dev)
                 f = getattr(mx, entry)
@@ -154,10 +161,15 @@ def overhead_cases(mx, synth, torch, reps=20):
             if base is None:
                 base = out
             for k in ("mxs_mixed_gemm_us", "mxs_mixed_gemm_mx_us", "mxs_mixed_gemm_cold_us"):
-                out[k.replace("_us", "_vs_uniform")] = out[k] / base[k]
-            print(json.dumps(out), flush=True)
+                if k in out:
+                    out[k.replace("_us", "_vs_uniform")] = out[k] / base[k]
+            if brief:
+                rows.append(out)
+            else:
+                print(json.dumps(out), flush=True)
             del Wq, Aq, Y
         del W, X
+    return rows
 
 
 FP32_MFMA_PEAK = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
@@ -920,6 +932,8 @@ def block_line(mx, synth, torch, args):
                                                  "variant_mx", "variant_fused", "stages")}
         out["mlp_gemm"] = mlp_gemms(mx, synth, torch)
         out["decode"] = decode_cases(mx, synth, torch)
+        log("mixed map against uniform MXINT4 (q_proj prefill, 70B up decode)")
+        out["mixed_vs_uniform"] = overhead_cases(mx, synth, torch, reps=10, brief=True)
     return out
 
 

@@ -163,25 +163,48 @@ __global__ __launch_bounds__(256) void k_quant_gather_pf(const T *__restrict__ X
                 if (tid + 256 * i < nvec) srow[tid + 256 * i] = ring[d][i];
             lds_barrier();
             if (row + DEPTH * G < R) fetch(ring[d], row + DEPTH * G);
-            for (int64_t cg = tid; cg * 8 < K; cg += 256) {   // whole quads stay together
-                float v[8];
-                if (PG) {
-                    const uint32_t kmax = (uint32_t)K - 1u;
-                    const uint4 a = reinterpret_cast<const uint4 *>(perm + cg * 8)[0];
-                    const uint4 b = reinterpret_cast<const uint4 *>(perm + cg * 8)[1];
-                    const uint32_t j[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            if constexpr (PG) {
+                // the permutation entries of a group are loaded two groups
+                // ahead of its gather (an L2 round trip per group otherwise)
+                const uint32_t kmax = (uint32_t)K - 1u;
+                uint4 pa[2], pb[2];
+                auto pload = [&](int k, int64_t c) {
+                    if (c * 8 < K) {
+                        pa[k] = reinterpret_cast<const uint4 *>(perm + c * 8)[0];
+                        pb[k] = reinterpret_cast<const uint4 *>(perm + c * 8)[1];
+                    }
+                };
+                auto gather = [&](int k, int64_t c) {   // whole quads stay together
+                    const uint32_t j[8] = {pa[k].x, pa[k].y, pa[k].z, pa[k].w, pb[k].x, pb[k].y, pb[k].z, pb[k].w};
+                    float v[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) v[i] = load1<T>(s + (j[i] < kmax ? j[i] : kmax));
-                } else {
+                    emit(P, row, c >> 2, (int)(c & 3), v);
+                };
+                int64_t cg = tid;
+                pload(0, cg);
+                pload(1, cg + 256);
+                while (cg * 8 < K) {
+                    gather(0, cg);
+                    pload(0, cg + 512);
+                    cg += 256;
+                    if (cg * 8 >= K) break;
+                    gather(1, cg);
+                    pload(1, cg + 512);
+                    cg += 256;
+                }
+            } else {
+                for (int64_t cg = tid; cg * 8 < K; cg += 256) {   // whole quads stay together
                     const uint4 pi = *reinterpret_cast<const uint4 *>(sperm + cg * 8);
                     const uint32_t w[4] = {pi.x, pi.y, pi.z, pi.w};
+                    float v[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         v[2 * i] = load1<T>(s + (w[i] & 0xFFFFu));
                         v[2 * i + 1] = load1<T>(s + (w[i] >> 16));
                     }
+                    emit(P, row, cg >> 2, (int)(cg & 3), v);
                 }
-                emit(P, row, cg >> 2, (int)(cg & 3), v);
             }
             row += G;
         }
