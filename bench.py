@@ -11,7 +11,8 @@ MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128).
 
 Prints one JSON line. `value` is the block's GEMM work (2 M N K summed over
 the seven layers) over the block step time, in TOPS, with mxs_mixed_gemm
-(int8 block sums); `stages` gives every stage's time per step, GB/s (and
+(int8 block sums for the 4-bit blocks, exact bf16 products for the 8- and
+6-bit blocks); `stages` gives every stage's time per step, GB/s (and
 TOPS) and fraction of its peak, from HIP events around every call on the
 library's stream in the timed steps; `roofline` is for the stage with the
 largest share of the step, `roofline_gemm` and `roofline_calibrate` for the
@@ -1012,7 +1013,7 @@ def q_proj_line(mx, synth, torch, args):
     achieved = ops / gemm_call_s / 1e12
     roofline = dict(bound="mfma", achieved=achieved, peak=INT8_PEAK / 1e12, unit="TOP/s",
                     frac=achieved * 1e12 / INT8_PEAK, traffic=measured_traffic(),
-                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_a2r (int8 MFMA)",
+                    kernel="mixed_gemm call: k_gemm_prep + k_gemm_a2r (int8 MFMA for 4-bit blocks, bf16 MFMA for 8- and 6-bit blocks)",
                     algorithmic_ops_per_launch=ops, launch_us=gemm_call_s * 1e6,
                     algorithmic_bytes_per_launch=work["mixed_gemm"]["bytes"])
     ach_x = ops / gemm_x / 1e12

@@ -254,9 +254,10 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W);
  *     Y[t, n] = sum_b 2^(sa[t,b] + sw[n,b]) * sum_{j in b} ca[t, j] cw[n, j]
  * where A (activations, A->rows = M tokens) and W (weights, W->rows = N) are
  * quantised with the same K, the same (n8, n6, n4) and the same permutation.
- * Each block's integer dot product is exact (int8 MFMA, int32 sums); block
- * terms are combined in fp32 (error ~ sqrt(K/32) ulp relative to
- * sum |A||W|). Y: [M, ldy] fp32 device output, ldy >= N.
+ * Each block's dot product is exact (from 64 tokens on: int8 MFMA with
+ * int32 sums for the 4-bit blocks, exact bf16 products for the 8- and 6-bit
+ * blocks; below: int32 sums); the terms are combined in fp32 (error ~
+ * sqrt(K/32) ulp relative to sum |A||W|). Y: [M, ldy] fp32 device output, ldy >= N.
  * ws: >= mxs_mixed_gemm_workspace(A, W) bytes (NULL if that is 0).
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K or block counts differ, ldy < N),
  * MXS_ERR_UNSUPPORTED (plane pointers or strides not 16/4/8-byte aligned
@@ -294,16 +295,17 @@ mxs_status mxs_mixed_gemm_noalloc(const mxs_qmat *A, const mxs_qmat *W, float *Y
 /*
  * Weights prepared once for the prefill product ([NL] §1 and §5: no
  * separate dequantisation pass inside the product). mxs_mixed_gemm expands
- * both operands' codes into the prefill kernel's exponent-aligned int8
- * operand, with fp32 window scales, in every call. Weights do not change
+ * both operands' codes into the prefill kernel's operand (bf16 values for
+ * the 8- and 6-bit blocks, exponent-aligned int8 codes with fp32 window
+ * scales for the 4-bit blocks) in every call. Weights do not change
  * between calls, so mxs_prepare_weights builds W's half once, and
  * mxs_mixed_gemm_prepared and mxs_mixed_gemm_fused_prepared reuse it for any
  * number of tokens. Their results are bit-identical to mxs_mixed_gemm and
  * mxs_mixed_gemm_fused on the same planes.
  * wprep: device buffer of mxs_prepare_weights_size(W) bytes (0 when W has
  * no rows), 256-byte aligned, owned by the caller. Its contents are private
- * to the library (W's int8 codes with rows padded to 128 and K to a multiple
- * of 128, then fp32 scales per block and row). It stays valid while W's
+ * to the library (W's prepared rows, padded to 128 rows and to a multiple
+ * of 128 bytes, then fp32 scales per 32-byte unit and row). It stays valid while W's
  * planes and shape are unchanged; a buffer prepared from other planes of the
  * same shape gives wrong results but no out-of-bounds access.
  * mxs_mixed_gemm_prepared: A, W, Y, ldy as for mxs_mixed_gemm (W's planes
@@ -347,7 +349,7 @@ mxs_status mxs_mixed_gemm_mx(const mxs_qmat *A, const mxs_qmat *W, float *Y, int
  * result bit for bit as mxs_quantize into planes followed by mxs_mixed_gemm.
  * With 64 or more rows (and, for the row staging, K <= 65536 with
  * K * (2 + element size) <= 96 KiB) the activation rows are quantised
- * straight into the prefill kernel's exponent-aligned int8 operand, so no
+ * straight into the prefill kernel's operand, so no
  * activation planes are written or read; other shapes quantise into planes
  * kept in the workspace and run the mxs_mixed_gemm kernels.
  * X: [M, ldx >= K] row-major of `dtype` (device); perm: [K] int32 gather
