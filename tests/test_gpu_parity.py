@@ -276,6 +276,40 @@ def test_mixed_gemm_exponent_spread(mx, orc, M, N, K, budget, entry):
     assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), "spread")
 
 
+@pytest.mark.parametrize("M", [128, 4])
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_nonfinite_and_zero_by_class(mx, orc, entry, M):
+    # NaN/Inf and all-zero blocks placed in each kind of block of the prefill
+    # operand: 8-bit and 6-bit blocks (bf16 values), the 4-bit blocks that
+    # round the bf16 run up to five blocks (3/4 wide blocks -> blocks 7..9),
+    # and ordinary 4-bit blocks (exponent-aligned int8); M = 4 runs the
+    # decode kernels on the same data
+    N, K = 96, 1024
+    n8, n6, n4 = 3, 4, 25
+    g = torch.Generator(device="cpu").manual_seed(4242 + M)
+    X = torch.randn(M, K, generator=g)
+    W = torch.randn(N, K, generator=g)
+    perm = torch.randperm(K, generator=g).to(torch.int32)
+    col = lambda b, j=5: int(perm[32 * b + j])      # original column of position 32 b + j
+    X[3 % M, col(1)] = float("nan")                  # 8-bit block of A
+    W[10, col(5)] = float("inf")                      # 6-bit block of W
+    X[(77 % M), col(8)] = -float("inf")              # 4-bit block carried as bf16
+    W[50, col(20)] = float("nan")                     # narrow 4-bit block of W
+    for b in (2, 6, 9, 25):                           # all-zero blocks, one per kind
+        X[:, perm[32 * b:32 * b + 32].long()] = 0.0
+        W[7, perm[32 * b:32 * b + 32].long()] = 0.0
+    X, W, perm = X.to(DEV).to(torch.bfloat16), W.to(DEV).to(torch.bfloat16), perm.to(DEV)
+    A = mx.mxs_quantize(X, perm, n8, n6, n4)
+    B = mx.mxs_quantize(W, perm, n8, n6, n4)
+    Y = getattr(mx, entry)(A, B).cpu().numpy().astype(np.float64)
+    Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), perm.cpu().numpy(), n8, n6, n4),
+                                orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4))
+    nan_ref = np.isnan(Yref)
+    assert nan_ref[3 % M].all() and nan_ref[:, 10].all() and nan_ref[:, 50].all()
+    assert np.array_equal(np.isnan(Y), nan_ref)
+    assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), "nonfinite")
+
+
 @pytest.mark.parametrize("entry", GEMMS)
 def test_mixed_gemm_fp32_tiny_layer(mx, orc, entry):
     cfg = synth.CONFIGS[1]
