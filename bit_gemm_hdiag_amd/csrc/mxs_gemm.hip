@@ -1685,6 +1685,143 @@ __global__ __launch_bounds__(64) void k_gemv(const int8_t *__restrict__ a8, int6
 }
 
 // ---------------------------------------------------------------------------
+// One token (k_gemv_row): each W row is read by S waves of one workgroup and
+// no partial rows leave the kernel. A row is walked in 16-byte pieces, in
+// plane order: the two halves of each 8-bit block, the two halves of each
+// 6-bit block (bytes 0..15 or 8..23 of the block, as in gemv_fetch), then
+// each 4-bit block whole. Wave w of the workgroup takes rows of group w / S
+// (R rows) and the pieces of split s = w % S: lane l takes pieces
+// 64 J s + l + 64 j, j < J, so consecutive lanes read consecutive bytes of a
+// plane row. The token's matching pieces (shared by the wave's R rows) and
+// both scale bytes of every piece are loaded with the W pieces, all at once.
+// Block sums are exact in int32 exactly as in vec_dot (the two lanes of a
+// half-block pair add their sums; the even lane scales the block); a lane
+// adds its blocks in piece order into an fp32 sum per row, the 64 lanes meet
+// in a fixed butterfly, and the S splits of a row are added in split order
+// through LDS.
+constexpr int kRowWaves = 4;      // waves per workgroup
+
+template <int J, int R, int S>
+__global__ __launch_bounds__(64 * kRowWaves) void k_gemv_row(const int8_t *__restrict__ a8,
+                                                              const uint8_t *__restrict__ a6,
+                                                              const uint8_t *__restrict__ a4,
+                                                              const uint8_t *__restrict__ asc, QView W, int64_t N,
+                                                              int32_t n8, int32_t n6, int32_t n4,
+                                                              float *__restrict__ y) {
+    static_assert(kRowWaves % S == 0, "splits of a row must divide the workgroup");
+    __shared__ float part[kRowWaves][R];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, sp = w % S;
+    const int64_t grp = (int64_t)blockIdx.x * (kRowWaves / S) + w / S;
+    const int32_t P8 = 2 * n8, P6 = P8 + 2 * n6, Pr = P6 + n4;
+    // rows of the group past N re-read row N - 1 and are not written
+    int64_t row[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) row[r] = min(grp * R + r, N - 1);
+
+    // piece j of the lane: class (0 past the row's pieces), byte offset in
+    // its plane row, global block. Pieces past the row re-read its last piece
+    // (every load is unconditional, so all of them are in flight at once)
+    int32_t cls[J], off[J], gb[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int32_t pu = 64 * J * sp + lane + 64 * j, p = min(pu, Pr - 1);
+        if (p < P8) { cls[j] = 8; off[j] = 16 * p; gb[j] = p >> 1; }
+        else if (p < P6) {
+            const int32_t q = p - P8;
+            cls[j] = 6; off[j] = 24 * (q >> 1) + 8 * (q & 1); gb[j] = n8 + (q >> 1);
+        } else { cls[j] = 4; off[j] = 16 * (p - P6); gb[j] = n8 + n6 + (p - P6); }
+        if (pu >= Pr) cls[j] = 0;
+    }
+    uint32_t T[J][4], R4[R][J][4], sa[J], sw[R][J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const bool c8 = gb[j] < n8, c6 = !c8 && gb[j] < n8 + n6;   // plane of the (clamped) piece
+        const uint8_t *ab = c8 ? reinterpret_cast<const uint8_t *>(a8) : c6 ? a6 : a4;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint8_t *wb = c8   ? reinterpret_cast<const uint8_t *>(W.q8) + row[r] * W.ld8
+                                : c6 ? W.q6 + row[r] * W.ld6
+                                     : W.q4 + row[r] * W.ld4;
+            const uint4 v = *reinterpret_cast<const uint4 *>(wb + off[j]);
+            R4[r][j][0] = v.x; R4[r][j][1] = v.y; R4[r][j][2] = v.z; R4[r][j][3] = v.w;
+            sw[r][j] = W.sc[row[r] * W.lds + gb[j]];
+        }
+        const uint4 v = *reinterpret_cast<const uint4 *>(ab + off[j]);
+        T[j][0] = v.x; T[j][1] = v.y; T[j][2] = v.z; T[j][3] = v.w;
+        sa[j] = asc[gb[j]];
+    }
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = cls[j];
+        const bool second = (lane & 1) != 0;   // odd piece of an 8/6-bit pair (pieces of a split start even)
+        uint32_t ab[4];
+        if (c == 6) {
+            uint32_t aw[3];
+            piece6(T[j], second, aw);
+            wide6x16(aw, ab);
+        }
+        const float fa = e8m0_to_f32(sa[j]) * (c == 6 ? 0.0625f : 1.0f);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int d;
+            if (c == 4) {
+                d = __builtin_amdgcn_sdot8((int)T[j][0], (int)R4[r][j][0], 0, false);
+                d = __builtin_amdgcn_sdot8((int)T[j][1], (int)R4[r][j][1], d, false);
+                d = __builtin_amdgcn_sdot8((int)T[j][2], (int)R4[r][j][2], d, false);
+                d = __builtin_amdgcn_sdot8((int)T[j][3], (int)R4[r][j][3], d, false);
+            } else if (c == 8) {
+                d = __builtin_amdgcn_sdot4((int)T[j][0], (int)R4[r][j][0], 0, false);
+                d = __builtin_amdgcn_sdot4((int)T[j][1], (int)R4[r][j][1], d, false);
+                d = __builtin_amdgcn_sdot4((int)T[j][2], (int)R4[r][j][2], d, false);
+                d = __builtin_amdgcn_sdot4((int)T[j][3], (int)R4[r][j][3], d, false);
+                d += __builtin_amdgcn_mov_dpp(d, 0xB1, 0xF, 0xF, true);
+            } else if (c == 6) {
+                uint32_t wb[4], ww[3];
+                piece6(R4[r][j], second, ww);
+                wide6x16(ww, wb);
+                d = __builtin_amdgcn_sdot4((int)ab[0], (int)wb[0], 0, false);
+                d = __builtin_amdgcn_sdot4((int)ab[1], (int)wb[1], d, false);
+                d = __builtin_amdgcn_sdot4((int)ab[2], (int)wb[2], d, false);
+                d = __builtin_amdgcn_sdot4((int)ab[3], (int)wb[3], d, false);
+                d += __builtin_amdgcn_mov_dpp(d, 0xB1, 0xF, 0xF, true);
+            } else {
+                d = 0;
+            }
+            const bool use = c == 4 || ((c == 8 || c == 6) && !second);
+            acc[r] = __builtin_fmaf((float)d, use ? fa * e8m0_to_f32(sw[r][j]) : 0.f, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float v = acc[r];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+        acc[r] = v;
+    }
+    if constexpr (S == 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (lane == 0 && grp * R + r < N) y[grp * R + r] = acc[r];
+    } else {
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) part[w][r] = acc[r];
+        }
+        __syncthreads();
+        if (sp == 0 && lane < R && grp * R + lane < N) {
+            float v = part[w][lane];
+#pragma unroll
+            for (int k = 1; k < S; ++k) v += part[w + k][lane];
+            y[grp * R + lane] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode with the matrix cores (9 to 32 tokens).
 //
 // One v_mfma_i32_32x32x32_i8 yields a 32 token x 32 row tile of exact block
@@ -2049,9 +2186,42 @@ hipError_t launch_decode(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t
     return hipGetLastError();
 }
 
+// One token: J pieces per lane, R rows per wave, S waves per row
+template <int J, int R, int S>
+hipError_t launch_row_t(const mxs_qmat &A, const mxs_qmat &W, float *Y, hipStream_t st) {
+    const int64_t N = W.rows, rows_per_wg = (int64_t)R * (kRowWaves / S);
+    hipLaunchKernelGGL((k_gemv_row<J, R, S>), dim3((unsigned)ceil_div(N, rows_per_wg)), dim3(64 * kRowWaves), 0, st,
+                       A.q8, A.q6, A.q4, A.sc, view_of(W), N, A.n8, A.n6, A.n4, Y);
+    return hipGetLastError();
+}
+
+// pieces of one row (16-byte pieces: two per 8- or 6-bit block, one per 4-bit block)
+int64_t row_pieces(const mxs_qmat &A) { return 2 * A.n8 + 2 * A.n6 + A.n4; }
+constexpr int64_t kRowMaxPieces = 4 * 64 * 8;   // longer rows take the slice kernel
+
+hipError_t launch_row(const mxs_qmat &A, const mxs_qmat &W, float *Y, hipStream_t st) {
+    const int64_t P = row_pieces(A);
+    // measured on the 70B MLP rows (308 pieces at K = 8192, 1076 at 28672):
+    // three pieces per lane for four rows, split over two waves, and five
+    // pieces for two rows over four waves, keep the most bytes in flight
+    // (about 100 VGPRs, five waves per SIMD); one wave per long row (17
+    // pieces) left two waves per SIMD and was 40 % slower
+    if (P <= 3 * 64) return launch_row_t<3, 4, 1>(A, W, Y, st);
+    if (P <= 2 * 3 * 64) return launch_row_t<3, 4, 2>(A, W, Y, st);
+    if (P <= 4 * 3 * 64) return launch_row_t<3, 4, 4>(A, W, Y, st);
+    if (P <= 4 * 5 * 64) return launch_row_t<5, 2, 4>(A, W, Y, st);
+    return launch_row_t<8, 2, 4>(A, W, Y, st);
+}
+
+bool use_row(const mxs_qmat &A) {
+    const int64_t P = row_pieces(A);
+    return A.rows == 1 && P > 0 && P <= kRowMaxPieces;
+}
+
 hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy, void *ws, hipStream_t st) {
     const int64_t M = A.rows;
     if (M > kGemvVecRows) return launch_decode(A, W, Y, ldy, ws, st);
+    if (use_row(A)) return launch_row(A, W, Y, st);
     if (M <= 1) return launch_gemv_t<1>(A, W, Y, ldy, ws, st);
     if (M <= 2) return launch_gemv_t<2>(A, W, Y, ldy, ws, st);
     if (M <= 4) return launch_gemv_t<4>(A, W, Y, ldy, ws, st);
@@ -2095,6 +2265,7 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
 // Decode (up to 32 tokens) and 33..63 tokens take the same kernels in both
 // entry points; they differ in the prefill kernels only.
 size_t decode_workspace(const mxs_qmat &A, const mxs_qmat &W) {
+    if (use_row(A)) return 0;   // one token: whole rows per wave, no partial rows
     const int64_t ns = A.rows > kGemvVecRows ? decode_groups(A) : [&] {
         const VecSlices S = vec_slices(A.n8, A.n6, A.n4);
         return (int64_t)S.s8 + S.s6 + S.s4;

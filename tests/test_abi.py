@@ -148,6 +148,9 @@ def test_quantize_and_gemm_errors(lib):
         wsf.restype = ctypes.c_size_t
         assert wsf(ctypes.byref(qm(rows=128)), ctypes.byref(qm(rows=16))) > 0
         assert wsf(ctypes.byref(qm(rows=0)), ctypes.byref(qm(rows=16))) == 0
+        # decode (scale rows 4-byte aligned): one token needs no partial rows, two do
+        assert wsf(ctypes.byref(qm(rows=1, lds=4)), ctypes.byref(qm(rows=16, lds=4))) == 0
+        assert wsf(ctypes.byref(qm(rows=2, lds=4)), ctypes.byref(qm(rows=16, lds=4))) > 0
     kv = lib.mxs_quantize_kv
     kv.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
     assert kv(FAKE, 1, 4, 8, 100, FAKE, FAKE, None) == -2

@@ -310,6 +310,41 @@ def test_mixed_gemm_nonfinite_and_zero_by_class(mx, orc, entry, M):
     assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), "nonfinite")
 
 
+@pytest.mark.parametrize("N,K,bits", [(97, 2048, (0, 0, 64)), (130, 4096, (4, 12, 112)),
+                                       (1001, 8192, (12, 40, 204)), (64, 16384, (0, 0, 512)),
+                                       (257, 24576, (0, 0, 768)), (33, 28672, (45, 134, 717)),
+                                       (70, 40960, (0, 0, 1280)), (50, 41024, (0, 0, 1282)),
+                                       (40, 65536, (0, 0, 2048)), (40, 32800, (1025, 0, 0)),
+                                       (65, 1024, (32, 0, 0)), (129, 1536, (0, 48, 0))])
+@pytest.mark.parametrize("entry", GEMMS)
+def test_mixed_gemm_one_token_rows(mx, orc, entry, N, K, bits):
+    # one token: rows of 64 ... 2048 16-byte pieces on every (pieces per
+    # lane, rows per wave, waves per row) instance, each at or near its upper
+    # bound, then 2050 pieces (the slice kernel); ragged row counts;
+    # single-width maps; non-finite and all-zero W blocks in each width class
+    n8, n6, n4 = bits
+    g = torch.Generator(device="cpu").manual_seed(N + K)
+    X = torch.randn(1, K, generator=g)
+    W = torch.randn(N, K, generator=g) * 2.0 ** torch.randint(-6, 7, (N, K // 32), generator=g).repeat_interleave(32, 1)
+    perm = torch.randperm(K, generator=g).to(torch.int32)
+    col = lambda b, j=3: int(perm[32 * b + j])
+    firsts = [b for b, n in ((0, n8), (n8, n6), (n8 + n6, n4)) if n > 0]
+    for i, b in enumerate(firsts):                     # one non-finite and one all-zero block per class
+        W[(5 + 7 * i) % N, col(b)] = float("nan") if i != 1 else float("inf")
+        W[(2 + 7 * i) % N, perm[32 * b:32 * b + 32].long()] = 0.0
+    X[0, perm[32 * firsts[-1]:32 * firsts[-1] + 32].long()] = 0.0   # an all-zero block of the token
+    X, W, perm = X.to(DEV).to(torch.bfloat16), W.to(DEV).to(torch.bfloat16), perm.to(DEV)
+    A = mx.mxs_quantize(X, perm, n8, n6, n4)
+    B = mx.mxs_quantize(W, perm, n8, n6, n4)
+    Y = getattr(mx, entry)(A, B).cpu().numpy().astype(np.float64)
+    Yref, Yabs = orc.mixed_gemm(orc.quantize(host(X), perm.cpu().numpy(), n8, n6, n4),
+                                orc.quantize(host(W), perm.cpu().numpy(), n8, n6, n4))
+    nan_ref = np.isnan(Yref)
+    assert nan_ref[0, [(5 + 7 * i) % N for i in range(len(firsts))]].all() and not nan_ref.all()
+    assert np.array_equal(np.isnan(Y), nan_ref)
+    assert_gemm(np.where(nan_ref, 0, Y), np.where(nan_ref, 0, Yref), np.where(nan_ref, 1, Yabs), f"N={N} K={K}")
+
+
 @pytest.mark.parametrize("entry", GEMMS)
 def test_mixed_gemm_fp32_tiny_layer(mx, orc, entry):
     cfg = synth.CONFIGS[1]
