@@ -11,14 +11,23 @@
 // order, so results are bit-identical to any implementation of that order:
 //   rows in chunks of 256; within a chunk, partial sum p_i over the rows
 //   whose offset is i mod 8, in row order from +0; chunk total
-//   ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); chunk totals added in chunk order.
+//   ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); score: chunk totals added in chunk
+//   order; calibrate: runs of 16 chunks, a run total adding its chunk totals
+//   in order from the first, run totals added in run order.
 //
 // Mapping: a wavefront is 8 row groups x 8 lanes; lane (g, c) owns CPL
 // consecutive columns (one load per row) and the partial sum p_g of its
 // chunk, so each wave streams 8 rows x 8 CPL columns per step and the 4 waves
 // of a workgroup cover 32 CPL adjacent columns. The tree is three cross-lane
 // xor steps (8, 16, 32). Chunk totals go to a workspace and a second kernel
-// adds them in chunk order; a single chunk is written directly.
+// adds them in order; a single chunk is written directly. Large calibrations
+// give each workgroup a whole run of 16 chunks instead: it adds the run's
+// chunk totals in registers and writes one run total, so the workspace
+// traffic, whose write-back into a 4 GB read stream cost more than its share
+// of the bytes, falls 16-fold (measured 5.71 -> 6.50 TB/s at 262144 x 8192,
+// 5.80 -> 6.68 at 262144 x 28672). Smaller ones (fewer than 512 such
+// workgroups) keep one chunk per workgroup and let the second kernel form
+// the runs: the same order, the same bits.
 // CPL = 8 (16-byte bf16 loads): in the score kernel the 4 lanes of a quad
 // hold one 32-column MXINT4 block of a row, so the block maximum is two DPP
 // steps. (CPL = 4, with twice the waves and an 8-lane block maximum, measured
@@ -123,12 +132,14 @@ __device__ __forceinline__ void acc_sq(const float v[CPL], double acc[CPL]) {
 // MODE 1: calibrate, single chunk: hdiag[k] += total
 // MODE 2: score, write chunk totals to part[chunk][K]
 // MODE 3: score, single chunk: score[k] = hdiag[k] * total
+// MODE 4: calibrate, one run of kRunChunks chunks per workgroup: write run
+//         totals to part[run][K]
 template <typename T, bool VEC, int MODE, int CPL>
 __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t M, int64_t K,
                                                 int64_t ldx, int64_t chunk0,
                                                 double *__restrict__ out,
                                                 const double *__restrict__ hdiag) {
-    constexpr bool kScore = MODE >= 2;
+    constexpr bool kScore = MODE == 2 || MODE == 3;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 3;
@@ -148,7 +159,13 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
         }
     }
     const int64_t col0 = bx * (32 * CPL) + wave * (8 * CPL) + (lane & 7) * CPL;
-    const int64_t r0 = (chunk0 + by) * kChunkRows;
+    constexpr int kChunks = MODE == 4 ? (int)kRunChunks : 1;
+    double tot[CPL];   // chunk total, or the run total so far
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) tot[i] = 0.0;
+    for (int cc = 0; cc < kChunks; ++cc) {
+    const int64_t r0 = (chunk0 + by * kChunks + cc) * kChunkRows;
+    if (r0 >= M) break;   // a short last run (its first chunk always has rows)
     const int64_t r1 = r0 + kChunkRows < M ? r0 + kChunkRows : M;
 
     double acc[CPL];
@@ -202,38 +219,44 @@ __global__ __launch_bounds__(256) void k_colsum(const T *__restrict__ X, int64_t
         }
     }
 
-    // ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7)) across the row groups
+    // ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7)) across the row groups; a run
+    // adds its chunk totals in chunk order, starting from the first
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         double x = acc[i];
         x = x + __shfl_xor(x, 8);
         x = x + __shfl_xor(x, 16);
         x = x + __shfl_xor(x, 32);
-        acc[i] = x;
+        tot[i] = cc == 0 ? x : tot[i] + x;
+    }
     }
     if (g != 0 || col0 >= K) return;
 
-    if (MODE == 0 || MODE == 2) {
+    if (MODE == 0 || MODE == 2 || MODE == 4) {
         double *dst = out + by * K + col0;
 #pragma unroll
-        for (int i = 0; i < CPL; i += 2) *reinterpret_cast<double2 *>(dst + i) = make_double2(acc[i], acc[i + 1]);
+        for (int i = 0; i < CPL; i += 2) *reinterpret_cast<double2 *>(dst + i) = make_double2(tot[i], tot[i + 1]);
     } else if (MODE == 1) {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) out[col0 + i] = out[col0 + i] + acc[i];
+        for (int i = 0; i < CPL; ++i) out[col0 + i] = out[col0 + i] + tot[i];
     } else {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) out[col0 + i] = hdiag[col0 + i] * (0.0 + acc[i]);
+        for (int i = 0; i < CPL; ++i) out[col0 + i] = hdiag[col0 + i] * (0.0 + tot[i]);
     }
 }
 
-// Ordered combination of chunk totals.
-// calibrate: acc[k] += part[0][k]; acc[k] += part[1][k]; ...
+// Ordered combination of the workspace totals.
 // score: e = (init ? 0 : E[k]) + part[0][k] + ...; fin ? score = hdiag*e : E = e
-// One thread per column; its loads run up to 32 chunks ahead of the
-// (ordered) additions. (Deeper batches, 64 or 128 chunks, and staging 256
-// chunks x 32 columns per workgroup in LDS were measured no faster.)
+// calibrate (RUN = 1, run totals): acc[k] += part[0][k]; acc[k] += part[1][k]; ...
+// calibrate (RUN = kRunChunks, chunk totals): each run of RUN consecutive
+//   totals (the last may be short) is added in order from its first, then
+//   acc[k] += run total, run by run.
+// One thread per column; its loads run up to 32 totals ahead of the
+// (ordered) additions. (Deeper batches, 64 or 128, and staging 256 totals x
+// 32 columns per workgroup in LDS were measured no faster.)
 constexpr int kCmbAhead = 32;
-template <bool SCORE>
+static_assert(kCmbAhead % kRunChunks == 0, "a batch of loads holds whole runs");
+template <bool SCORE, int RUN>
 __global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part, int64_t nch,
                                                  int64_t K, double *__restrict__ acc,
                                                  const double *__restrict__ hdiag,
@@ -246,13 +269,28 @@ __global__ __launch_bounds__(64) void k_combine(const double *__restrict__ part,
 #pragma unroll
         for (int u = 0; u < kCmbAhead; ++u)
             if (c + u < nch) v[u] = part[(c + u) * K + k];
+        if constexpr (RUN == 1) {
 #pragma unroll
-        for (int u = 0; u < kCmbAhead; ++u)
-            if (c + u < nch) e = e + v[u];
+            for (int u = 0; u < kCmbAhead; ++u)
+                if (c + u < nch) e = e + v[u];
+        } else {
+            double r = 0.0;
+#pragma unroll
+            for (int u = 0; u < kCmbAhead; ++u)
+                if (c + u < nch) {
+                    r = u % RUN == 0 ? v[u] : r + v[u];
+                    if (u % RUN == RUN - 1 || c + u == nch - 1) e = e + r;
+                }
+        }
     }
     if (SCORE && fin) score[k] = hdiag[k] * e;
     else acc[k] = e;
 }
+
+// Calibrations with at least this many (run, column group) workgroups take
+// one run per workgroup (measured faster from 512 up: 65536 x 8192, 512 of
+// them, 5.64 -> 6.19 TB/s; 16384 x 4096, 64 of them, 4.75 -> 1.12)
+constexpr int64_t kRunPathMinWgs = 512;
 
 template <typename T, bool VEC, int CPL>
 hipError_t run_colsum(const T *X, int64_t M, int64_t K, int64_t ldx, bool score_mode,
@@ -268,16 +306,21 @@ hipError_t run_colsum(const T *X, int64_t M, int64_t K, int64_t ldx, bool score_
     }
     double *E = ws;                       // score: running column error
     double *part = score_mode ? ws + K : ws;
+    // launches cover whole runs (kMaxChunksPerLaunch is a multiple of kRunChunks)
     for (int64_t c0 = 0; c0 < nch; c0 += kMaxChunksPerLaunch) {
         const int64_t n = nch - c0 < kMaxChunksPerLaunch ? nch - c0 : kMaxChunksPerLaunch;
+        const int64_t runs = ceil_div(n, kRunChunks);
+        const unsigned gk = (unsigned)ceil_div(K, 64);
+        const int init = c0 == 0, fin = c0 + n >= nch;
+        const bool by_run = !score_mode && runs * (int64_t)gx >= kRunPathMinWgs;
         if (score_mode) hipLaunchKernelGGL((k_colsum<T, VEC, 2, CPL>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
+        else if (by_run) hipLaunchKernelGGL((k_colsum<T, VEC, 4, CPL>), dim3(gx, (unsigned)runs), block, 0, st, X, M, K, ldx, c0, part, hdiag);
         else hipLaunchKernelGGL((k_colsum<T, VEC, 0, CPL>), dim3(gx, (unsigned)n), block, 0, st, X, M, K, ldx, c0, part, hdiag);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const unsigned gk = (unsigned)ceil_div(K, 64);
-        const int init = c0 == 0, fin = c0 + n >= nch;
-        if (score_mode) hipLaunchKernelGGL((k_combine<true>), dim3(gk), dim3(64), 0, st, part, n, K, E, hdiag, result, init, fin);
-        else hipLaunchKernelGGL((k_combine<false>), dim3(gk), dim3(64), 0, st, part, n, K, result, hdiag, result, init, fin);
+        if (score_mode) hipLaunchKernelGGL((k_combine<true, 1>), dim3(gk), dim3(64), 0, st, part, n, K, E, hdiag, result, init, fin);
+        else if (by_run) hipLaunchKernelGGL((k_combine<false, 1>), dim3(gk), dim3(64), 0, st, part, runs, K, result, hdiag, result, init, fin);
+        else hipLaunchKernelGGL((k_combine<false, (int)kRunChunks>), dim3(gk), dim3(64), 0, st, part, n, K, result, hdiag, result, init, fin);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -12,7 +12,8 @@
 namespace mxs {
 
 constexpr int64_t kChunkRows = 256;        // rows per ordered partial sum
-constexpr int64_t kMaxChunksPerLaunch = 65535;
+constexpr int64_t kRunChunks = 16;         // chunks per run of the calibration sum
+constexpr int64_t kMaxChunksPerLaunch = 65520;   // grid.y limit, whole runs
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -118,7 +118,9 @@ size_t mxs_score_workspace(int64_t N, int64_t K);
  * call; later calls add more calibration tokens). Summation order (so that
  * rankings built on it are reproducible bit for bit): rows in chunks of 256;
  * inside a chunk eight partial sums over rows congruent mod 8, combined as
- * ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); chunk totals added in chunk order.
+ * ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); chunks in runs of 16 (4096 rows, the
+ * last run of a call may be short), a run total adding its chunk totals in
+ * chunk order from the first; run totals added to hdiag in run order.
  * Squares are exact in fp64. ws: >= mxs_calibrate_workspace(M, K) bytes of
  * device memory, 256-byte aligned, contents scratch. M = 0 is a no-op.
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K <= 0, K % 32, ldx < K, M < 0),
@@ -134,7 +136,8 @@ mxs_status mxs_calibrate(const void *X, mxs_dtype dtype, int64_t M, int64_t K, i
  *     score[k] = hdiag[k] * sum_n (W[n, k] - Q4(W)[n, k])^2
  * where Q4 is uniform 4-bit MXINT in 32-blocks along K in the original
  * channel order. The residual is exact in fp32, its square exact in fp64,
- * the sum over n follows the order of mxs_calibrate, the product is rounded
+ * the sum over n is taken in chunks as in mxs_calibrate, with the chunk
+ * totals added in chunk order (no runs), from 0; the product is rounded
  * once. W: [N, ldw] of `dtype`; hdiag, score: [K] fp64 device arrays.
  * ws: >= mxs_score_workspace(N, K) bytes. A block holding NaN/Inf yields NaN
  * for its 32 columns.

@@ -111,12 +111,17 @@ double or_dequant_value(int code, uint8_t scale_byte) { return or_dequant(code, 
  *   inside a chunk, partial sum p_i (i = 0..7) adds the rows whose offset in
  *   the chunk is congruent to i mod 8, in increasing row order, from +0;
  *   the chunk total is ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7));
- *   the running total adds chunk totals in chunk order.
+ *   score: the running total adds chunk totals in chunk order;
+ *   calibrate: chunks form runs of 16 consecutive chunks (4096 rows; the
+ *   last run of a call may be short); a run total adds its chunk totals in
+ *   chunk order, starting from the first, and the running total adds run
+ *   totals in run order.
  * All terms are exact squares (of fp32 values or exact fp32 residuals), so
  * only the fp64 additions round.
  */
 #define OR_CHUNK 256
 #define OR_PARTS 8
+#define OR_RUN 16     /* chunks per run of the calibration sum */
 
 static double or_chunk_total(const double p[OR_PARTS])
 {
@@ -131,7 +136,8 @@ static double or_chunk_total(const double p[OR_PARTS])
  * diagonal of the empirical Hessian H = X^T X, so Hdiag[k] = sum_t X[t,k]^2
  * over calibration tokens t. Reading: no 1/T normalisation and no damping.
  * hdiag is accumulated in place, so calibration may arrive in several calls;
- * each call adds its own chunk totals in order.
+ * each call cuts its own rows into chunks and runs (section 2) and adds its
+ * run totals in order.
  */
 int or_calibrate(const float *X, int64_t M, int64_t K, int64_t ldx, double *hdiag)
 {
@@ -139,11 +145,13 @@ int or_calibrate(const float *X, int64_t M, int64_t K, int64_t ldx, double *hdia
     #pragma omp parallel
     {
         double *p = (double *)malloc(sizeof(double) * OR_PARTS * (size_t)K);
+        double *run = (double *)malloc(sizeof(double) * (size_t)K);
         #pragma omp for schedule(static)
         for (int64_t kb = 0; kb < K; kb += 64) {
             int64_t ke = kb + 64 < K ? kb + 64 : K;
             for (int64_t r0 = 0; r0 < M; r0 += OR_CHUNK) {
                 int64_t r1 = r0 + OR_CHUNK < M ? r0 + OR_CHUNK : M;
+                int64_t c = r0 / OR_CHUNK;             /* chunk index within the call */
                 for (int64_t k = kb; k < ke; ++k)
                     for (int i = 0; i < OR_PARTS; ++i) p[i * K + k] = 0.0;
                 for (int64_t t = r0; t < r1; ++t) {
@@ -156,10 +164,13 @@ int or_calibrate(const float *X, int64_t M, int64_t K, int64_t ldx, double *hdia
                 for (int64_t k = kb; k < ke; ++k) {
                     double q[OR_PARTS];
                     for (int i = 0; i < OR_PARTS; ++i) q[i] = p[i * K + k];
-                    hdiag[k] += or_chunk_total(q);
+                    double tot = or_chunk_total(q);
+                    run[k] = c % OR_RUN == 0 ? tot : run[k] + tot;   /* run total */
+                    if (c % OR_RUN == OR_RUN - 1 || r1 == M) hdiag[k] += run[k];
                 }
             }
         }
+        free(run);
         free(p);
     }
     return 0;

@@ -146,8 +146,12 @@ def test_quantize_kv(mx, orc, T, H, D):
 
 # ------------------------------------------------------------ calibrate/score
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("M,K", [(64, 256), (1000, 96), (257, 4096), (8 * 2048, 4096)])
+@pytest.mark.parametrize("M,K", [(64, 256), (1000, 96), (257, 4096), (8 * 2048, 4096), (5000, 2048),
+                                 (30000, 16384)])
 def test_calibrate(mx, orc, dtype, M, K):
+    # 5000 x 2048: 20 chunks, runs of 16 and 4 formed by the combine kernel;
+    # 30000 x 16384: 118 chunks in 8 runs (the last 6 chunks, the last chunk
+    # 48 rows), 8 x 64 = 512 workgroups that each add a whole run
     gains = synth.outlier_gains(K, 3, max(1, K // 1000), max(2, K // 100))
     X = synth.activations(M, K, 1, gains, dtype=dtype, device=DEV)
     h = mx.mxs_calibrate(X)
@@ -168,6 +172,19 @@ def test_calibrate_in_calls_and_strided(mx, orc):
     Xs = base[:, 5:197]                                  # ldx = 200, unaligned start
     assert np.array_equal(mx.mxs_calibrate(Xs).cpu().numpy(), orc.calibrate(np.ascontiguousarray(host(Xs))))
     assert not mx.mxs_calibrate(torch.empty(0, 64, device=DEV)).any()
+
+
+def test_calibrate_runs_onto_nonzero_hdiag(mx, orc):
+    # whole runs per workgroup (30 runs x 32 column groups) added to an Hdiag
+    # that already holds values: each run total is added whole, in run order
+    gains = synth.outlier_gains(8192, 77)
+    X = synth.activations(30 * 4096 - 100, 8192, 78, gains, device=DEV)
+    h0 = np.random.default_rng(79).random(8192) * 1e6
+    h = torch.from_numpy(h0.copy()).to(DEV)
+    mx.mxs_calibrate(X, h)
+    ref = h0.copy()
+    orc.calibrate(host(X), ref)
+    assert np.array_equal(h.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -72,6 +72,29 @@ def test_hdiag_documented_order(orc):
     assert orc.calibrate(X2)[0] == 2.0 ** 54 + 256
 
 
+def test_hdiag_documented_run_order(orc):
+    # One column, 32 chunks (8192 rows). Chunk 0: rows 0 and 8 hold 2^26, so
+    # p0 = 2^52 + 2^52 = 2^53 exactly and chunk total T0 = 2^53 (fp64 ulp 2);
+    # chunks 8..31 hold one 1 each (T = 1), all other entries are 0.
+    # Documented order, runs of 16 chunks: run 0 = 2^53 + 1 (x8, each a tie
+    # to even -> 2^53) = 2^53; run 1 = 16 (exact); Hdiag = 0 + 2^53 + 16.
+    # Chunk totals added one by one give 2^53; runs of 8 give 2^53 + 24,
+    # runs of 32 give 2^53; the exact value is 2^53 + 24.
+    X = np.zeros((32 * 256, 1), np.float32)
+    X[0, 0] = X[8, 0] = 2.0 ** 26
+    X[256 * np.arange(8, 32), 0] = 1.0
+    h = orc.calibrate(X)
+    assert h[0] == 2.0 ** 53 + 16
+    # each call starts its own runs: Hdiag = 2^53 from a first call, then a
+    # second call of 16 chunks holding one 1 each: its run total 16 is added
+    # whole (2^53 + 16); adding its chunk totals one by one would give 2^53
+    h = orc.calibrate(X[:256])
+    X3 = np.zeros((16 * 256, 1), np.float32)
+    X3[256 * np.arange(16), 0] = 1.0
+    orc.calibrate(X3, h)
+    assert h[0] == 2.0 ** 53 + 16
+
+
 def test_hdiag_empty_and_zero(orc):
     h = orc.calibrate(np.zeros((0, 32), np.float32))
     assert not h.any()
