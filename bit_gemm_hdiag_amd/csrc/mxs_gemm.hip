@@ -1379,33 +1379,12 @@ __device__ __forceinline__ uint32_t wide6(uint32_t g) {   // four 6-bit fields -
     return ((g << 2) & 0xFCu) | ((g << 4) & 0xFC00u) | ((g << 6) & 0xFC0000u) | ((g << 8) & 0xFC000000u);
 }
 
-// bytes o..o+7 of a byte string held as 32-bit words p[], reading only the
-// words up to index last (o >> 2 <= last)
-__device__ __forceinline__ uint64_t bytes8(const uint32_t *p, int32_t o, int32_t last) {
-    const int32_t d0 = o >> 2, sh = o & 3;
-    const int32_t i1 = d0 + 1 < last ? d0 + 1 : last, i2 = d0 + 2 < last ? d0 + 2 : last;
-    const uint64_t lo = ((uint64_t)p[i1] << 32) | p[d0];
-    return sh ? (lo >> (8 * sh)) | ((uint64_t)p[i2] << (64 - 8 * sh)) : lo;
-}
-
 struct GemvChunk {
     int32_t cls;    // 8, 6 or 4
     int32_t gb;     // first block (global index)
     int32_t pb;     // first block within its class plane
     int32_t nblk;   // blocks in the chunk
 };
-
-__device__ __forceinline__ GemvChunk gemv_chunk(int32_t gb, int32_t b1, int32_t n8, int32_t h6, int32_t nb) {
-    GemvChunk c;
-    int32_t end;
-    if (gb < n8) { c.cls = 8; c.pb = gb; end = n8; c.nblk = 4; }
-    else if (gb < h6) { c.cls = 6; c.pb = gb - n8; end = h6; c.nblk = 4; }
-    else { c.cls = 4; c.pb = gb - h6; end = nb; c.nblk = 8; }
-    end = end < b1 ? end : b1;
-    c.gb = gb;
-    c.nblk = gb + c.nblk < end ? c.nblk : end - gb;
-    return c;
-}
 
 // Coalesced fetch of one chunk of codes for 64 rows into registers. Lane
 // roles (row within a group of 8 rows, piece of the row) are fixed; load i
