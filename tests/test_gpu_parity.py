@@ -174,6 +174,18 @@ def test_calibrate_in_calls_and_strided(mx, orc):
     assert not mx.mxs_calibrate(torch.empty(0, 64, device=DEV)).any()
 
 
+def test_calibrate_across_launches(mx, orc):
+    # more chunks than one launch takes (65520 = 4095 whole runs): the first
+    # launch adds whole runs per workgroup, the rest (4 chunks, the last
+    # short) is one run formed by the combine kernel; one column block
+    M = 65520 * 256 + 3 * 256 + 100
+    g = torch.Generator(device=DEV).manual_seed(91)
+    X = torch.randn(M, 32, generator=g, device=DEV).to(torch.bfloat16)
+    h = mx.mxs_calibrate(X)
+    ref = orc.calibrate(host(X))
+    assert np.array_equal(h.cpu().numpy(), ref)
+
+
 def test_calibrate_runs_onto_nonzero_hdiag(mx, orc):
     # whole runs per workgroup (30 runs x 32 column groups) added to an Hdiag
     # that already holds values: each run total is added whole, in run order
