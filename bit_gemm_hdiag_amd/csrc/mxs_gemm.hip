@@ -712,10 +712,22 @@ __device__ __forceinline__ void a2r_issue(const A2RLanes &D, int st, int nstage,
     for (int blk = 0; blk < kDSB; ++blk) ar[SL][blk] = D.a[(int64_t)(s * kDSB + blk) * 64];
 }
 
+// Split over K (SplitK, blockIdx.y = split): split k takes stages
+// s[k] .. s[k+1] - 1 and writes its fp32 tile sums to part[k][M][N]; a second
+// kernel adds the splits in order. Boundaries inside the wide run are
+// multiples of the ring's five slots, those after it multiples of a 16-unit
+// window (8 stages), so every split enters the narrow loop at slot 0 and no
+// window straddles two splits.
+struct SplitK {
+    int32_t n;        // splits (1: no split, the tile sums go to Y)
+    int32_t s[9];     // stage bounds, s[0] = 0, s[n] = all stages
+};
+constexpr int kMaxSplitK = 8;
+
 __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     const int8_t *__restrict__ Af, const float *__restrict__ csA, const int8_t *__restrict__ Wq,
     const float *__restrict__ csW, int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Kp,
-    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy, int32_t gm) {
+    int32_t nb, Segs S, float *__restrict__ Y, int64_t ldy, int32_t gm, SplitK SK, float *__restrict__ part) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
@@ -730,9 +742,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     const int64_t gsz = tilesM - first_m < gm ? tilesM - first_m : gm;
     const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
     const int64_t m0 = tm * kGBM, n0 = tn * kGBN;
-    const int nstage = (nb + kDSB - 1) / kDSB;
     const int64_t nbp = Kp / 32;
     const int hw = __builtin_amdgcn_readfirstlane(S.hw);   // wide blocks = wide stages
+    // this split's stages s0 .. nstage - 1 and units .. ub - 1; the wide loop
+    // ends at wend, where the narrow loop starts
+    const int s0 = __builtin_amdgcn_readfirstlane(SK.s[blockIdx.y]);
+    const int nstage = __builtin_amdgcn_readfirstlane(SK.s[blockIdx.y + 1]);
+    const int ub = min(nb, kDSB * nstage);
+    const int wend = min(max(hw, s0), nstage);
 
     // DMA roles: W rows 16 wave .. +15; waves 0, 1: A scales of block 0 / 1;
     // wave 2: W scales
@@ -823,10 +840,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) nw[j] = *reinterpret_cast<const v4i *>(sbase + (fbW[j] ^ ((blk + 1) << 5)));
             }
-            if (b >= nb) break;
+            if (b >= ub) break;
             const int off = b - 2 * hw;   // narrow windows start after the wide units
             const bool first = (off % kG) == 0;
-            const bool last = (off % kG) == kG - 1 || b == nb - 1;
+            const bool last = (off % kG) == kG - 1 || b == ub - 1;
             if (first) {
                 const float va = sCA[blk * kGBM + 32 * wave + l32];
                 const float vw0 = sCW[blk * kGBN + lane], vw1 = sCW[blk * kGBN + 64 + lane];
@@ -877,7 +894,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
     // allocator spill)
 #define MXS_WSTEP(s_, CUR, NXT)                                                               \
     do {                                                                                      \
-        if ((s_) >= hw) goto narrow;                                                          \
+        if ((s_) >= wend) goto narrow;                                                        \
         MXS_WAIT_ISSUE(s_, NXT);                                                              \
         compute_wide(aslot<CUR>(), ar[CUR]);                                                  \
     } while (0)
@@ -888,11 +905,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
         compute((s_), aslot<CUR>(), ar[CUR]);                                                 \
     } while (0)
 
-    a2r_issue<0>(D, 0, nstage, has_c, ar);
-    a2r_issue<1>(D, 1, nstage, has_c, ar);
-    a2r_issue<2>(D, 2, nstage, has_c, ar);
-    a2r_issue<3>(D, 3, nstage, has_c, ar);
-    for (int s = 0;; s += 5) {
+    a2r_issue<0>(D, s0, nstage, has_c, ar);
+    a2r_issue<1>(D, s0 + 1, nstage, has_c, ar);
+    a2r_issue<2>(D, s0 + 2, nstage, has_c, ar);
+    a2r_issue<3>(D, s0 + 3, nstage, has_c, ar);
+    for (int s = s0;; s += 5) {
         MXS_WSTEP(s, 0, 4);
         MXS_WSTEP(s + 1, 1, 0);
         MXS_WSTEP(s + 2, 2, 1);
@@ -900,7 +917,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_a2r(
         MXS_WSTEP(s + 4, 4, 3);
     }
 narrow:
-    for (int s = hw;; s += 5) {
+    for (int s = wend;; s += 5) {
         MXS_ASTEP(s, 0, 4);
         MXS_ASTEP(s + 1, 1, 0);
         MXS_ASTEP(s + 2, 2, 1);
@@ -927,6 +944,12 @@ done:
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
+    float *out = Y;
+    int64_t ldo = ldy;
+    if (SK.n > 1) {   // this split's sums into part[split][M][N]
+        out = part + (int64_t)blockIdx.y * M * N;
+        ldo = N;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + j * 32 + l32;
@@ -936,7 +959,7 @@ done:
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + 32 * wave + 8 * q + 4 * h + r;
-                if (row < M) Y[row * ldy + col] = acc[j][4 * q + r];
+                if (row < M) out[row * ldo + col] = acc[j][4 * q + r];
             }
     }
 }
@@ -2068,7 +2091,34 @@ struct PrepLayout {
     size_t a_codes, a_cs, a_bytes;   // offsets inside A's part
     size_t w_codes, w_cs, w_bytes;   // offsets inside W's part
     size_t total;                    // both parts
+    SplitK sk;                       // split of the product over K
+    size_t part_bytes;               // its fp32 partial sums (after the operands)
 };
+
+// Shapes with fewer tiles than CUs split the product over K into about
+// 256 / tiles parts of equal stage counts, boundaries rounded to the
+// nearest allowed stage (a multiple of 5 up to the wide run's end, the wide
+// run's end plus a multiple of 8 after it).
+SplitK split_k(int64_t ntiles, int32_t nq, int32_t hw) {
+    SplitK k;
+    const int32_t nstage = (nq + kDSB - 1) / kDSB;
+    int64_t want = ntiles <= 0 || ntiles >= 256 ? 1 : 256 / ntiles;   // no tiles (W only): no split
+    if (want > kMaxSplitK) want = kMaxSplitK;
+    k.n = 0;
+    k.s[0] = 0;
+    for (int64_t i = 1; i < want; ++i) {
+        const int32_t t = (int32_t)((int64_t)nstage * i / want);
+        int32_t b;
+        // (a wide run whose length is not a multiple of 5 has no narrow
+        // stages after it, so its splits never enter the narrow loop)
+        if (t <= hw) b = (hw % 5 == 0) ? (t + 2) / 5 * 5 : t / 5 * 5;
+        else b = hw + (t - hw + 4) / 8 * 8;
+        if (b <= k.s[k.n] || b >= nstage) continue;
+        k.s[++k.n] = b;
+    }
+    k.s[++k.n] = nstage;
+    return k;
+}
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -2085,6 +2135,8 @@ PrepLayout prep_layout(int64_t M, int64_t N, const Segs &S) {
     L.w_cs = align256((size_t)L.Np * L.Kp);
     L.w_bytes = L.w_cs + align256((size_t)nbp * L.Np * 4);
     L.total = L.a_bytes + L.w_bytes;
+    L.sk = split_k((L.Mp / kGBM) * (L.Np / kGBN), S.nq, S.hw);
+    L.part_bytes = L.sk.n > 1 ? align256((size_t)L.sk.n * M * N * sizeof(float)) : 0;
     return L;
 }
 
@@ -2106,12 +2158,16 @@ hipError_t launch_prep_w(const mxs_qmat &W, const PrepLayout &L, const Segs &S, 
 // The int8 prefill product over prepared operands at ap (A's part) and wp
 // (W's part).
 hipError_t launch_a2r(const PrepLayout &L, const Segs &S, int64_t M, int64_t N, const uint8_t *ap,
-                      const uint8_t *wp, float *Y, int64_t ldy, hipStream_t st) {
+                      const uint8_t *wp, float *Y, int64_t ldy, float *part, hipStream_t st) {
     const int64_t ntiles = (L.Mp / kGBM) * (L.Np / kGBN);
-    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles), dim3(512), 0, st,
+    hipLaunchKernelGGL(k_gemm_a2r, dim3((unsigned)ntiles, (unsigned)L.sk.n), dim3(512), 0, st,
                        reinterpret_cast<const int8_t *>(ap + L.a_codes), reinterpret_cast<const float *>(ap + L.a_cs),
                        reinterpret_cast<const int8_t *>(wp + L.w_codes), reinterpret_cast<const float *>(wp + L.w_cs),
-                       M, N, L.Mp, L.Np, L.Kp, S.nq, S, Y, ldy, tile_group(ntiles));
+                       M, N, L.Mp, L.Np, L.Kp, S.nq, S, Y, ldy, tile_group(ntiles), L.sk, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || L.sk.n == 1) return e;
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st, part,
+                       (int32_t)L.sk.n, (int32_t)M, N, Y, ldy);
     return hipGetLastError();
 }
 
@@ -2268,7 +2324,7 @@ size_t gemm_workspace(const mxs_qmat &A, const mxs_qmat &W, bool w_prepared) {
     if (use_gemv(A, W)) return decode_workspace(A, W);
     if (!use_prefill(A)) return 0;
     const PrepLayout L = prep_layout(A.rows, W.rows, segs_of(A));
-    return w_prepared ? L.a_bytes : L.total;
+    return (w_prepared ? L.a_bytes : L.total) + L.part_bytes;
 }
 
 size_t wprep_bytes(const mxs_qmat &W) {
@@ -2314,7 +2370,8 @@ hipError_t launch_mixed_gemm(const mxs_qmat &A, const mxs_qmat &W, const void *w
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_a2r(L, S, M, N, ap, wp, Y, ldy, st);
+    float *part = reinterpret_cast<float *>(ap + (wprep ? L.a_bytes : L.total));
+    return launch_a2r(L, S, M, N, ap, wp, Y, ldy, part, st);
 }
 
 
@@ -2410,7 +2467,7 @@ size_t gemm_fused_workspace(int64_t M, mxs_dtype dt, const mxs_qmat &W, bool w_p
     const mxs_qmat A = act_shape(M, W);
     if (fused_prefill(M, W.K, dt) && !use_gemv(A, W)) {
         const PrepLayout L = prep_layout(M, W.rows, segs_of(A));
-        return w_prepared ? L.a_bytes : L.total;
+        return (w_prepared ? L.a_bytes : L.total) + L.part_bytes;
     }
     return act_planes(A).total + gemm_workspace(A, W, w_prepared);
 }
@@ -2448,7 +2505,8 @@ hipError_t launch_mixed_gemm_fused(const void *X, mxs_dtype dt, int64_t M, int64
         if (e != hipSuccess) return e;
         wp = base + L.a_bytes;
     }
-    return launch_a2r(L, S, M, N, base, wp, Y, ldy, st);
+    float *part = reinterpret_cast<float *>(base + (wprep ? L.a_bytes : L.total));
+    return launch_a2r(L, S, M, N, base, wp, Y, ldy, part, st);
 }
 
 hipError_t launch_mixed_gemm_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy,

@@ -260,7 +260,10 @@ size_t mxs_mixed_gemm_workspace(const mxs_qmat *A, const mxs_qmat *W);
  * Each block's dot product is exact (from 64 tokens on: int8 MFMA with
  * int32 sums for the 4-bit blocks, exact bf16 products for the 8- and 6-bit
  * blocks; below: int32 sums); the terms are combined in fp32 (error ~
- * sqrt(K/32) ulp relative to sum |A||W|). Y: [M, ldy] fp32 device output, ldy >= N.
+ * sqrt(K/32) ulp relative to sum |A||W|). Products with fewer than 256
+ * output tiles of 256 x 128 split K into up to 8 ranges whose fp32 sums,
+ * kept in the workspace, are added in range order.
+ * Y: [M, ldy] fp32 device output, ldy >= N.
  * ws: >= mxs_mixed_gemm_workspace(A, W) bytes (NULL if that is 0).
  * Errors: MXS_ERR_ARG, MXS_ERR_SHAPE (K or block counts differ, ldy < N),
  * MXS_ERR_UNSUPPORTED (plane pointers or strides not 16/4/8-byte aligned
