@@ -13,7 +13,8 @@
 // whose partial counts are added with integer atomics (order-independent). The
 // perm output buffer holds the ranks until the last kernel overwrites it.
 // (A one-workgroup bitonic sort in LDS measured 54 us at K = 4096, against
-// 15 us for these three launches; 23 us at K = 8192, 97 us at K = 28672.)
+// 11.5 us for these three launches; they take 20 us at K = 8192 and 88 us at
+// K = 28672, and about 11 us of launch latency at any K.)
 #include "mxs_device.h"
 #include "mxs_internal.h"
 
@@ -139,42 +140,58 @@ __global__ __launch_bounds__(kScanThreads) void k_perm(const uint8_t *__restrict
 
 // One workgroup, K <= kPermLdsMaxK: ranks (held in the perm buffer) are read
 // into LDS, turned into the bit map, and the stable partition 8 -> 6 -> 4
-// overwrites the perm buffer.
-__global__ __launch_bounds__(kScanThreads) void k_class_perm(int32_t *__restrict__ perm, int64_t K, int32_t c8,
+// overwrites the perm buffer. Wave w owns one contiguous segment of columns
+// (a multiple of 64). A first walk counts the segment's 8- and 6-bit columns
+// with ballots; a column's place is then its class's base, plus the columns
+// of that class in the segments before (the wave counts) and in the
+// segment before it (running ballot counts and the prefix of the lanes below).
+__global__ __launch_bounds__(kScanThreads) void k_class_perm(int32_t *__restrict__ perm, int32_t K, int32_t c8,
                                                              int32_t c6, uint8_t *__restrict__ bits) {
+    constexpr int NW = kScanThreads / 64;
     extern __shared__ int32_t s_rank[];
-    __shared__ int32_t cnt[3][kScanThreads];
-    const int t = threadIdx.x;
-    for (int64_t k = t; k < K; k += kScanThreads) s_rank[k] = perm[k];
+    __shared__ int32_t wcnt[2][NW];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    for (int k = t; k < K; k += kScanThreads) s_rank[k] = perm[k];
     __syncthreads();
-    const int64_t per = (K + kScanThreads - 1) / kScanThreads;
-    const int64_t k0 = t * per;
-    const int64_t k1 = k0 + per < K ? k0 + per : K;
-    int32_t c[3] = {0, 0, 0};
-    for (int64_t k = k0; k < k1; ++k) {
-        const int32_t r = s_rank[k];
-        const int i = r < c8 ? 0 : (r < c8 + c6 ? 1 : 2);
-        bits[k] = (uint8_t)(i == 0 ? 8 : (i == 1 ? 6 : 4));
-        c[i]++;
+    const int seg = (K + NW * 64 - 1) / (NW * 64) * 64;
+    const int k0 = w * seg < K ? w * seg : K;
+    const int k1 = k0 + seg < K ? k0 + seg : K;
+    const int32_t c86 = c8 + c6;
+    int32_t n8 = 0, n6 = 0;
+    for (int kb = k0; kb < k1; kb += 64) {
+        const int k = kb + lane;
+        const int32_t r = k < k1 ? s_rank[k] : INT32_MAX;   // past the end: no class
+        n8 += __popcll(__ballot(r < c8));
+        n6 += __popcll(__ballot(r >= c8 && r < c86));
     }
-    for (int i = 0; i < 3; ++i) cnt[i][t] = c[i];
+    if (lane == 0) {
+        wcnt[0][w] = n8;
+        wcnt[1][w] = n6;
+    }
     __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        int32_t v[3];
-        for (int i = 0; i < 3; ++i) v[i] = t >= off ? cnt[i][t - off] : 0;
-        __syncthreads();
-        for (int i = 0; i < 3; ++i) cnt[i][t] += v[i];
-        __syncthreads();
+    int32_t p8 = 0, p6 = 0;
+    for (int v = 0; v < w; ++v) {
+        p8 += wcnt[0][v];
+        p6 += wcnt[1][v];
     }
-    int32_t pos[3];
-    pos[0] = cnt[0][t] - c[0];
-    pos[1] = c8 + cnt[1][t] - c[1];
-    pos[2] = c8 + c6 + cnt[2][t] - c[2];
-    for (int64_t k = k0; k < k1; ++k) {
-        const int32_t r = s_rank[k];
-        const int i = r < c8 ? 0 : (r < c8 + c6 ? 1 : 2);
-        const int32_t at = pos[i]++;
-        if (at < K) perm[at] = (int32_t)k;   // always true when ranks are a permutation
+    int32_t p4 = c86 + (k0 - p8 - p6);   // 4-bit columns before the segment
+    p6 += c8;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int kb = k0; kb < k1; kb += 64) {
+        const int k = kb + lane;
+        const bool in = k < k1;
+        const int32_t r = in ? s_rank[k] : INT32_MAX;
+        const bool is8 = r < c8, is6 = !is8 && r < c86;
+        const uint64_t m8 = __ballot(is8), m6 = __ballot(is6), m4 = __ballot(in && !is8 && !is6);
+        if (in) {
+            const int32_t at = is8 ? p8 + __popcll(m8 & below)
+                                   : (is6 ? p6 + __popcll(m6 & below) : p4 + __popcll(m4 & below));
+            bits[k] = (uint8_t)(is8 ? 8 : (is6 ? 6 : 4));
+            if (at < K) perm[at] = k;   // always true when ranks are a permutation
+        }
+        p8 += __popcll(m8);
+        p6 += __popcll(m6);
+        p4 += __popcll(m4);
     }
 }
 
@@ -209,7 +226,8 @@ hipError_t launch_allocate(const double *score, int64_t K, int32_t c8, int32_t c
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_class_perm),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kPermLdsMaxK * 4));
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_class_perm, dim3(1), dim3(kScanThreads), (size_t)(K * 4), st, perm, K, c8, c6, bits);
+        hipLaunchKernelGGL(k_class_perm, dim3(1), dim3(kScanThreads), (size_t)(K * 4), st, perm, (int32_t)K, c8,
+                           c6, bits);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_class, dim3(gk), dim3(256), 0, st, perm, K, c8, c6, bits);
