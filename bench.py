@@ -12,9 +12,13 @@ MXINT4 quantisation of K and V (2048 tokens x 8 heads x 128).
 Prints one JSON line. `value` is the block's GEMM work (2 M N K summed over
 the seven layers) over the block step time, in TOPS, with mxs_mixed_gemm
 (int8 block sums for the 4-bit blocks, exact bf16 products for the 8- and
-6-bit blocks); `stages` gives every stage's time per step, GB/s (and
+6-bit blocks). The step is timed twice: eagerly (every call from Python,
+`eager`) and as one HIP graph of the step's calls, captured once and
+replayed (`graph`); `value` and `ms_per_step` are the replay's when every
+output of the replayed step equals the eager step's bit for bit, else the
+eager step's. `stages` gives every stage's time per step, GB/s (and
 TOPS) and fraction of its peak, from HIP events around every call on the
-library's stream in the timed steps; `roofline` is for the stage with the
+library's stream in the eager steps; `roofline` is for the stage with the
 largest share of the step, `roofline_gemm` and `roofline_calibrate` for the
 GEMM and calibration calls; `variant_mx`, `variant_fused` and
 `variant_prepared` repeat the step with mxs_mixed_gemm_mx (fp6 block-scaled
@@ -572,6 +576,42 @@ def run_block_steps(torch, calls, steps, warmup):
     return step_s, stages
 
 
+def run_block_graph(torch, calls, steps, warmup):
+    """The same step captured once in a HIP graph and replayed: `warmup`
+    untimed replays, then `steps` timed replays between two
+    synchronisations. Every replay launches every kernel of the step; what
+    it drops is the host's per-call work (Python, argument marshalling,
+    launch calls), which leaves the GPU idle between short kernels."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, _, fn, _ in calls:
+            fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    step_s = s.elapsed_time(e) / steps * 1e-3
+    del g
+    return step_s
+
+
+def block_outputs(w):
+    """Copies of everything a block step writes (Hdiag, scores, bit maps,
+    permutations, planes, Y, K/V codes and scales)."""
+    out = [I["hdiag"].clone() for I in w["inputs"].values()]
+    for L in w["layers"]:
+        out += [L["score"].clone(), L["bits"].clone(), L["perm"].clone(), L["Y"].clone()]
+        for q in (L["Wq"], L["Aq"]):
+            out += [t.clone() for t in (q.q8, q.q6, q.q4, q.sc) if t is not None]
+    return out + [w["kvc"].clone(), w["kvs"].clone()]
+
+
 def run_block_steps_concurrent(torch, calls, w, steps, warmup):
     """The same step with two streams (default priority): the four
     calibrations run in order on one, each layer's score, allocate,
@@ -866,8 +906,15 @@ def block_line(mx, synth, torch, args):
     M = w["M"]
     gemm_ops = sum(2 * M * L["N"] * L["K"] for L in w["layers"])
     log(f"warmup {args.warmup}, timing {args.steps} block steps")
-    step_s, stages = run_block_steps(torch, block_calls(mx, w, args.block_variant), args.steps, args.warmup)
-    log(f"block step {step_s * 1e3:.3f} ms")
+    calls = block_calls(mx, w, args.block_variant)
+    eager_s, stages = run_block_steps(torch, calls, args.steps, args.warmup)
+    log(f"block step {eager_s * 1e3:.3f} ms (eager)")
+    ref = block_outputs(w)
+    graph_s = run_block_graph(torch, calls, args.steps, args.warmup)
+    same = all(torch.equal(a, b) for a, b in zip(ref, block_outputs(w)))
+    del ref
+    log(f"block step {graph_s * 1e3:.3f} ms (graph replay, outputs equal to the eager step: {same})")
+    step_s = graph_s if same else eager_s
     dominant = max(stages, key=lambda k: stages[k]["s"])
     out = {
         "metric": "mixed MXINT GEMM TOPS & quantize GB/s, % of MI355X roofline (1 GPU)",
@@ -888,8 +935,11 @@ def block_line(mx, synth, torch, args):
                                "8/6/4-bit), quantize X and mixed GEMM at M=2048 for all 7, MXINT4 K and V "
                                "2048x8x128; one step = one block",
                    "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)",
-                   "pipeline_80_layers_s": step_s * 80, "gemm_variant": args.block_variant or "mxs_mixed_gemm"},
+                   "pipeline_80_layers_s": step_s * 80, "gemm_variant": args.block_variant or "mxs_mixed_gemm",
+                   "launch": "the step's calls captured once in a HIP graph and replayed" if same else "eager"},
         "gemm_ops_per_step": gemm_ops,
+        "eager": dict(value=gemm_ops / eager_s / 1e12, ms_per_step=eager_s * 1e3),
+        "graph": dict(value=gemm_ops / graph_s / 1e12, ms_per_step=graph_s * 1e3, outputs_equal_eager=same),
         "stages": stage_summary(stages),
         "roofline": roofline_of(dominant, stages[dominant]),
         "roofline_gemm": roofline_of("mixed_gemm", stages["mixed_gemm"], prepared=args.block_variant == "prepared"),
