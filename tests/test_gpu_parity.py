@@ -267,6 +267,17 @@ def test_mixed_gemm(mx, orc, M, N, K, budget, entry):
     gemm_case(mx, orc, M, N, K, budget, seed=M * 7 + N, entry=entry)
 
 
+# Prefill products with fewer than 256 tiles of 256 x 128 split K into up to
+# 8 ranges whose fp32 sums are added in range order: 8 and 32 tiles (8
+# ranges; 256 x 1024 x 8192 is the 70B k/v shape at 256 tokens), 64 tiles (4
+# ranges), 128 tiles (2 ranges). Rows sampled across every row tile.
+@pytest.mark.parametrize("M,N,K", [(256, 1024, 8192), (300, 2048, 8192), (64, 8192, 8192), (512, 4096, 4096),
+                                   (2048, 2048, 4096)])
+def test_mixed_gemm_split_k(mx, orc, M, N, K):
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 12)), [M - 1]]))
+    gemm_case(mx, orc, M, N, K, (500, 1500), seed=M + N + K, sample_rows=rows)
+
+
 @pytest.mark.parametrize("M,N,K,budget", [(1, 65, 32, (0, 0)), (2, 130, 512, (10000, 0)), (3, 64, 352, (0, 10000)),
                                           (4, 200, 480, (3100, 4000)), (4, 1000, 4096, (500, 1500)),
                                           (2, 77, 1056, (300, 1000)), (1, 129, 800, (800, 2000)),

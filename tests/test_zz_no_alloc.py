@@ -27,8 +27,10 @@ def test_noalloc_matches_mixed_gemm_twice_then_smaller():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import bit_gemm_hdiag_amd as mx
     # prefill 2048 x 4096 x 4096 (prepared operands in the scratch array), then
-    # decode 8 tokens of the same K (partial rows in the scratch array)
-    for M, N, K, seed in ((2048, 4096, 4096, 8100), (8, 3000, 4096, 8200)):
+    # prefill 256 x 1024 x 8192 (8 tiles, K split into 8 ranges: the ranges'
+    # fp32 sums also in the scratch array), then decode 8 tokens (partial rows
+    # in the scratch array)
+    for M, N, K, seed in ((2048, 4096, 4096, 8100), (256, 1024, 8192, 8300), (8, 3000, 4096, 8200)):
         print(f"noalloc M={M} N={N} K={K}", flush=True)
         A, B = operands(mx, M, N, K, seed)
         need = mx.mxs_mixed_gemm_workspace(A, B)
