@@ -1015,19 +1015,21 @@ __device__ __forceinline__ int lds_i32(uint32_t a) { return *reinterpret_cast<ld
 //                rows of k-half 0 and then those of k-half 1;
 //   bytes 6144..6399: four scale bytes per row, byte 2j + h.
 // Rows past the matrix hold zero codes and zero scale bytes.
-constexpr int kXBM = 256, kXBN = 128;    // workgroup tile (A rows x W rows)
+constexpr int kXBM = 256, kXBN = 256;    // workgroup tile (A rows x W rows)
 constexpr int kXCode = 6144;             // code bytes of a (group, stage) record
 constexpr int kXRec = kXCode + 256;      // record bytes
-constexpr int kXGroups = kXBM / 64 + kXBN / 64;
-// LDS image of one stage of the workgroup tile: the code parts of the six
-// group records (A groups 0..3, W groups 0..1), then the A scale parts, the
-// W scale parts, and 1.5 KiB that only absorbs the copies that keep every
-// wave's load count equal (see xdma_issue)
-constexpr int kXScA = kXGroups * kXCode;        // 36864
-constexpr int kXScW = kXScA + (kXBM / 64) * 256; // 37888
-constexpr int kXSink = kXScW + 512;             // 38400
-constexpr int kXSlot = kXSink + 1536;           // 39936
-constexpr int kXLoads = 5;                      // loads per wave and stage
+constexpr int kXGA = kXBM / 64, kXGW = kXBN / 64;
+constexpr int kXGroups = kXGA + kXGW;
+// LDS image of one stage of the workgroup tile: the code parts of the eight
+// group records (A groups 0..3, W groups 0..3), then the A scale parts and
+// the W scale parts
+constexpr int kXScA = kXGroups * kXCode;        // 49152
+constexpr int kXScW = kXScA + kXGA * 256;       // 50176
+constexpr int kXSink = kXScW + kXGW * 256;      // 51200: 1 KiB that absorbs the two padding loads
+constexpr int kXSlot = kXSink + 1024;           // 52224
+constexpr int kXRing = 3;                       // stage slots
+constexpr int kXLoads = 13;                     // loads per wave and stage
+static_assert(6 * kXGroups + 2 == 4 * kXLoads - 2, "50 loads per stage over four waves, plus two into the sink");
 
 struct XPlan {
     int32_t p8, p6, p4;   // block pairs per width class
@@ -1178,23 +1180,26 @@ __global__ __launch_bounds__(256) void k_mx_prep(QView A, QView W, int64_t M, in
     rec[kXCode + rho * 4 + q] = (int8_t)sb;
 }
 
-// the ring of four stage slots
-__shared__ __attribute__((aligned(16))) int8_t g_xring[4 * kXSlot];
+// A stage of the workgroup tile in LDS: the code parts of the eight group
+// records (A groups 0..3, W groups 0..3), then the four A and the four W
+// scale parts, and a 1 KiB sink. Ring of three stage slots (153 KiB of the
+// CU's 160 KiB).
+__shared__ __attribute__((aligned(16))) int8_t g_xring[kXRing * kXSlot];
 
-// A stage is 40 loads of 1 KiB, straight from global memory into LDS, five
-// per wave (no branch, and the same wait count in every wave): load L =
-// 5 wave + k is code chunk L mod 6 of group L / 6 for L < 36; load 36 the
-// scale parts of the four A groups (16 lanes each); load 37 those of the two
-// W groups (lanes 32..63 repeat lanes 0..31 into the sink); loads 38, 39
-// repeat load 37 into the sink. Every source advances by one record per
-// stage.
+// A stage is 50 loads of 1 KiB, straight from global memory into LDS: load
+// L < 48 is code chunk L mod 6 of group L / 6; load 48 the scale parts of
+// the four A groups (16 lanes each), load 49 those of the four W groups.
+// Wave w issues loads w, w + 4, w + 8, ..., 13 per wave: loads 50 and 51
+// (the last of waves 2 and 3) repeat the wave's first load into the slot's sink,
+// so that every wave has the same count and no branch. Every source
+// advances by one record per stage.
 struct XDma {
     const int8_t *src[kXLoads];   // this lane's source at stage 0
     uint32_t lds[kXLoads];        // wave-uniform LDS offset in the slot
 };
 
-__device__ __forceinline__ void xdma_issue(const XDma &D, uint32_t slot, int st, int ns) {
-    const int s = st < ns ? st : ns - 1;   // past the end: reload the last stage
+__device__ __forceinline__ void xdma_issue(const XDma &D, uint32_t slot, int st, int s_end) {
+    const int s = st < s_end ? st : s_end - 1;   // past the end: reload the last stage
     const int64_t o = (int64_t)s * kXRec;
 #pragma unroll
     for (int k = 0; k < kXLoads; ++k) dma16(D.src[k] + o, slot + D.lds[k]);
@@ -1205,18 +1210,24 @@ typedef __attribute__((address_space(3))) const v2i lds_v2i_t;
 __device__ __forceinline__ v2i lds_v2(uint32_t a) { return *reinterpret_cast<lds_v2i_t *>((uintptr_t)a); }
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// Workgroup: 8 waves (4 x 2), tile 256 x 128; each wave owns 64 x 64 outputs
-// as 2 x 2 MFMA tiles, i.e. one 64-row A group and one 64-row W group. Both
-// operands reach LDS by DMA, through a ring of four stage slots. The fp6
-// matrix cores outrun the LDS here: a 4-bit step reads 6 KiB of fragments
-// per wave for 4 MFMAs, so the 4-bit stages are bound by LDS reads and the
-// 6/8-bit stages (four MFMAs per fragment set) by the matrix cores.
-// (Loading A straight into registers instead, with 4 waves of 64 x 128,
-// halves the LDS reads but measured slower: the vector memory path then
-// carries the same bytes.)
-__global__ __launch_bounds__(512, 1) void k_gemm_mx(const int8_t *__restrict__ PA, const int8_t *__restrict__ PW,
-                                                    int64_t M, int64_t N, int64_t Mp, int64_t Np, XPlan P,
-                                                    float *__restrict__ Y, int64_t ldy) {
+// Split over K for grids of fewer tiles than CUs: split k takes stages
+// s[k] .. s[k+1] - 1 and writes its fp32 tile sums to part[k][M][N], which
+// k_gemv_reduce adds in split order.
+struct XSplit {
+    int32_t n;        // splits (1: the tile sums go to Y)
+    int32_t s[9];     // stage bounds, s[0] = 0, s[n] = all stages
+};
+
+// Workgroup: 4 waves (2 x 2), one per SIMD, tile 256 x 256; each wave owns
+// 128 x 128 outputs as 4 x 4 MFMA tiles (256 fp32 sums per lane, held in
+// the accumulation registers), i.e. two 64-row A groups and two 64-row W
+// groups. Per 64-deep MFMA step a wave reads 8 fragments (12 KiB) for 16
+// MFMAs, half the LDS bytes per MFMA of a 64 x 64 wave tile, and the
+// workgroup fetches 512 operand rows per 65536 outputs instead of 384 per
+// 32768. Both operands reach LDS by DMA.
+__global__ __launch_bounds__(256, 1) void k_gemm_mx(const int8_t *__restrict__ PA, const int8_t *__restrict__ PW,
+                                                    int64_t M, int64_t N, int64_t Mp, int64_t Np, XPlan P, XSplit SK,
+                                                    float *__restrict__ Y, int64_t ldy, float *__restrict__ part) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
@@ -1232,142 +1243,181 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(const int8_t *__restrict__ P
     const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
     const int64_t m0 = tm * kXBM, n0 = tn * kXBN;
     const int ns = P.ns, nd = P.nd;
+    const int s0 = __builtin_amdgcn_readfirstlane(SK.s[blockIdx.y]);
+    const int s1 = __builtin_amdgcn_readfirstlane(SK.s[blockIdx.y + 1]);
 
     // this lane's DMA sources and the wave's LDS destinations
     XDma D;
     {
         auto rec = [&](int g) -> const int8_t * {   // group record g of the tile at stage 0
-            return g < kXBM / 64 ? PA + ((m0 / 64 + g) * ns) * (int64_t)kXRec
-                                 : PW + ((n0 / 64 + (g - kXBM / 64)) * ns) * (int64_t)kXRec;
+            return g < kXGA ? PA + ((m0 / 64 + g) * ns) * (int64_t)kXRec
+                            : PW + ((n0 / 64 + (g - kXGA)) * ns) * (int64_t)kXRec;
         };
 #pragma unroll
         for (int k = 0; k < kXLoads; ++k) {
-            const int L = kXLoads * wave + k;
+            const int L = wave + 4 * k;
             if (L < 6 * kXGroups) {
                 D.src[k] = rec(L / 6) + (L % 6) * 1024 + lane * 16;
                 D.lds[k] = (uint32_t)((L / 6) * kXCode + (L % 6) * 1024);
             } else if (L == 6 * kXGroups) {
                 D.src[k] = rec(lane >> 4) + kXCode + (lane & 15) * 16;
                 D.lds[k] = kXScA;
-            } else {
-                D.src[k] = rec(kXBM / 64 + ((lane >> 4) & 1)) + kXCode + (lane & 15) * 16;
-                D.lds[k] = L == 6 * kXGroups + 1 ? kXScW : kXSink + 512;
+            } else if (L == 6 * kXGroups + 1) {
+                D.src[k] = rec(kXGA + ((lane >> 4) & 3)) + kXCode + (lane & 15) * 16;
+                D.lds[k] = kXScW;
+            } else {   // loads 50, 51: a copy of load 0 of this wave into the sink
+                D.src[k] = D.src[0];
+                D.lds[k] = kXSink;
             }
         }
     }
 
     // LDS byte offsets (inside a slot) of this lane's pieces of fragment 0,
-    // step 0 (16-byte piece, 8-byte piece, scale dword); fragment i adds 512
-    // / 256 / 128 bytes, step j adds 3072 / 3072 / 0. Addresses are formed as
-    // slot base + lane offset + immediate, so one register per piece kind
-    // serves every slot and step.
-    const uint32_t ca = (uint32_t)(wm * kXCode), cw = (uint32_t)((kXBM / 64 + wn) * kXCode);
-    const uint32_t sa0 = (uint32_t)(kXScA + wm * 256), sw0 = (uint32_t)(kXScW + wn * 256);
+    // step 0 (16-byte piece, 8-byte piece, scale dword). A fragment f (0..3)
+    // is group 2 wm + f / 2, rows 32 (f % 2) .. + 31 of it; W likewise with
+    // wn; step j adds 3072 bytes to the code pieces.
+    const uint32_t ca = (uint32_t)(2 * wm * kXCode), cw = (uint32_t)((kXGA + 2 * wn) * kXCode);
+    const uint32_t sa0 = (uint32_t)(kXScA + wm * 512), sw0 = (uint32_t)(kXScW + wn * 512);
     const uint32_t lq = (uint32_t)(h * 1024 + l32 * 16), ld = (uint32_t)(2048 + h * 512 + l32 * 8),
                    ls = (uint32_t)(l32 * 4);
+    auto foff_q = [](int f) { return (uint32_t)((f >> 1) * kXCode + (f & 1) * 512); };
+    auto foff_d = [](int f) { return (uint32_t)((f >> 1) * kXCode + (f & 1) * 256); };
 
-    v16f acc[2][2];
+    v16f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jw = 0; jw < 2; ++jw)
+        for (int jw = 0; jw < 4; ++jw)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][jw][e] = 0.f;
 
     // the fragments and scale bytes of one MFMA step (A rows, W rows)
     struct Frags {
-        v8i a[2], w[2];
-        int sa[2], sw[2];
+        v8i a[4], w[4];
+        int sa[4], sw[4];
     };
-    // scale bytes: one dword per row holds (step 0, k-half 0/1, step 1, k-half
-    // 0/1); the MFMA reads bits 0..7 of its scale operand, so the lane shifts
-    // its byte (2 j + h) down and leaves the others above it
-    auto read_scales = [&](uint32_t slot, int (&sa)[2], int (&sw)[2]) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            sa[i] = lds_i32(slot + sa0 + ls + i * 128);
-            sw[i] = lds_i32(slot + sw0 + ls + i * 128);
-        }
+    // fragment u of a step (u < 4: A fragment u, else W fragment u - 4):
+    // its 16-byte and 8-byte pieces; scale bytes: one dword per row holds
+    // (step 0, k-half 0/1, step 1, k-half 0/1); the MFMA reads bits 0..7 of
+    // its scale operand, so the lane shifts its byte (2 j + h) down
+    auto read_frag = [&](uint32_t slot, int j, int u, Frags &F) {
+        const uint32_t base = slot + (u < 4 ? ca : cw) + j * 3072;
+        const int f = u & 3;
+        const v4i pq = lds_v4(base + lq + foff_q(f));
+        const v2i pd = lds_v2(base + ld + foff_d(f));
+        const v8i x = v8i{pq[0], pq[1], pq[2], pq[3], pd[0], pd[1], 0, 0};
+        if (u < 4) F.a[f] = x;
+        else F.w[f] = x;
     };
-    auto read_step = [&](uint32_t slot, int j, const int (&sa)[2], const int (&sw)[2], Frags &F) {
-        const uint32_t qa = slot + ca + lq, da = slot + ca + ld;
-        const uint32_t qw = slot + cw + lq, dw = slot + cw + ld;
+    auto read_scale = [&](uint32_t slot, int u, int (&sa)[4], int (&sw)[4]) {
+        if (u < 4) sa[u] = lds_i32(slot + sa0 + ls + u * 128);
+        else sw[u - 4] = lds_i32(slot + sw0 + ls + (u - 4) * 128);
+    };
+    auto set_scales = [&](int j, const int (&sa)[4], const int (&sw)[4], Frags &F) {
         const int sh = 16 * j + 8 * h;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const v4i pa = lds_v4(qa + i * 512 + j * 3072), pw = lds_v4(qw + i * 512 + j * 3072);
-            const v2i ra = lds_v2(da + i * 256 + j * 3072), rw = lds_v2(dw + i * 256 + j * 3072);
-            F.a[i] = v8i{pa[0], pa[1], pa[2], pa[3], ra[0], ra[1], 0, 0};
-            F.w[i] = v8i{pw[0], pw[1], pw[2], pw[3], rw[0], rw[1], 0, 0};
-            F.sa[i] = (int)((uint32_t)sa[i] >> sh);
-            F.sw[i] = (int)((uint32_t)sw[i] >> sh);
+        for (int f = 0; f < 4; ++f) {
+            F.sa[f] = (int)((uint32_t)sa[f] >> sh);
+            F.sw[f] = (int)((uint32_t)sw[f] >> sh);
         }
+    };
+    auto mma1 = [&](const Frags &X, const Frags &Z, int k) {   // output tile k: A fragment k / 4, W fragment k % 4
+        const int i = k >> 2, jw = k & 3;
+        acc[i][jw] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(X.a[i], Z.w[jw], acc[i][jw], 2, 2, 0, X.sa[i],
+                                                                    0, Z.sw[jw]);
     };
     auto mma = [&](const Frags &X, const Frags &Z) {   // X: A fragments, Z: W fragments
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jw = 0; jw < 2; ++jw)
-                acc[i][jw] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(X.a[i], Z.w[jw], acc[i][jw], 2, 2, 0,
-                                                                            X.sa[i], 0, Z.sw[jw]);
+        for (int k = 0; k < 16; ++k) mma1(X, Z, k);
     };
 
     // Software pipeline over MFMA steps, two fragment sets (F0: step 0, F1:
-    // step 1 of the current stage). Stage s: read F1; MFMAs that need only
-    // F0 and F1 (single stage: A0 W0; digit stage: hi*hi, hi*lo, lo*hi);
-    // wait for this wave's loads of stage s+1; barrier (all of stage s+1 has
-    // landed, every wave has finished reading stage s); issue stage s+4 into
-    // the slot of stage s; read F0 of stage s+1; the last MFMAs of stage s
-    // (A1 W1, or lo*lo), which overlap those reads. Ring of four slots,
-    // stage k in slot k % 4. After the last stage the reads of the following
-    // slot still run (in bounds, result unused), which keeps the loop free
-    // of branches.
+    // step 1 of the current stage), with the memory instructions spread
+    // between the MFMAs so that the matrix core never waits for a burst of
+    // them (one wave per SIMD: no other wave fills its gaps). Stage s:
+    //   phase 1: the MFMAs that need only F0 (A0 W0, or hi*hi), one F1
+    //            fragment read after each of the first eight; then, on a
+    //            digit stage, hi*lo and lo*hi;
+    //   wait for this wave's loads of stage s+1; barrier (all of stage s+1
+    //   has landed, every wave has finished reading stage s);
+    //   phase 2: the MFMAs of F1 (A1 W1, or lo*lo), with the DMA of stage
+    //            s+3 into the slot of stage s and the reads of stage s+1's
+    //            scales and F0 between them.
+    // Ring of three slots, stage k in slot k % 3. After the last stage the
+    // reads of the following slot still run (in bounds, result unused), which
+    // keeps the loop free of branches.
     const uint32_t ring = lds_addr(g_xring);
+    auto slot_of = [&](int s) { return ring + (uint32_t)((s % kXRing) * kXSlot); };
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xdma_issue(D, ring + k * kXSlot, k, ns);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kXLoads));
+    for (int k = 0; k < kXRing; ++k) xdma_issue(D, slot_of(s0 + k), s0 + k, s1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kXLoads));
     lds_barrier();
     Frags F0, F1;
-    int scA[2], scW[2];   // scale dwords of the current stage
-    read_scales(ring, scA, scW);
-    read_step(ring, 0, scA, scW, F0);
-    auto next = [&](int s) {
-        __builtin_amdgcn_sched_barrier(0);   // the MFMAs above issue before the wait
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kXLoads));
-        lds_barrier();
-        xdma_issue(D, ring + (uint32_t)((s & 3) * kXSlot), s + 4, ns);
-        const uint32_t nxt = ring + (uint32_t)(((s + 1) & 3) * kXSlot);
-        read_scales(nxt, scA, scW);
-        read_step(nxt, 0, scA, scW, F0);
+    int scA[4], scW[4];   // scale dwords of the current stage
+#pragma unroll
+    for (int u = 0; u < 8; ++u) read_scale(slot_of(s0), u, scA, scW);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) read_frag(slot_of(s0), 0, u, F0);
+    set_scales(0, scA, scW, F0);
+
+    auto phase1 = [&](int s) {
+        const uint32_t cur = slot_of(s);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            mma1(F0, F0, k);
+            if (k < 8) read_frag(cur, 1, k, F1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        set_scales(1, scA, scW, F1);
     };
-    int s = 0;
-    for (; s < nd; ++s) {   // digit stages: hi and lo steps of a 6/8-bit pair
-        read_step(ring + (uint32_t)((s & 3) * kXSlot), 1, scA, scW, F1);
-        mma(F0, F0);
+    auto phase2 = [&](int s) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kXLoads));
+        lds_barrier();
+        const uint32_t cur = slot_of(s), nxt = slot_of(s + 1);
+        const int sd = s + kXRing < s1 ? s + kXRing : s1 - 1;   // past the end: reload the last stage
+        const int64_t o = (int64_t)sd * kXRec;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            mma1(F1, F1, k);
+            if (k < kXLoads) dma16(D.src[k] + o, cur + D.lds[k]);
+            if (k < 8) read_scale(nxt, k, scA, scW);
+            else read_frag(nxt, 0, k - 8, F0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        set_scales(0, scA, scW, F0);
+    };
+    int s = s0;
+    const int dend = nd < s1 ? nd : s1;
+    for (; s < dend; ++s) {   // digit stages: hi and lo steps of a 6/8-bit pair
+        phase1(s);
         mma(F0, F1);
         mma(F1, F0);
-        next(s);
-        mma(F1, F1);
+        phase2(s);
     }
-    for (; s < ns; ++s) {   // two 4-bit pairs
-        read_step(ring + (uint32_t)((s & 3) * kXSlot), 1, scA, scW, F1);
-        mma(F0, F0);
-        next(s);
-        mma(F1, F1);
+    for (; s < s1; ++s) {   // two 4-bit pairs
+        phase1(s);
+        phase2(s);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
+    float *out = Y;
+    int64_t ldo = ldy;
+    if (SK.n > 1) {   // this split's sums into part[split][M][N]
+        out = part + (int64_t)blockIdx.y * M * N;
+        ldo = N;
+    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jw = 0; jw < 2; ++jw) {
-            const int64_t col = n0 + wn * 64 + jw * 32 + l32;
+        for (int jw = 0; jw < 4; ++jw) {
+            const int64_t col = n0 + wn * 128 + jw * 32 + l32;
             if (col >= N) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * q + 4 * h + r;
-                    if (row < M) Y[row * ldy + col] = acc[i][jw][4 * q + r];
+                    const int64_t row = m0 + wm * 128 + i * 32 + 8 * q + 4 * h + r;
+                    if (row < M) out[row * ldo + col] = acc[i][jw][4 * q + r];
                 }
         }
 }
@@ -2263,21 +2313,37 @@ hipError_t launch_gemv(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t l
     return launch_gemv_t<8>(A, W, Y, ldy, ws, st);
 }
 
-// Prefill workspace: the two prepared operands, record-aligned.
+// Prefill workspace: the two prepared operands, record-aligned, then the
+// split sums when the product is split over K.
 struct XLayout {
     int64_t Mp, Np;
     XPlan P;
-    size_t a_off, w_off, total;
+    XSplit sk;
+    size_t a_off, w_off, part_off, total;
 };
+
+// Grids of fewer tiles than CUs split the stages into about 256 / tiles
+// parts of equal length (at most kMaxSplitK).
+XSplit mx_split(int64_t ntiles, int32_t ns) {
+    XSplit k;
+    int64_t want = ntiles <= 0 || ntiles >= 256 ? 1 : 256 / ntiles;
+    if (want > kMaxSplitK) want = kMaxSplitK;
+    if (want > ns) want = ns > 0 ? ns : 1;
+    k.n = (int32_t)want;
+    for (int64_t i = 0; i <= want; ++i) k.s[i] = (int32_t)((int64_t)ns * i / want);
+    return k;
+}
 
 XLayout mx_layout(const mxs_qmat &A, const mxs_qmat &W) {
     XLayout L;
     L.Mp = ceil_div(A.rows, kXBM) * kXBM;
     L.Np = ceil_div(W.rows, kXBN) * kXBN;
     L.P = make_xplan(A.n8, A.n6, A.n4);
+    L.sk = mx_split((L.Mp / kXBM) * (L.Np / kXBN), L.P.ns);
     L.a_off = 0;
     L.w_off = align256((size_t)(L.Mp / 64) * (size_t)L.P.ns * kXRec);
-    L.total = L.w_off + (size_t)(L.Np / 64) * (size_t)L.P.ns * kXRec;
+    L.part_off = align256(L.w_off + (size_t)(L.Np / 64) * (size_t)L.P.ns * kXRec);
+    L.total = L.part_off + (L.sk.n > 1 ? (size_t)L.sk.n * (size_t)A.rows * (size_t)W.rows * sizeof(float) : 0);
     return L;
 }
 
@@ -2285,14 +2351,20 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
     const XLayout L = mx_layout(A, W);
     int8_t *pa = static_cast<int8_t *>(ws) + L.a_off;
     int8_t *pw = static_cast<int8_t *>(ws) + L.w_off;
+    float *part = reinterpret_cast<float *>(static_cast<int8_t *>(ws) + L.part_off);
     const int64_t ga = L.Mp / 64, gw = L.Np / 64;
     hipLaunchKernelGGL(k_mx_prep, dim3((unsigned)((ga + gw) * L.P.ns)), dim3(256), 0, st, view_of(A), view_of(W),
                        A.rows, W.rows, ga, A.n8, A.n6, A.n4, L.P, pa, pw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntiles = (L.Mp / kXBM) * (L.Np / kXBN);
-    hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)ntiles), dim3(512), 0, st, pa, pw, A.rows, W.rows, L.Mp, L.Np, L.P,
-                       Y, ldy);
+    hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)ntiles, (unsigned)L.sk.n), dim3(256), 0, st, pa, pw, A.rows,
+                       W.rows, L.Mp, L.Np, L.P, L.sk, Y, ldy, part);
+    e = hipGetLastError();
+    if (e != hipSuccess || L.sk.n <= 1) return e;
+    const int64_t MN = A.rows * W.rows;
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(MN, 256)), dim3(256), 0, st, part, L.sk.n,
+                       (int32_t)A.rows, W.rows, Y, ldy);
     return hipGetLastError();
 }
 
