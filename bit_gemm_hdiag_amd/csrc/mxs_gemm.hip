@@ -1423,6 +1423,216 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const int8_t *__restrict__ P
 }
 
 // ---------------------------------------------------------------------------
+// The same product on 256 x 128 workgroup tiles of eight waves (64 x 64 per
+// wave), for grids of 64 to 255 tiles of 256 x 256: there the larger tile
+// would leave CUs idle or need a K split and its reduction, while the
+// smaller tile fills the chip in one pass. Same prepared records.
+namespace ntile {
+constexpr int kXBN = 128;                       // workgroup tile: 256 A rows x 128 W rows
+constexpr int kXGroups = kXBM / 64 + kXBN / 64;
+// LDS image of one stage of the workgroup tile: the code parts of the six
+// group records (A groups 0..3, W groups 0..1), then the A scale parts, the
+// W scale parts, and 1.5 KiB that only absorbs the copies that keep every
+// wave's load count equal (see xdma_issue)
+constexpr int kXScA = kXGroups * kXCode;        // 36864
+constexpr int kXScW = kXScA + (kXBM / 64) * 256; // 37888
+constexpr int kXSink = kXScW + 512;             // 38400
+constexpr int kXSlot = kXSink + 1536;           // 39936
+constexpr int kXLoads = 5;                      // loads per wave and stage
+
+// the ring of four stage slots
+__shared__ __attribute__((aligned(16))) int8_t g_xring[4 * kXSlot];
+
+// A stage is 40 loads of 1 KiB, straight from global memory into LDS, five
+// per wave (no branch, and the same wait count in every wave): load L =
+// 5 wave + k is code chunk L mod 6 of group L / 6 for L < 36; load 36 the
+// scale parts of the four A groups (16 lanes each); load 37 those of the two
+// W groups (lanes 32..63 repeat lanes 0..31 into the sink); loads 38, 39
+// repeat load 37 into the sink. Every source advances by one record per
+// stage.
+struct XDma {
+    const int8_t *src[kXLoads];   // this lane's source at stage 0
+    uint32_t lds[kXLoads];        // wave-uniform LDS offset in the slot
+};
+
+__device__ __forceinline__ void xdma_issue(const XDma &D, uint32_t slot, int st, int ns) {
+    const int s = st < ns ? st : ns - 1;   // past the end: reload the last stage
+    const int64_t o = (int64_t)s * kXRec;
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k) dma16(D.src[k] + o, slot + D.lds[k]);
+}
+
+
+// Workgroup: 8 waves (4 x 2), tile 256 x 128; each wave owns 64 x 64 outputs
+// as 2 x 2 MFMA tiles, i.e. one 64-row A group and one 64-row W group. Both
+// operands reach LDS by DMA, through a ring of four stage slots. The fp6
+// matrix cores outrun the LDS here: a 4-bit step reads 6 KiB of fragments
+// per wave for 4 MFMAs, so the 4-bit stages are bound by LDS reads and the
+// 6/8-bit stages (four MFMAs per fragment set) by the matrix cores.
+// (Loading A straight into registers instead, with 4 waves of 64 x 128,
+// halves the LDS reads but measured slower: the vector memory path then
+// carries the same bytes.)
+__global__ __launch_bounds__(512, 1) void k_gemm_mx_n(const int8_t *__restrict__ PA, const int8_t *__restrict__ PW,
+                                                    int64_t M, int64_t N, int64_t Mp, int64_t Np, XPlan P,
+                                                    float *__restrict__ Y, int64_t ldy) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+
+    // tile order: each XCD (workgroups are dealt round-robin to the 8 XCDs)
+    // takes a contiguous run of tiles; runs sweep groups of 8 row-tiles
+    const int64_t tilesM = Mp / kXBM, tilesN = Np / kXBN, ntiles = tilesM * tilesN;
+    int64_t t = blockIdx.x;
+    if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+    const int64_t per_group = 8 * tilesN;
+    const int64_t gid = t / per_group, first_m = gid * 8;
+    const int64_t gsz = tilesM - first_m < 8 ? tilesM - first_m : 8;
+    const int64_t tm = first_m + (t % per_group) % gsz, tn = (t % per_group) / gsz;
+    const int64_t m0 = tm * kXBM, n0 = tn * kXBN;
+    const int ns = P.ns, nd = P.nd;
+
+    // this lane's DMA sources and the wave's LDS destinations
+    XDma D;
+    {
+        auto rec = [&](int g) -> const int8_t * {   // group record g of the tile at stage 0
+            return g < kXBM / 64 ? PA + ((m0 / 64 + g) * ns) * (int64_t)kXRec
+                                 : PW + ((n0 / 64 + (g - kXBM / 64)) * ns) * (int64_t)kXRec;
+        };
+#pragma unroll
+        for (int k = 0; k < kXLoads; ++k) {
+            const int L = kXLoads * wave + k;
+            if (L < 6 * kXGroups) {
+                D.src[k] = rec(L / 6) + (L % 6) * 1024 + lane * 16;
+                D.lds[k] = (uint32_t)((L / 6) * kXCode + (L % 6) * 1024);
+            } else if (L == 6 * kXGroups) {
+                D.src[k] = rec(lane >> 4) + kXCode + (lane & 15) * 16;
+                D.lds[k] = kXScA;
+            } else {
+                D.src[k] = rec(kXBM / 64 + ((lane >> 4) & 1)) + kXCode + (lane & 15) * 16;
+                D.lds[k] = L == 6 * kXGroups + 1 ? kXScW : kXSink + 512;
+            }
+        }
+    }
+
+    // LDS byte offsets (inside a slot) of this lane's pieces of fragment 0,
+    // step 0 (16-byte piece, 8-byte piece, scale dword); fragment i adds 512
+    // / 256 / 128 bytes, step j adds 3072 / 3072 / 0. Addresses are formed as
+    // slot base + lane offset + immediate, so one register per piece kind
+    // serves every slot and step.
+    const uint32_t ca = (uint32_t)(wm * kXCode), cw = (uint32_t)((kXBM / 64 + wn) * kXCode);
+    const uint32_t sa0 = (uint32_t)(kXScA + wm * 256), sw0 = (uint32_t)(kXScW + wn * 256);
+    const uint32_t lq = (uint32_t)(h * 1024 + l32 * 16), ld = (uint32_t)(2048 + h * 512 + l32 * 8),
+                   ls = (uint32_t)(l32 * 4);
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jw = 0; jw < 2; ++jw)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][jw][e] = 0.f;
+
+    // the fragments and scale bytes of one MFMA step (A rows, W rows)
+    struct Frags {
+        v8i a[2], w[2];
+        int sa[2], sw[2];
+    };
+    // scale bytes: one dword per row holds (step 0, k-half 0/1, step 1, k-half
+    // 0/1); the MFMA reads bits 0..7 of its scale operand, so the lane shifts
+    // its byte (2 j + h) down and leaves the others above it
+    auto read_scales = [&](uint32_t slot, int (&sa)[2], int (&sw)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            sa[i] = lds_i32(slot + sa0 + ls + i * 128);
+            sw[i] = lds_i32(slot + sw0 + ls + i * 128);
+        }
+    };
+    auto read_step = [&](uint32_t slot, int j, const int (&sa)[2], const int (&sw)[2], Frags &F) {
+        const uint32_t qa = slot + ca + lq, da = slot + ca + ld;
+        const uint32_t qw = slot + cw + lq, dw = slot + cw + ld;
+        const int sh = 16 * j + 8 * h;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const v4i pa = lds_v4(qa + i * 512 + j * 3072), pw = lds_v4(qw + i * 512 + j * 3072);
+            const v2i ra = lds_v2(da + i * 256 + j * 3072), rw = lds_v2(dw + i * 256 + j * 3072);
+            F.a[i] = v8i{pa[0], pa[1], pa[2], pa[3], ra[0], ra[1], 0, 0};
+            F.w[i] = v8i{pw[0], pw[1], pw[2], pw[3], rw[0], rw[1], 0, 0};
+            F.sa[i] = (int)((uint32_t)sa[i] >> sh);
+            F.sw[i] = (int)((uint32_t)sw[i] >> sh);
+        }
+    };
+    auto mma = [&](const Frags &X, const Frags &Z) {   // X: A fragments, Z: W fragments
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jw = 0; jw < 2; ++jw)
+                acc[i][jw] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(X.a[i], Z.w[jw], acc[i][jw], 2, 2, 0,
+                                                                            X.sa[i], 0, Z.sw[jw]);
+    };
+
+    // Software pipeline over MFMA steps, two fragment sets (F0: step 0, F1:
+    // step 1 of the current stage). Stage s: read F1; MFMAs that need only
+    // F0 and F1 (single stage: A0 W0; digit stage: hi*hi, hi*lo, lo*hi);
+    // wait for this wave's loads of stage s+1; barrier (all of stage s+1 has
+    // landed, every wave has finished reading stage s); issue stage s+4 into
+    // the slot of stage s; read F0 of stage s+1; the last MFMAs of stage s
+    // (A1 W1, or lo*lo), which overlap those reads. Ring of four slots,
+    // stage k in slot k % 4. After the last stage the reads of the following
+    // slot still run (in bounds, result unused), which keeps the loop free
+    // of branches.
+    const uint32_t ring = lds_addr(g_xring);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xdma_issue(D, ring + k * kXSlot, k, ns);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kXLoads));
+    lds_barrier();
+    Frags F0, F1;
+    int scA[2], scW[2];   // scale dwords of the current stage
+    read_scales(ring, scA, scW);
+    read_step(ring, 0, scA, scW, F0);
+    auto next = [&](int s) {
+        __builtin_amdgcn_sched_barrier(0);   // the MFMAs above issue before the wait
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kXLoads));
+        lds_barrier();
+        xdma_issue(D, ring + (uint32_t)((s & 3) * kXSlot), s + 4, ns);
+        const uint32_t nxt = ring + (uint32_t)(((s + 1) & 3) * kXSlot);
+        read_scales(nxt, scA, scW);
+        read_step(nxt, 0, scA, scW, F0);
+    };
+    int s = 0;
+    for (; s < nd; ++s) {   // digit stages: hi and lo steps of a 6/8-bit pair
+        read_step(ring + (uint32_t)((s & 3) * kXSlot), 1, scA, scW, F1);
+        mma(F0, F0);
+        mma(F0, F1);
+        mma(F1, F0);
+        next(s);
+        mma(F1, F1);
+    }
+    for (; s < ns; ++s) {   // two 4-bit pairs
+        read_step(ring + (uint32_t)((s & 3) * kXSlot), 1, scA, scW, F1);
+        mma(F0, F0);
+        next(s);
+        mma(F1, F1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outstanding at exit
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jw = 0; jw < 2; ++jw) {
+            const int64_t col = n0 + wn * 64 + jw * 32 + l32;
+            if (col >= N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * q + 4 * h + r;
+                    if (row < M) Y[row * ldy + col] = acc[i][jw][4 * q + r];
+                }
+        }
+}
+
+}  // namespace ntile
+
+// ---------------------------------------------------------------------------
 // Decode path (M <= kGemvMaxRows tokens): stream W once from HBM. Up to
 // kGemvVecRows tokens use the vector kernel below (k_gemv), more tokens the
 // matrix-core kernel further down (k_decode).
@@ -2319,11 +2529,14 @@ struct XLayout {
     int64_t Mp, Np;
     XPlan P;
     XSplit sk;
+    bool narrow;   // 256 x 128 tiles (k_gemm_mx_n), no split
     size_t a_off, w_off, part_off, total;
 };
 
-// Grids of fewer tiles than CUs split the stages into about 256 / tiles
-// parts of equal length (at most kMaxSplitK).
+// Grids of fewer than 64 tiles of 256 x 256 split the stages into about
+// 256 / tiles parts of equal length (at most kMaxSplitK); grids of 64 to 255
+// such tiles take the 256 x 128 kernel instead, unsplit (mx_split(256, ..)
+// gives one part).
 XSplit mx_split(int64_t ntiles, int32_t ns) {
     XSplit k;
     int64_t want = ntiles <= 0 || ntiles >= 256 ? 1 : 256 / ntiles;
@@ -2339,7 +2552,9 @@ XLayout mx_layout(const mxs_qmat &A, const mxs_qmat &W) {
     L.Mp = ceil_div(A.rows, kXBM) * kXBM;
     L.Np = ceil_div(W.rows, kXBN) * kXBN;
     L.P = make_xplan(A.n8, A.n6, A.n4);
-    L.sk = mx_split((L.Mp / kXBM) * (L.Np / kXBN), L.P.ns);
+    const int64_t t256 = (L.Mp / kXBM) * (L.Np / kXBN);
+    L.narrow = t256 >= 64 && t256 < 256;
+    L.sk = L.narrow ? mx_split(256, L.P.ns) : mx_split(t256, L.P.ns);
     L.a_off = 0;
     L.w_off = align256((size_t)(L.Mp / 64) * (size_t)L.P.ns * kXRec);
     L.part_off = align256(L.w_off + (size_t)(L.Np / 64) * (size_t)L.P.ns * kXRec);
@@ -2357,6 +2572,12 @@ hipError_t launch_mx(const mxs_qmat &A, const mxs_qmat &W, float *Y, int64_t ldy
                        A.rows, W.rows, ga, A.n8, A.n6, A.n4, L.P, pa, pw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (L.narrow) {
+        const int64_t ntiles = (L.Mp / kXBM) * (L.Np / ntile::kXBN);
+        hipLaunchKernelGGL(ntile::k_gemm_mx_n, dim3((unsigned)ntiles), dim3(512), 0, st, pa, pw, A.rows, W.rows,
+                           L.Mp, L.Np, L.P, Y, ldy);
+        return hipGetLastError();
+    }
     const int64_t ntiles = (L.Mp / kXBM) * (L.Np / kXBN);
     hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)ntiles, (unsigned)L.sk.n), dim3(256), 0, st, pa, pw, A.rows,
                        W.rows, L.Mp, L.Np, L.P, L.sk, Y, ldy, part);
