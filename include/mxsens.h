@@ -342,6 +342,9 @@ size_t mxs_mixed_gemm_mx_workspace(const mxs_qmat *A, const mxs_qmat *W);
  * two digits whose weight goes into the scale byte); every product and each
  * 64-element partial sum is exact, only the fp32 accumulation rounds (once
  * per instruction). Up to 63 rows it runs the kernels of mxs_mixed_gemm.
+ * Shapes with fewer than 64 output tiles of 256 x 256 split K into up to 8
+ * ranges whose fp32 sums, kept in the workspace, are added in range order,
+ * so the result is deterministic.
  * Arguments, layout, ownership, stream semantics and errors as for
  * mxs_mixed_gemm, with ws >= mxs_mixed_gemm_mx_workspace(A, W) bytes.
  */
