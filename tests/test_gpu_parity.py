@@ -278,6 +278,24 @@ def test_mixed_gemm_split_k(mx, orc, M, N, K):
     gemm_case(mx, orc, M, N, K, (500, 1500), seed=M + N + K, sample_rows=rows)
 
 
+# The fp6 entry's three prefill paths, chosen by the count of 256 x 256
+# output tiles: 256 or more (256 x 256 kernel, unsplit; W rows padded to 256),
+# 64 to 255 (256 x 128 kernel), fewer than 64 (256 x 256 kernel with K split
+# into up to 8 ranges added in order). Ragged M and N in each, whole-Y or
+# rows sampled across every row tile.
+@pytest.mark.parametrize("M,N,K,budget,sample", [
+    (2000, 8000, 256, (500, 1500), False),     # 256 tiles, last row and column tiles partial
+    (4000, 9000, 96, (0, 0), False),           # 576 tiles (2.25 passes), one 4-bit stage
+    (2048, 8192, 1024, (500, 1500), True),     # 256 tiles, digit and 4-bit stages
+    (1100, 8192, 256, (3100, 4000), False),    # 160 tiles: 256 x 128 kernel
+    (300, 1000, 4096, (500, 1500), False),     # 8 tiles: 8 K ranges
+    (520, 260, 1056, (800, 2000), False),      # 6 tiles: 6 K ranges, ragged both ways
+])
+def test_mixed_gemm_mx_tile_paths(mx, orc, M, N, K, budget, sample):
+    rows = np.unique(np.concatenate([np.arange(0, M, 37), [M - 1]])) if sample else None
+    gemm_case(mx, orc, M, N, K, budget, seed=M + 3 * N + K, sample_rows=rows, entry="mxs_mixed_gemm_mx")
+
+
 @pytest.mark.parametrize("M,N,K,budget", [(1, 65, 32, (0, 0)), (2, 130, 512, (10000, 0)), (3, 64, 352, (0, 10000)),
                                           (4, 200, 480, (3100, 4000)), (4, 1000, 4096, (500, 1500)),
                                           (2, 77, 1056, (300, 1000)), (1, 129, 800, (800, 2000)),
